@@ -1,0 +1,330 @@
+#!/usr/bin/env python3
+"""Benchmark: sharded paged-MLA decode step + LSE merge on one MI355X.
+
+A step is one pass of the whole path over one batch: for each of the S
+shards, the shard-local metadata and the rank-local partial decode, then the
+LSE-weighted merge of the S partials. Inputs are synthetic (seeded, shaped
+like the pages' workloads) and already resident in HBM when timing starts;
+two copies of the KV pool and queries are alternated so the 256 MB
+Infinity Cache cannot serve repeated reads.
+
+Default: the Kimi-K2.5-like workload (batch 64, 64 heads, q_len 1, 4 shards,
+bf16 KV, lengths uniform in [4096, 8192]) plus the merge-only sweep
+(4 partials of T x 64 heads x 512 bf16 + fp32 LSE, T in 1..128).
+Prints ONE JSON line on stdout. ``--all`` also measures the other four
+workloads and writes them to ``--details`` (JSON).
+
+Reported:
+  value         KV-GB/s of the step = bytes of every visible token's latent
+                row read once / step time;
+  tflops        2 * rows * (576 + 512) flops per visible (row, token) / time;
+  roofline      the attention kernel alone, timed with HIP events recorded by
+                the library around its launch: algorithmic bytes per launch
+                (the shard's KV rows + Q + partial out + LSE) / mean duration,
+                against 8 TB/s;
+  cpu_baseline  the fp64 oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
+METRIC = "MLA split-KV decode KV-GB/s + TFLOP/s vs roofline; merge μs (64 heads, D=512)"
+KERNEL_SRC = os.path.join(ROOT, "decode_attention_paged_amd", "csrc", "mla_decode.hip")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------
+# algorithmic work of a workload
+# --------------------------------------------------------------------------
+def workload_work(wl):
+    import numpy as np
+    row_bytes = 576 * (1 if wl.kv_dtype == "fp8" else 2)
+    lens = wl.seq_lens.astype(np.int64)
+    kv_bytes = int(lens.sum()) * row_bytes
+    q = wl.q_len
+    vis = (q * lens - q * (q - 1) // 2).clip(min=0)        # sum over draft rows of visible tokens
+    flops = 2.0 * wl.heads * (576 + 512) * float(vis.sum())
+    out_elt = 2 if wl.out_dtype == "bf16" else 4
+    per_shard = []
+    for r in range(wl.shards):
+        loc = lens // wl.shards + (r < lens % wl.shards)
+        rows = wl.batch * q * wl.heads
+        b = int(loc.sum()) * row_bytes + rows * 576 * 2 + rows * 512 * out_elt + rows * 4
+        locvis = 0
+        for i in range(q):
+            Lv = (lens - q + i + 1).clip(min=0)
+            locvis += int((Lv // wl.shards + (r < Lv % wl.shards)).sum())
+        per_shard.append((b, 2.0 * wl.heads * (576 + 512) * locvis))
+    return kv_bytes, flops, per_shard
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(os.path.dirname(KERNEL_SRC))):
+        with open(os.path.join(os.path.dirname(KERNEL_SRC), name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per attention-kernel launch from the committed counter summary
+    (null unless it was taken on the current kernel sources)."""
+    path = os.path.join(ROOT, "profiles", f"attn_kernel_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_sources_sha256_16") != kernel_sha():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# --------------------------------------------------------------------------
+# GPU timing
+# --------------------------------------------------------------------------
+def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True):
+    import torch
+
+    from decode_attention_paged_amd import step as ST
+    from workloads import make_config
+
+    log(f"[bench] config {index}: generating inputs")
+    wl = make_config(index)
+    kv_bytes, flops, per_shard = workload_work(wl)
+    dws = [ST.DeviceWorkload.upload(wl)]
+    if rotate and kv_bytes < 600e6:
+        d0 = dws[0]
+        import dataclasses
+        dws.append(dataclasses.replace(d0, q=d0.q.clone(), kv_pages=d0.kv_pages.clone()))
+    bufs = ST.StepBuffers(dws[0])
+    S = wl.shards
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(S)]
+          for _ in range(steps)]
+    mev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+
+    def one_step(k, timed):
+        dw = dws[k % len(dws)]
+        for r in range(S):
+            ST.run_metadata(dw, bufs, r)
+            ST.run_partial(dw, bufs, r, events=ev[k][r] if timed else None)
+        if timed:
+            mev[k][0].record()
+        ST.run_merge(dw, bufs)
+        if timed:
+            mev[k][1].record()
+
+    log(f"[bench] config {index}: warmup {warmup}")
+    for k in range(warmup):
+        one_step(k, False)
+    torch.cuda.synchronize()
+    log(f"[bench] config {index}: timing {steps} steps")
+    t0 = time.perf_counter()
+    for k in range(steps):
+        one_step(k, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = 1e3 * elapsed / steps
+    attn_ms = [[ev[k][r][0].elapsed_time(ev[k][r][1]) for r in range(S)] for k in range(steps)]
+    merge_ms = [mev[k][0].elapsed_time(mev[k][1]) for k in range(steps)]
+    tot_bytes = sum(b for b, _ in per_shard)
+    tot_flops = sum(f for _, f in per_shard)
+    attn_total_ms = statistics.mean(sum(row) for row in attn_ms)
+    mean_launch_ms = attn_total_ms / S
+    achieved_gbs = tot_bytes / (attn_total_ms * 1e-3) / 1e9
+    achieved_tflops = tot_flops / (attn_total_ms * 1e-3) / 1e12
+    res = dict(
+        index=index, name=wl.name, batch=wl.batch, heads=wl.heads, q_len=wl.q_len, shards=S,
+        kv_dtype=wl.kv_dtype, lse_base=wl.lse_base, tokens=int(wl.seq_lens.sum()),
+        ms_per_step=ms_step, kv_gbs=kv_bytes / (ms_step * 1e-3) / 1e9,
+        tflops=flops / (ms_step * 1e-3) / 1e12,
+        attn_kernel_mean_us=1e3 * mean_launch_ms, attn_kernel_bytes_per_launch=tot_bytes / S,
+        attn_kernel_gbs=achieved_gbs, attn_kernel_tflops=achieved_tflops,
+        merge_us=1e3 * statistics.median(merge_ms), steps=steps, warmup=warmup, rotated=len(dws),
+    )
+    peak_tf = FP8_PEAK_TFLOPS if wl.kv_dtype == "fp8" else BF16_PEAK_TFLOPS
+    res["attn_kernel_hbm_frac"] = achieved_gbs / HBM_PEAK_GBS
+    res["attn_kernel_mfma_frac"] = achieved_tflops / peak_tf
+    del dws, bufs
+    torch.cuda.empty_cache()
+    return wl, res
+
+
+def bench_merge_sweep(iters: int = 100, warmup: int = 10):
+    """Merge-only: 4 partials of [T, 64, 512] bf16 + fp32 LSE -> [T, 64, 512] bf16."""
+    import torch
+
+    from decode_attention_paged_amd import _lib as L
+    from workloads import MERGE_TOKENS, make_merge_inputs
+
+    out = {}
+    for T in MERGE_TOKENS:
+        mi = make_merge_inputs(T, seed=4000 + T)
+        set_bytes = 4 * T * 64 * (512 * 2 + 4) + T * 64 * 512 * 2 + T * 64 * 4
+        nsets = max(2, min(32, int(math.ceil(600e6 / set_bytes))))
+        sets = []
+        for s in range(nsets):
+            outs = [torch.from_numpy(o).view(torch.bfloat16).cuda() for o in mi.outs]
+            lses = [torch.from_numpy(l).cuda() for l in mi.lses]
+            sets.append((outs, lses, torch.empty((T, 64, 512), dtype=torch.bfloat16, device="cuda"),
+                         torch.empty((T, 64), dtype=torch.float32, device="cuda")))
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        for k in range(warmup):
+            o, l, y, yl = sets[k % nsets]
+            L.mla_merge_partials(o, l, [L.LSE_BASE_E] * 4, y, yl)
+        torch.cuda.synchronize()
+        for k in range(iters):
+            o, l, y, yl = sets[k % nsets]
+            evs[k][0].record()
+            L.mla_merge_partials(o, l, [L.LSE_BASE_E] * 4, y, yl)
+            evs[k][1].record()
+        torch.cuda.synchronize()
+        us = sorted(1e3 * a.elapsed_time(b) for a, b in evs)
+        med = statistics.median(us)
+        out[str(T)] = dict(us_median=med, us_min=us[0], bytes=set_bytes,
+                           gbs=set_bytes / (med * 1e-6) / 1e9, sets=nsets)
+        del sets
+    torch.cuda.empty_cache()
+    return out
+
+
+# --------------------------------------------------------------------------
+# CPU oracle baseline
+# --------------------------------------------------------------------------
+def cpu_baseline(wl, seconds: float):
+    import numpy as np
+
+    from oracle import mla_oracle as O
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    row_bytes = 576 * (1 if wl.kv_dtype == "fp8" else 2)
+    order = list(range(wl.batch))
+    done, nbytes = [], 0
+    t0 = time.perf_counter()
+    for b in order:
+        O.decode_step(wl, [b])
+        done.append(b)
+        nbytes += int(wl.seq_lens[b]) * row_bytes
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    return dict(value=nbytes / el / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
+                sample=f"{len(done)} of {wl.batch} requests ({sum(int(wl.seq_lens[b]) for b in done)} tokens) "
+                       f"of the {wl.name} workload: all {wl.shards} shard partials + merge, fp64 NumPy, "
+                       f"{el:.1f} s",
+                seconds=el)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload index 1..5 for the headline line")
+    ap.add_argument("--all", action="store_true", help="also measure every workload")
+    ap.add_argument("--details", default=None, help="write per-workload results (JSON) here")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-merge-sweep", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    from decode_attention_paged_amd import _lib as L
+    L.load()
+
+    wl, res = bench_workload(args.config, args.steps, args.warmup)
+    details = {"headline": res}
+    merge = None if args.no_merge_sweep else bench_merge_sweep()
+    if merge:
+        details["merge_only"] = merge
+    if args.all:
+        for idx in (1, 2, 3, 4, 5):
+            if idx == args.config:
+                continue
+            _, r = bench_workload(idx, max(3, args.steps // 2), max(1, args.warmup // 2))
+            details[f"config{idx}"] = r
+            log(f"[bench] config {idx} {r['name']}: {r['ms_per_step']:.3f} ms/step, "
+                f"{r['kv_gbs']:.0f} KV-GB/s, {r['tflops']:.1f} TFLOP/s, attn kernel "
+                f"{r['attn_kernel_gbs']:.0f} GB/s ({100 * r['attn_kernel_hbm_frac']:.1f}% HBM, "
+                f"{100 * r['attn_kernel_mfma_frac']:.1f}% MFMA)")
+
+    cpu = None if args.no_cpu else cpu_baseline(wl, args.cpu_seconds)
+    mfma_bound = res["attn_kernel_mfma_frac"] > res["attn_kernel_hbm_frac"] and wl.q_len > 1
+    if mfma_bound:
+        peak = FP8_PEAK_TFLOPS if wl.kv_dtype == "fp8" else BF16_PEAK_TFLOPS
+        roof = dict(bound="mfma", achieved=res["attn_kernel_tflops"], peak=peak, unit="TFLOP/s",
+                    frac=res["attn_kernel_tflops"] / peak)
+    else:
+        roof = dict(bound="hbm", achieved=res["attn_kernel_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=res["attn_kernel_gbs"] / HBM_PEAK_GBS)
+    roof["traffic"] = traffic_from_profile(wl.name)
+    roof["kernel"] = "attn_kernel (mla_decode.hip), mean of %d launches" % (args.steps * wl.shards)
+    roof["mean_launch_us"] = res["attn_kernel_mean_us"]
+    roof["algorithmic_bytes_per_launch"] = res["attn_kernel_bytes_per_launch"]
+
+    line = {
+        "metric": METRIC,
+        "value": round(res["kv_gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if wl.kv_dtype == "fp8" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: batch {wl.batch}, {wl.heads} heads, q_len {wl.q_len}, "
+                               f"{wl.shards} cyclic shards, {wl.kv_dtype} KV, page 64, "
+                               f"{res['tokens']} context tokens, partials + merge",
+                   "global_batch": wl.batch, "shards": wl.shards},
+        "tflops": round(res["tflops"], 3),
+        "merge_us": {T: round(v["us_median"], 2) for T, v in merge.items()} if merge else None,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    if args.details:
+        os.makedirs(os.path.dirname(os.path.abspath(args.details)), exist_ok=True)
+        with open(args.details, "w") as f:
+            json.dump(details, f, indent=1)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,268 @@
+// Host side of the C ABI declared in include/mla_dcp.h: argument checks,
+// workspace layout, launch configuration and error reporting. Every check
+// runs before any device work is enqueued.
+#include "../../include/mla_dcp.h"
+#include "mla_internal.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mla_status_t fail(mla_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+mla_status_t ok() {
+  g_last_error.clear();
+  return MLA_STATUS_OK;
+}
+
+mla_status_t device_fail(hipError_t err, const char* what) {
+  return fail(MLA_STATUS_DEVICE_ERROR, "%s: %s", what, hipGetErrorString(err));
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Compute units of the current device, cached per device ordinal.
+int device_cus(int* out) {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return -1;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int n = 0;
+    err = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess || n <= 0) return -1;
+    cache[dev] = n;
+  }
+  *out = cache[dev];
+  return 0;
+}
+
+}  // namespace
+
+namespace mla {
+
+WorkspaceLayout decode_workspace_layout(int32_t batch, int32_t rows) {
+  WorkspaceLayout w{};
+  const int64_t items = (int64_t)batch + kSplitTargetMax;
+  w.max_items = (int32_t)(((items + 7) / 8) * 8);
+  size_t off = 0;
+  w.plan = off;      off = align_up(off + 64, 256);
+  w.req_info = off;  off = align_up(off + sizeof(int2) * (size_t)batch, 256);
+  w.items = off;     off = align_up(off + sizeof(int2) * (size_t)w.max_items, 256);
+  w.part_lse = off;  off = align_up(off + sizeof(float) * (size_t)w.max_items * rows, 256);
+  w.part_o = off;    off = align_up(off + sizeof(float) * (size_t)w.max_items * rows * kDv, 256);
+  w.total = off;
+  return w;
+}
+
+}  // namespace mla
+
+extern "C" {
+
+const char* mla_status_string(mla_status_t status) {
+  switch (status) {
+    case MLA_STATUS_OK: return "ok";
+    case MLA_STATUS_INVALID_ARGUMENT: return "invalid argument";
+    case MLA_STATUS_UNSUPPORTED: return "unsupported";
+    case MLA_STATUS_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MLA_STATUS_DEVICE_ERROR: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* mla_last_error(void) { return g_last_error.c_str(); }
+int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+size_t mla_sizeof_decode_args(void) { return sizeof(mla_decode_args_t); }
+size_t mla_sizeof_merge_args(void) { return sizeof(mla_merge_args_t); }
+
+mla_status_t mla_build_shard_metadata(const int32_t* seq_lens, const int32_t* block_table,
+                                      int32_t batch, int32_t max_pages, int32_t page_size,
+                                      int32_t max_seq_len, int32_t shard_id, int32_t num_shards,
+                                      int32_t* local_seq_lens, int32_t* local_kv_indices,
+                                      int32_t local_kv_stride, int32_t* local_max_out,
+                                      void* stream) {
+  if (batch < 0) return fail(MLA_STATUS_INVALID_ARGUMENT, "batch must be >= 0 (got %d)", batch);
+  if (num_shards < 1 || num_shards > MLA_MAX_SHARDS)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "num_shards must be in [1, %d] (got %d)", MLA_MAX_SHARDS, num_shards);
+  if (shard_id < 0 || shard_id >= num_shards)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "shard_id %d outside [0, %d)", shard_id, num_shards);
+  if (page_size != MLA_PAGE_SIZE)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "page_size must be %d (got %d)", MLA_PAGE_SIZE, page_size);
+  if (max_pages < 1) return fail(MLA_STATUS_INVALID_ARGUMENT, "max_pages must be >= 1 (got %d)", max_pages);
+  if (max_seq_len < 0) return fail(MLA_STATUS_INVALID_ARGUMENT, "max_seq_len must be >= 0 (got %d)", max_seq_len);
+  const int32_t lmax_raw = max_seq_len / num_shards + (shard_id < max_seq_len % num_shards ? 1 : 0);
+  const int32_t lmax = lmax_raw > 1 ? lmax_raw : 1;
+  if (batch > 0 && (seq_lens == nullptr || local_seq_lens == nullptr))
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "seq_lens and local_seq_lens are required");
+  if (local_kv_indices != nullptr) {
+    if (block_table == nullptr && batch > 0)
+      return fail(MLA_STATUS_INVALID_ARGUMENT, "block_table is required with local_kv_indices");
+    if (local_kv_stride < lmax)
+      return fail(MLA_STATUS_INVALID_ARGUMENT, "local_kv_stride %d is below the local max %d", local_kv_stride, lmax);
+  }
+  if (local_max_out) *local_max_out = lmax;
+  hipError_t err = mla::launch_metadata(seq_lens, block_table, batch, max_pages, shard_id, num_shards,
+                                        local_seq_lens, local_kv_indices, local_kv_stride,
+                                        (hipStream_t)stream);
+  if (err != hipSuccess) return device_fail(err, "metadata launch");
+  return ok();
+}
+
+size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t q_len) {
+  if (batch < 0 || num_heads < 16 || num_heads % 16 != 0 || q_len < 1 || q_len > MLA_MAX_Q_LEN) return 0;
+  return mla::decode_workspace_layout(batch, num_heads * q_len).total;
+}
+
+mla_status_t mla_decode_partial(const mla_decode_args_t* a, mla_lse_base_t* lse_base_written, void* stream) {
+  if (a == nullptr) return fail(MLA_STATUS_INVALID_ARGUMENT, "args is NULL");
+  if (a->batch < 0) return fail(MLA_STATUS_INVALID_ARGUMENT, "batch must be >= 0 (got %d)", a->batch);
+  if (a->num_heads < 16 || a->num_heads % 16 != 0)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "num_heads must be a positive multiple of 16 (got %d)", a->num_heads);
+  if (a->q_len < 1 || a->q_len > MLA_MAX_Q_LEN)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "q_len must be in [1, %d] (got %d)", MLA_MAX_Q_LEN, a->q_len);
+  if (a->page_size != MLA_PAGE_SIZE)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "page_size must be %d (got %d)", MLA_PAGE_SIZE, a->page_size);
+  if (a->num_shards < 1 || a->num_shards > MLA_MAX_SHARDS)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "num_shards must be in [1, %d] (got %d)", MLA_MAX_SHARDS, a->num_shards);
+  if (a->shard_id < 0 || a->shard_id >= a->num_shards)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "shard_id %d outside [0, %d)", a->shard_id, a->num_shards);
+  if (a->max_pages < 1) return fail(MLA_STATUS_INVALID_ARGUMENT, "max_pages must be >= 1 (got %d)", a->max_pages);
+  if (a->num_pages < 1) return fail(MLA_STATUS_INVALID_ARGUMENT, "num_pages must be >= 1 (got %d)", a->num_pages);
+  if ((long long)a->num_pages * MLA_PAGE_SIZE > 0x7FFFFFFFLL)
+    return fail(MLA_STATUS_UNSUPPORTED, "num_pages %d exceeds 2^31 KV rows", a->num_pages);
+  if (a->kv_dtype != MLA_DTYPE_BF16 && a->kv_dtype != MLA_DTYPE_FP8_E4M3)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "kv_dtype must be BF16 or FP8_E4M3");
+  if (a->out_dtype != MLA_DTYPE_F32 && a->out_dtype != MLA_DTYPE_BF16)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "out_dtype must be F32 or BF16");
+  if (a->lse_base != MLA_LSE_BASE_E && a->lse_base != MLA_LSE_BASE_2)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "lse_base must be E or 2");
+  if (!(a->softmax_scale > 0.f) || !isfinite(a->softmax_scale))
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "softmax_scale must be positive and finite");
+  if (!(a->kv_scale > 0.f) || !isfinite(a->kv_scale))
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "kv_scale must be positive and finite");
+  if ((a->local_seq_lens == nullptr) != (a->local_kv_indices == nullptr))
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "local_seq_lens and local_kv_indices go together");
+  if (a->local_kv_indices != nullptr && a->local_kv_stride < 1)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "local_kv_stride must be >= 1 (got %d)", a->local_kv_stride);
+  if (a->split_target < 0 || a->split_target > mla::kSplitTargetMax)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "split_target must be in [0, %d] (got %d)", mla::kSplitTargetMax, a->split_target);
+  if (a->batch > 0) {
+    if (!a->q || !a->kv_pages || !a->block_table || !a->seq_lens || !a->out || !a->lse || !a->workspace)
+      return fail(MLA_STATUS_INVALID_ARGUMENT, "q, kv_pages, block_table, seq_lens, out, lse and workspace are required");
+  }
+  const int32_t rows = a->num_heads * a->q_len;
+  const mla::WorkspaceLayout w = mla::decode_workspace_layout(a->batch, rows);
+  if (a->batch > 0 && a->workspace_bytes < w.total)
+    return fail(MLA_STATUS_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", w.total, a->workspace_bytes);
+  if (lse_base_written) *lse_base_written = a->lse_base;
+  if (a->batch == 0) return ok();
+
+  int cus = 0;
+  if (device_cus(&cus) != 0) return fail(MLA_STATUS_DEVICE_ERROR, "cannot query the current device");
+  const int32_t row_blocks = (rows + mla::kRowsPerBlock - 1) / mla::kRowsPerBlock;
+  int32_t target = a->split_target;
+  if (target == 0) {
+    target = cus / row_blocks;
+    if (target < 1) target = 1;
+  }
+  if (target > mla::kSplitTargetMax) target = mla::kSplitTargetMax;
+
+  mla::DecodeParams p{};
+  p.q = (const uint16_t*)a->q;
+  p.kv = (const uint8_t*)a->kv_pages;
+  p.block_table = a->block_table;
+  p.seq_lens = a->seq_lens;
+  p.local_seq_lens = a->local_seq_lens;
+  p.local_kv_indices = a->local_kv_indices;
+  p.local_kv_stride = a->local_kv_stride;
+  p.batch = a->batch;
+  p.heads = a->num_heads;
+  p.q_len = a->q_len;
+  p.rows = rows;
+  p.row_blocks = row_blocks;
+  p.max_pages = a->max_pages;
+  p.num_pages = a->num_pages;
+  p.shard = a->shard_id;
+  p.num_shards = a->num_shards;
+  const float kv_scale = a->kv_dtype == MLA_DTYPE_FP8_E4M3 ? a->kv_scale : 1.f;
+  p.scale_log2 = (float)((double)a->softmax_scale * (double)kv_scale * 1.4426950408889634);
+  p.out_scale = kv_scale;
+  p.lse_base2 = a->lse_base == MLA_LSE_BASE_2;
+  p.out_bf16 = a->out_dtype == MLA_DTYPE_BF16;
+  p.out = a->out;
+  p.lse = a->lse;
+  uint8_t* ws = (uint8_t*)a->workspace;
+  p.plan = (int32_t*)(ws + w.plan);
+  p.req_info = (int2*)(ws + w.req_info);
+  p.items = (int2*)(ws + w.items);
+  p.part_lse = (float*)(ws + w.part_lse);
+  p.part_o = (float*)(ws + w.part_o);
+  p.max_items = w.max_items;
+  p.split_target = target;
+
+  hipError_t err = mla::launch_decode(p, a->kv_dtype == MLA_DTYPE_FP8_E4M3, (hipEvent_t)a->event_begin,
+                                      (hipEvent_t)a->event_end, (hipStream_t)stream);
+  if (err != hipSuccess) return device_fail(err, "decode launch");
+  return ok();
+}
+
+mla_status_t mla_merge_partials(const mla_merge_args_t* a, void* stream) {
+  if (a == nullptr) return fail(MLA_STATUS_INVALID_ARGUMENT, "args is NULL");
+  if (a->num_shards < 1 || a->num_shards > MLA_MAX_SHARDS)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "num_shards must be in [1, %d] (got %d)", MLA_MAX_SHARDS, a->num_shards);
+  if (a->rows < 0) return fail(MLA_STATUS_INVALID_ARGUMENT, "rows must be >= 0 (got %d)", a->rows);
+  if (a->num_heads < 1) return fail(MLA_STATUS_INVALID_ARGUMENT, "num_heads must be >= 1 (got %d)", a->num_heads);
+  if (a->dv < 8 || a->dv % 8 != 0) return fail(MLA_STATUS_INVALID_ARGUMENT, "dv must be a positive multiple of 8 (got %d)", a->dv);
+  if (a->in_dtype != MLA_DTYPE_F32 && a->in_dtype != MLA_DTYPE_BF16)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "in_dtype must be F32 or BF16");
+  if (a->out_dtype != MLA_DTYPE_F32 && a->out_dtype != MLA_DTYPE_BF16)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "out_dtype must be F32 or BF16");
+  if (a->lse_out_base != MLA_LSE_BASE_E && a->lse_out_base != MLA_LSE_BASE_2)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "lse_out_base must be E or 2");
+  if (a->outs == nullptr || a->lses == nullptr || a->bases == nullptr)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "outs, lses and bases arrays are required");
+  mla::MergeParams p{};
+  p.num_shards = a->num_shards;
+  for (int r = 0; r < a->num_shards; ++r) {
+    if (a->rows > 0 && (a->outs[r] == nullptr || a->lses[r] == nullptr))
+      return fail(MLA_STATUS_INVALID_ARGUMENT, "shard %d has a NULL out or lse pointer", r);
+    if (a->bases[r] != MLA_LSE_BASE_E && a->bases[r] != MLA_LSE_BASE_2)
+      return fail(MLA_STATUS_INVALID_ARGUMENT, "shard %d has an invalid LSE base", r);
+    p.outs[r] = a->outs[r];
+    p.lses[r] = a->lses[r];
+    p.lse_to_log2[r] = a->bases[r] == MLA_LSE_BASE_E ? 1.4426950408889634f : 1.f;
+  }
+  if (a->rows > 0 && a->out == nullptr) return fail(MLA_STATUS_INVALID_ARGUMENT, "out is required");
+  p.vectors = (int64_t)a->rows * a->num_heads;
+  p.dv = a->dv;
+  p.in_bf16 = a->in_dtype == MLA_DTYPE_BF16;
+  p.out_bf16 = a->out_dtype == MLA_DTYPE_BF16;
+  p.out = a->out;
+  p.lse_out = a->lse_out;
+  p.lse_out_from_log2 = a->lse_out_base == MLA_LSE_BASE_E ? 0.69314718055994531f : 1.f;
+  hipError_t err = mla::launch_merge(p, (hipStream_t)stream);
+  if (err != hipSuccess) return device_fail(err, "merge launch");
+  return ok();
+}
+
+}  // extern "C"

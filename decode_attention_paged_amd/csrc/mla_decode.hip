@@ -1,0 +1,520 @@
+// Rank-local paged MLA decode for gfx950 (MI355X).
+//
+// Computes, for one context shard r of S, softmax attention of every query
+// row over the KV tokens the shard owns (token t belongs to shard t mod S;
+// prhub.com.cn digest of sgl-project/sglang PR 33926, sections 功能与动机 and
+// 实现拆解 step 3), emitting (out, lse) with the neutral (0, -inf) for rows
+// that see no owned token.
+//
+// Three kernels per call, all on the caller's stream:
+//   plan_kernel    splits the shard's tokens into equal chunks over the
+//                  compute units (split-KV schedule derived on device from the
+//                  lengths, so the call needs no host synchronisation);
+//   attn_kernel    one workgroup per (chunk, 128-query-row block): KV tiles of
+//                  32 tokens are gathered from their pages into LDS once and
+//                  shared by four waves of 32 query rows each; S^T = K Q^T and
+//                  O^T += V^T P^T run on 32x32x16 bf16 MFMA with an online
+//                  base-2 softmax; a request held by one chunk is finalised in
+//                  place, otherwise a normalised partial goes to workspace;
+//   combine_kernel LSE-weighted combine of a request's chunk partials.
+//
+// Data layout in LDS per stage (one 32-token tile):
+//   K tile  [32 tokens][72 chunks of 16 B], chunk c of token t stored at
+//           slot 72 t + (c ^ h(t)) with h(t) = (t & 7) ^ ((t >> 3) & 1):
+//           the MFMA A-operand reads (token = lane % 32) hit distinct banks.
+//   Vt tile [512 dims][4 groups of 8 tokens] (bf16), the transposed V needed
+//           as the A operand of O^T += V^T P^T. The token order inside a
+//           group matches the order of P values that the S^T accumulator
+//           leaves in each lane, so P never leaves registers.
+#include "mla_internal.h"
+
+#include <limits.h>
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kNegInf = -__builtin_inff();
+// The exponent reference of a row is fixed at the max of the first tile that
+// holds a visible token, so the output accumulator is never rescaled inside
+// the tile loop. Unnormalised probabilities stay below 2^kOverflowSlack; a
+// later tile whose max exceeds the reference by more than that makes the
+// workgroup redo the chunk with the chunk's true max as the reference.
+constexpr float kOverflowSlack = 64.0f;
+
+constexpr int kKBytes = kTile * kDqk * 2;        // 36864
+constexpr int kVtBytes = kDv * 4 * 16;           // 32768
+constexpr int kStageBytes = kKBytes + kVtBytes;  // 69632
+constexpr int kChunks = kDqk / 8;                // 72 chunks of 8 dims per row
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ int req_len(const DecodeParams& p, int b) {
+  int L = p.seq_lens[b];
+  L = L < 0 ? 0 : L;
+  const int cap = p.max_pages * kPage;   // never read past the block-table row
+  return L > cap ? cap : L;
+}
+
+// Number of tokens of request b the shard owns (before any causal limit).
+__device__ __forceinline__ int local_count(const DecodeParams& p, int b) {
+  if (p.local_seq_lens != nullptr) {
+    int n = p.local_seq_lens[b];
+    n = n < 0 ? 0 : n;
+    return n > p.local_kv_stride ? p.local_kv_stride : n;
+  }
+  const int L = req_len(p, b);
+  return L / p.num_shards + (p.shard < L % p.num_shards ? 1 : 0);
+}
+
+// Physical KV row of the shard's j-th owned token of request b (j < count),
+// or -1 when the page id / row is outside the pool.
+__device__ __forceinline__ int kv_row(const DecodeParams& p, int b, int j) {
+  long long row;
+  if (p.local_kv_indices != nullptr) {
+    row = p.local_kv_indices[(long long)b * p.local_kv_stride + j];
+  } else {
+    const int t = j * p.num_shards + p.shard;
+    const int page = p.block_table[(long long)b * p.max_pages + (t >> 6)];
+    row = (page < 0 || page >= p.num_pages) ? -1 : (long long)page * kPage + (t & 63);
+  }
+  return (row < 0 || row >= (long long)p.num_pages * kPage) ? -1 : (int)row;
+}
+
+// ---------------------------------------------------------------------------
+// plan: chunk size and the (request, chunk) work list
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void plan_kernel(DecodeParams p) {
+  __shared__ long long s_part[16];
+  __shared__ int s_scan[1024];
+  __shared__ int s_chunk;
+  __shared__ int s_base;
+  const int tid = threadIdx.x;
+
+  long long tot = 0;
+  for (int b = tid; b < p.batch; b += 1024) tot += local_count(p, b);
+  for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off);
+  if ((tid & 63) == 0) s_part[tid >> 6] = tot;
+  __syncthreads();
+  if (tid == 0) {
+    long long all = 0;
+    for (int w = 0; w < 16; ++w) all += s_part[w];
+    const long long target = p.split_target;
+    long long c = (all + target - 1) / target;
+    c = ((c + kTile - 1) / kTile) * kTile;
+    if (c < kMinChunk) c = kMinChunk;
+    if (c > INT_MAX / 4) c = INT_MAX / 4;
+    s_chunk = (int)c;
+    s_base = 0;
+  }
+  __syncthreads();
+  const int C = s_chunk;
+
+  for (int base = 0; base < p.batch; base += 1024) {
+    const int b = base + tid;
+    int n = 0;
+    if (b < p.batch) {
+      const int cnt = local_count(p, b);
+      n = cnt > 0 ? (cnt + C - 1) / C : 1;   // an empty request still gets one item
+    }
+    s_scan[tid] = n;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int v = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += v;
+      __syncthreads();
+    }
+    const int first = s_base + s_scan[tid] - n;
+    if (b < p.batch) {
+      p.req_info[b] = make_int2(first, n);
+      for (int c = 0; c < n; ++c) p.items[first + c] = make_int2(b, c);
+    }
+    __syncthreads();
+    if (tid == 1023) s_base += s_scan[1023];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    p.plan[0] = s_base;
+    p.plan[1] = C;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// tile staging
+// ---------------------------------------------------------------------------
+// Token of tile position p (0..7) in group G (0..3): groups hold the tokens
+// whose P values sit in k-slots of one half of one PV MFMA.
+__device__ __forceinline__ int group_token(int G, int pidx) {
+  return 16 * (G >> 1) + 4 * (G & 1) + 8 * (pidx >> 2) + (pidx & 3);
+}
+
+__device__ __forceinline__ int k_slot(int tok, int chunk) {
+  const int h = (tok & 7) ^ ((tok >> 3) & 1);
+  return kChunks * tok + (chunk ^ h);
+}
+
+// Vt slot (16-byte units) of (dim, group): the low four bits mix dim bits so
+// that both the MFMA reads (consecutive dims) and the loader's writes (dims
+// eight apart) spread over all banks.
+__device__ __forceinline__ int vt_slot(int dim, int G) {
+  const int b0 = dim & 1, b1 = (dim >> 1) & 1, b2 = (dim >> 2) & 1, b3 = (dim >> 3) & 1;
+  const int b4 = (dim >> 4) & 1, b5 = (dim >> 5) & 1, b6 = (dim >> 6) & 1;
+  const int low = (b0 ^ b4) | ((b1 ^ b5) << 1) | ((b2 ^ b3 ^ b6) << 2) | (b3 << 3);
+  return 16 * (4 * (dim >> 4) + G) + low;
+}
+
+template <bool kFp8> struct Raw;
+template <> struct Raw<false> { u32x4_t v[8]; u32x4_t rope; };
+template <> struct Raw<true> { u32x2_t v[8]; u32x2_t rope; };
+
+// OCP e4m3 -> bf16 bit pattern, exact. Normal codes (exponent field >= 1)
+// move into the bf16 fields with the exponent rebiased from 7 to 127;
+// subnormal codes are m * 2^-9 (m <= 7), exact in float; S.1111.111 is NaN.
+__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t x) {
+  const uint32_t em = x & 0x7Fu;
+  const uint32_t sign = (x & 0x80u) << 8;
+  const uint32_t normal = (em << 4) + (120u << 7);
+  const uint32_t sub = __float_as_uint((float)em * 0x1p-9f) >> 16;
+  const uint32_t mag = em == 0x7Fu ? 0x7FC0u : (em >= 8u ? normal : sub);
+  return sign | mag;
+}
+
+// 8 e4m3 bytes -> 8 bf16 (as four 32-bit words)
+__device__ __forceinline__ u32x4_t e4m3x8_to_bf16x8(u32x2_t w) {
+  u32x4_t r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t word = w[k >> 1] >> (16 * (k & 1));
+    r[k] = e4m3_to_bf16_bits(word & 0xFFu) | (e4m3_to_bf16_bits((word >> 8) & 0xFFu) << 16);
+  }
+  return r;
+}
+
+template <bool kFp8>
+__device__ __forceinline__ void load_tile(const DecodeParams& p, int b, int jt, int j1, Raw<kFp8>& raw) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int G = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // rows of the tile's 32 tokens, computed by lanes 0..31 of every wave:
+  // -2 = past the chunk end (zero fill), -1 = bad page (NaN fill). Loads are
+  // issued unconditionally from row 0 for those and replaced afterwards, so
+  // the loader has no branches.
+  int my_row = -2;
+  if (lane < kTile && jt + lane < j1) my_row = kv_row(p, b, jt + lane);
+  constexpr int row_bytes = kFp8 ? kDqk : 2 * kDqk;
+  constexpr int chunk_bytes = kFp8 ? 8 : 16;
+  constexpr uint32_t kNanFill = kFp8 ? 0x7F7F7F7Fu : 0x7FC07FC0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = __builtin_amdgcn_readlane(my_row, group_token(G, i));
+    const uint8_t* src = p.kv + (long long)(r >= 0 ? r : 0) * row_bytes + lane * chunk_bytes;
+    const uint32_t fill = r == -1 ? kNanFill : 0u;
+    if constexpr (kFp8) {
+      const u32x2_t x = *(const u32x2_t*)src;
+      raw.v[i] = r >= 0 ? x : u32x2_t{fill, fill};
+    } else {
+      const u32x4_t x = *(const u32x4_t*)src;
+      raw.v[i] = r >= 0 ? x : u32x4_t{fill, fill, fill, fill};
+    }
+  }
+  // rope dims (chunks 64..71): token tid / 8, chunk 64 + tid % 8
+  const int r = __shfl(my_row, tid >> 3);
+  const uint8_t* src = p.kv + (long long)(r >= 0 ? r : 0) * row_bytes + (64 + (tid & 7)) * chunk_bytes;
+  const uint32_t fill = r == -1 ? kNanFill : 0u;
+  if constexpr (kFp8) {
+    const u32x2_t x = *(const u32x2_t*)src;
+    raw.rope = r >= 0 ? x : u32x2_t{fill, fill};
+  } else {
+    const u32x4_t x = *(const u32x4_t*)src;
+    raw.rope = r >= 0 ? x : u32x4_t{fill, fill, fill, fill};
+  }
+}
+
+template <bool kFp8>
+__device__ __forceinline__ void store_tile(uint8_t* stage, const Raw<kFp8>& raw) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int G = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint8_t* ks = stage;
+  uint8_t* vt = stage + kKBytes;
+  u32x4_t d[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if constexpr (kFp8) d[i] = e4m3x8_to_bf16x8(raw.v[i]);
+    else d[i] = raw.v[i];
+    *(u32x4_t*)(ks + 16 * k_slot(group_token(G, i), lane)) = d[i];
+  }
+  {
+    u32x4_t rp;
+    if constexpr (kFp8) rp = e4m3x8_to_bf16x8(raw.rope);
+    else rp = raw.rope;
+    *(u32x4_t*)(ks + 16 * k_slot(tid >> 3, 64 + (tid & 7))) = rp;
+  }
+  // transpose the 8 tokens x 8 dims block: column e holds dim 8*lane+e of
+  // the group's tokens in position order
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    u32x4_t col;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t lo = d[2 * w][e >> 1], hi = d[2 * w + 1][e >> 1];
+      col[w] = (e & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+    }
+    *(u32x4_t*)(vt + 16 * vt_slot(8 * lane + e, G)) = col;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// attention over one chunk for 128 query rows
+// ---------------------------------------------------------------------------
+template <bool kFp8>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  int item, rbk;
+  if (p.row_blocks == 1) {
+    item = blockIdx.x;
+    rbk = 0;
+  } else {
+    // the row blocks of one chunk get ids congruent mod 8, i.e. the same XCD,
+    // so their repeated reads of the chunk's KV are served by that XCD's L2
+    const int x = blockIdx.x & 7, s = blockIdx.x >> 3;
+    item = (s / p.row_blocks) * 8 + x;
+    rbk = s % p.row_blocks;
+  }
+  if (item >= p.plan[0]) return;
+  const int2 it = p.items[item];
+  const int b = it.x;
+  const int chunk = p.plan[1];
+  const int cnt = local_count(p, b);
+  const int j0 = it.y * chunk;
+  const int j1 = min(cnt, j0 + chunk);
+  const int L = req_len(p, b);
+  const bool single = p.req_info[b].y == 1;
+
+  const int row = rbk * kRowsPerBlock + wave * kRowsPerWave + (lane & 31);
+  const bool row_ok = row < p.rows;
+  const bool wave_active = rbk * kRowsPerBlock + wave * kRowsPerWave < p.rows;
+
+  // local index bound of the tokens this row may see: t = j*S + r <= L - q + i
+  int jvis = j1;
+  if (row_ok) {
+    const int i = row / p.heads;
+    const int lim = L - p.q_len + i - p.shard;
+    const int jl = lim >= 0 ? lim / p.num_shards + 1 : 0;
+    jvis = min(j1, jl);
+  }
+
+  bf16x8_t qreg[kDqk / 16];
+  {
+    // rows past the end load row 0 and are zeroed (branch-free)
+    const uint16_t* qrow = p.q + ((long long)b * p.rows + (row_ok ? row : 0)) * kDqk + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < kDqk / 16; ++ks) {
+      const bf16x8_t x = *(const bf16x8_t*)(qrow + 16 * ks);
+      qreg[ks] = row_ok ? x : bf16x8_t{};
+    }
+  }
+
+  // per-lane LDS offsets of the MFMA operands
+  const int tok = lane & 31, hi = lane >> 5;
+  const int h_tok = (tok & 7) ^ ((tok >> 3) & 1);
+  const int ntiles = j1 > j0 ? (j1 - j0 + kTile - 1) / kTile : 0;
+
+  f32x16_t o[kDv / 32];
+  float m_ref = kNegInf;   // exponent reference (log2 domain)
+  float m_all = kNegInf;   // true max over the chunk's visible scores
+  float l_sum = 0.f;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+#pragma unroll
+    for (int db = 0; db < kDv / 32; ++db) o[db] = f32x16_t{};
+    l_sum = 0.f;
+    m_ref = attempt == 0 ? kNegInf : m_all;
+    bool overflow = false;
+
+    Raw<kFp8> raw;
+    if (ntiles > 0) {
+      load_tile<kFp8>(p, b, j0, j1, raw);
+      store_tile<kFp8>(smem, raw);
+    }
+    __syncthreads();
+
+    for (int tile = 0; tile < ntiles; ++tile) {
+      const int jt = j0 + tile * kTile;
+      const bool more = tile + 1 < ntiles;
+      if (more) load_tile<kFp8>(p, b, jt + kTile, j1, raw);
+      const uint8_t* ks = smem + (tile & 1) * kStageBytes;
+      const uint8_t* vt = ks + kKBytes;
+
+      if (wave_active) {
+        // S^T[token][row] = sum_d K[token][d] Q[row][d]
+        f32x16_t s = f32x16_t{};
+#pragma unroll
+        for (int kk = 0; kk < kDqk / 16; ++kk) {
+          const int c = 2 * kk + hi;
+          const bf16x8_t a = *(const bf16x8_t*)(ks + 16 * (kChunks * tok + (c ^ h_tok)));
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], s, 0, 0, 0);
+        }
+        // softmax numerators, base 2; a lane holds row (lane % 32) and 16 tokens
+        float tmax = kNegInf;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int j = jt + 8 * (v >> 2) + 4 * hi + (v & 3);
+          s[v] = j < jvis ? s[v] * p.scale_log2 : kNegInf;
+          tmax = fmaxf(tmax, s[v]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        m_all = fmaxf(m_all, tmax);
+        m_ref = m_ref == kNegInf ? tmax : m_ref;
+        overflow = overflow || tmax > m_ref + kOverflowSlack;
+        const float m_use = m_ref == kNegInf ? 0.f : m_ref;
+        bf16x8_t pb[2];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float pv = exp2_fast(s[v] - m_use);
+          l_sum += pv;
+          pb[v >> 3][v & 7] = (__bf16)pv;
+        }
+        // O^T[dim][row] += sum_token V^T[dim][token] P^T[token][row]
+#pragma unroll
+        for (int db = 0; db < kDv / 32; ++db) {
+          const int dim = 32 * db + tok;
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            const bf16x8_t a = *(const bf16x8_t*)(vt + 16 * vt_slot(dim, 2 * m + hi));
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[m], o[db], 0, 0, 0);
+          }
+        }
+      }
+      if (more) store_tile<kFp8>(smem + ((tile + 1) & 1) * kStageBytes, raw);
+      __syncthreads();
+    }
+    if (!__syncthreads_or(overflow ? 1 : 0)) break;
+  }
+
+  if (!wave_active) return;
+  const float l_tot = l_sum + __shfl_xor(l_sum, 32);
+  const bool any = l_tot > 0.f;
+  const float inv = any ? p.out_scale / l_tot : 0.f;
+  const float lse2 = any ? m_ref + log2_fast(l_tot) : kNegInf;
+  if (!row_ok) return;
+
+  // a request held by one chunk is final here; otherwise write the chunk's
+  // normalised partial (f32, base-2 lse) for the combine kernel
+  const long long orow = (long long)b * p.rows + row;
+  const long long prow = (long long)item * p.rows + row;
+  if (single && p.out_bf16) {
+    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+    __bf16* dst = (__bf16*)p.out + orow * kDv + 4 * hi;
+#pragma unroll
+    for (int db = 0; db < kDv / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4_t v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(o[db][4 * g + e] * inv);
+        *(bf16x4_t*)(dst + 32 * db + 8 * g) = v4;
+      }
+  } else {
+    float* dst = (single ? (float*)p.out + orow * kDv : p.part_o + prow * kDv) + 4 * hi;
+#pragma unroll
+    for (int db = 0; db < kDv / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4_t v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = o[db][4 * g + e] * inv;
+        *(f32x4_t*)(dst + 32 * db + 8 * g) = v4;
+      }
+  }
+  if (hi == 0) {
+    if (single) p.lse[orow] = p.lse_base2 ? lse2 : lse2 * kLn2;
+    else p.part_lse[prow] = lse2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// combine the chunk partials of requests split over several workgroups
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
+  const int b = blockIdx.x;
+  const int2 ri = p.req_info[b];
+  if (ri.y <= 1) return;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (row >= p.rows) return;
+
+  float mx = kNegInf;
+  for (int c = 0; c < ri.y; ++c) mx = fmaxf(mx, p.part_lse[(long long)(ri.x + c) * p.rows + row]);
+  f32x4_t acc0 = f32x4_t{}, acc1 = f32x4_t{};
+  float wsum = 0.f;
+  if (mx != kNegInf) {
+    for (int c = 0; c < ri.y; ++c) {
+      const long long prow = (long long)(ri.x + c) * p.rows + row;
+      const float w = exp2_fast(p.part_lse[prow] - mx);
+      const f32x4_t* src = (const f32x4_t*)(p.part_o + prow * kDv + 8 * lane);
+      acc0 += w * src[0];
+      acc1 += w * src[1];
+      wsum += w;
+    }
+  }
+  const bool any = wsum > 0.f;
+  const float inv = any ? 1.f / wsum : 0.f;
+  acc0 *= inv;
+  acc1 *= inv;
+  const long long orow = (long long)b * p.rows + row;
+  if (p.out_bf16) {
+    __bf16* dst = (__bf16*)p.out + orow * kDv + 8 * lane;
+    bf16x8_t v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = (__bf16)acc0[e];
+      v[4 + e] = (__bf16)acc1[e];
+    }
+    *(bf16x8_t*)dst = v;
+  } else {
+    f32x4_t* dst = (f32x4_t*)((float*)p.out + orow * kDv + 8 * lane);
+    dst[0] = acc0;
+    dst[1] = acc1;
+  }
+  if (lane == 0) {
+    const float lse2 = any ? mx + log2_fast(wsum) : kNegInf;
+    p.lse[orow] = p.lse_base2 ? lse2 : lse2 * kLn2;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, bool fp8, hipEvent_t ev_begin, hipEvent_t ev_end,
+                         hipStream_t stream) {
+  if (p.batch == 0) return hipSuccess;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int items = p.batch + p.split_target;
+  const int grid = p.row_blocks == 1 ? items : ((items + 7) / 8) * 8 * p.row_blocks;
+  if (ev_begin) {
+    err = hipEventRecord(ev_begin, stream);
+    if (err != hipSuccess) return err;
+  }
+  if (fp8) hipLaunchKernelGGL(attn_kernel<true>, dim3(grid), dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(attn_kernel<false>, dim3(grid), dim3(256), 0, stream, p);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (ev_end) {
+    err = hipEventRecord(ev_end, stream);
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(combine_kernel, dim3(p.batch, (p.rows + 3) / 4), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,76 @@
+// Internal declarations shared by the HIP translation units of libmla_dcp.
+// Not part of the C ABI (see include/mla_dcp.h for that).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kPage = 64;
+constexpr int kDqk = 576;       // latent 512 + rope 64
+constexpr int kDv = 512;        // V = first 512 latent dims
+constexpr int kTile = 32;       // KV tokens per attention tile
+constexpr int kWaves = 4;       // waves per attention workgroup
+constexpr int kRowsPerWave = 32;
+constexpr int kRowsPerBlock = kWaves * kRowsPerWave;   // 128 query rows
+constexpr int kMinChunk = 64;   // smallest KV chunk one workgroup takes
+constexpr int kSplitTargetMax = 512;
+constexpr int kMaxShards = 16;
+
+// Everything the plan / attention / combine kernels need for one shard.
+struct DecodeParams {
+  const uint16_t* q;              // bf16 [B][q_len][H][576]
+  const uint8_t* kv;              // [num_pages][64][576] bf16 or e4m3
+  const int32_t* block_table;     // [B][max_pages]
+  const int32_t* seq_lens;        // [B] global lengths
+  const int32_t* local_seq_lens;  // optional [B]
+  const int32_t* local_kv_indices;// optional [B][stride]
+  int32_t local_kv_stride;
+  int32_t batch, heads, q_len, rows, row_blocks;
+  int32_t max_pages, num_pages, shard, num_shards;
+  float scale_log2;               // softmax_scale * kv_scale * log2(e)
+  float out_scale;                // kv_scale (fp8) or 1
+  int32_t lse_base2;              // write lse in base 2 (else natural)
+  int32_t out_bf16;               // out dtype bf16 (else f32)
+  void* out;
+  float* lse;
+  // workspace
+  int32_t* plan;                  // [0] items, [1] chunk tokens
+  int2* req_info;                 // [B] (first item, number of items)
+  int2* items;                    // [max_items] (request, chunk index)
+  float* part_lse;                // [max_items][rows] base-2
+  float* part_o;                  // [max_items][rows][512], normalised, scaled
+  int32_t max_items;
+  int32_t split_target;
+};
+
+struct WorkspaceLayout {
+  size_t plan, req_info, items, part_lse, part_o, total;
+  int32_t max_items;
+};
+WorkspaceLayout decode_workspace_layout(int32_t batch, int32_t rows);
+
+struct MergeParams {
+  const void* outs[kMaxShards];
+  const float* lses[kMaxShards];
+  float lse_to_log2[kMaxShards];  // multiplier taking shard r's lse to base 2
+  int32_t num_shards;
+  int64_t vectors;                // rows * heads
+  int32_t dv;
+  int32_t in_bf16, out_bf16;
+  void* out;
+  float* lse_out;
+  float lse_out_from_log2;        // multiplier from base 2 to the output base
+};
+
+hipError_t launch_metadata(const int32_t* seq_lens, const int32_t* block_table, int32_t batch,
+                           int32_t max_pages, int32_t shard, int32_t num_shards,
+                           int32_t* local_seq_lens, int32_t* local_kv_indices,
+                           int32_t stride, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, bool fp8, hipEvent_t ev_begin, hipEvent_t ev_end,
+                         hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+
+}  // namespace mla

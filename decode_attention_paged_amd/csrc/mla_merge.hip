@@ -1,0 +1,142 @@
+// Cross-shard LSE-weighted merge and shard-local metadata for gfx950.
+//
+// Merge: the LSE-weighted softmax reduction of every shard's partial output
+// into the full-context result (github.com sgl-project/sglang PR 33364,
+// "[Attention][DCP] Add symm_a2a ...", Modifications, the fourth kernel; the
+// LSE base is resolved here, at the merge site, as the prhub.com.cn digest of
+// sgl-project/sglang PR 33926 notes under its related PRs). Bandwidth-bound:
+// one wave per (row, head) vector, each lane owning 8 consecutive elements,
+// so every shard's vector is read with one coalesced 16- or 32-byte load per
+// lane and the output written once.
+//
+// Metadata: the shard-local lengths and token-granular KV indices of the
+// rank's cyclic slice (prhub.com.cn digest of sgl-project/sglang PR 33926,
+// 关键源码片段: the DCP metadata helpers).
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+constexpr float kNegInf = -__builtin_inff();
+
+__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
+  const long long vec = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (vec >= p.vectors) return;
+  const int lane = threadIdx.x & 63;
+
+  float lse2[kMaxShards];
+  float mx = kNegInf;
+#pragma unroll
+  for (int r = 0; r < kMaxShards; ++r) {
+    if (r < p.num_shards) {
+      const float v = p.lses[r][vec];
+      lse2[r] = v * p.lse_to_log2[r];     // -inf stays -inf (multiplier > 0)
+      mx = fmaxf(mx, lse2[r]);
+    }
+  }
+  float w[kMaxShards];
+  float wsum = 0.f;
+#pragma unroll
+  for (int r = 0; r < kMaxShards; ++r) {
+    if (r < p.num_shards) {
+      w[r] = mx == kNegInf ? 0.f : __builtin_amdgcn_exp2f(lse2[r] - mx);
+      wsum += w[r];
+    }
+  }
+  const bool any = wsum > 0.f;
+  const float inv = any ? 1.f / wsum : 0.f;
+
+  for (int e0 = 8 * lane; e0 < p.dv; e0 += 512) {
+    f32x4_t a0 = f32x4_t{}, a1 = f32x4_t{};
+#pragma unroll
+    for (int r = 0; r < kMaxShards; ++r) {
+      if (r < p.num_shards && w[r] != 0.f) {
+        if (p.in_bf16) {
+          const bf16x8_t x = *(const bf16x8_t*)((const __bf16*)p.outs[r] + vec * p.dv + e0);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            a0[k] += w[r] * (float)x[k];
+            a1[k] += w[r] * (float)x[4 + k];
+          }
+        } else {
+          const f32x4_t* x = (const f32x4_t*)((const float*)p.outs[r] + vec * p.dv + e0);
+          a0 += w[r] * x[0];
+          a1 += w[r] * x[1];
+        }
+      }
+    }
+    a0 *= inv;
+    a1 *= inv;
+    if (p.out_bf16) {
+      bf16x8_t y;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        y[k] = (__bf16)a0[k];
+        y[4 + k] = (__bf16)a1[k];
+      }
+      *(bf16x8_t*)((__bf16*)p.out + vec * p.dv + e0) = y;
+    } else {
+      f32x4_t* y = (f32x4_t*)((float*)p.out + vec * p.dv + e0);
+      y[0] = a0;
+      y[1] = a1;
+    }
+  }
+  if (lane == 0 && p.lse_out != nullptr) {
+    const float l2 = any ? mx + __builtin_amdgcn_logf(wsum) : kNegInf;
+    p.lse_out[vec] = l2 * p.lse_out_from_log2;
+  }
+}
+
+__global__ __launch_bounds__(256) void metadata_kernel(const int32_t* seq_lens, const int32_t* block_table,
+                                                       int32_t batch, int32_t max_pages, int32_t shard,
+                                                       int32_t num_shards, int32_t* local_seq_lens,
+                                                       int32_t* local_kv_indices, int32_t stride) {
+  const long long total = local_kv_indices ? (long long)batch * stride : (long long)batch;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (long long)gridDim.x * blockDim.x) {
+    const int b = local_kv_indices ? (int)(e / stride) : (int)e;
+    const int j = local_kv_indices ? (int)(e % stride) : 0;
+    int L = seq_lens[b];
+    L = L < 0 ? 0 : L;
+    const int n = L / num_shards + (shard < L % num_shards ? 1 : 0);
+    if (j == 0) local_seq_lens[b] = n;
+    if (local_kv_indices) {
+      int v = -1;
+      if (j < n) {
+        const int t = j * num_shards + shard;
+        const int pg = t >> 6;
+        if (pg < max_pages) {
+          const int page = block_table[(long long)b * max_pages + pg];
+          v = page * kPage + (t & 63);
+        }
+      }
+      local_kv_indices[e] = v;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
+  if (p.vectors == 0) return hipSuccess;
+  const long long blocks = (p.vectors + 3) / 4;
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_metadata(const int32_t* seq_lens, const int32_t* block_table, int32_t batch,
+                           int32_t max_pages, int32_t shard, int32_t num_shards,
+                           int32_t* local_seq_lens, int32_t* local_kv_indices, int32_t stride,
+                           hipStream_t stream) {
+  if (batch == 0) return hipSuccess;
+  const long long total = local_kv_indices ? (long long)batch * stride : (long long)batch;
+  long long blocks = (total + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(metadata_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, seq_lens, block_table,
+                     batch, max_pages, shard, num_shards, local_seq_lens, local_kv_indices, stride);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,114 @@
+"""One sharded decode step on the GPU through the C ABI.
+
+A step is: for every shard r, the shard-local metadata (local lengths and
+KV row indices of the cyclic slice), the rank-local partial decode
+(out_r, lse_r), then the LSE-weighted merge of the S partials into the
+full-context result. PyTorch only allocates device memory; all arithmetic
+runs in the library's kernels.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+@dataclasses.dataclass
+class DeviceWorkload:
+    """Device copies of a workload's input bytes (and the scalars to use them)."""
+    batch: int
+    heads: int
+    q_len: int
+    shards: int
+    kv_fp8: bool
+    kv_scale: float
+    softmax_scale: float
+    lse_base: int
+    out_bf16: bool
+    max_seq_len: int
+    q: torch.Tensor            # [B, q_len, H, 576] bf16
+    kv_pages: torch.Tensor     # [P, 64, 576] bf16 | uint8
+    block_table: torch.Tensor  # [B, max_pages] i32
+    seq_lens: torch.Tensor     # [B] i32
+
+    @staticmethod
+    def upload(wl, device="cuda", out_dtype: Optional[str] = None) -> "DeviceWorkload":
+        q = torch.from_numpy(np.ascontiguousarray(wl.q)).view(torch.bfloat16).to(device)
+        if wl.kv_dtype == "bf16":
+            kv = torch.from_numpy(np.ascontiguousarray(wl.kv_pages)).view(torch.bfloat16).to(device)
+        else:
+            kv = torch.from_numpy(np.ascontiguousarray(wl.kv_pages)).to(device)
+        return DeviceWorkload(
+            batch=wl.batch, heads=wl.heads, q_len=wl.q_len, shards=wl.shards,
+            kv_fp8=wl.kv_dtype == "fp8", kv_scale=wl.kv_scale, softmax_scale=wl.softmax_scale,
+            lse_base=L.LSE_BASE_2 if wl.lse_base == "2" else L.LSE_BASE_E,
+            out_bf16=(out_dtype or wl.out_dtype) == "bf16", max_seq_len=wl.max_seq_len,
+            q=q, kv_pages=kv,
+            block_table=torch.from_numpy(np.ascontiguousarray(wl.block_table)).to(device),
+            seq_lens=torch.from_numpy(np.ascontiguousarray(wl.seq_lens)).to(device))
+
+    def local_max(self, shard: int) -> int:
+        M, S = self.max_seq_len, self.shards
+        return max(M // S + int(shard < M % S), 1)
+
+
+class StepBuffers:
+    """Outputs, metadata and workspace of one step, allocated once."""
+
+    def __init__(self, dw: DeviceWorkload, merged_out_bf16: Optional[bool] = None):
+        dev = dw.q.device
+        B, q, H, S = dw.batch, dw.q_len, dw.heads, dw.shards
+        odt = torch.bfloat16 if dw.out_bf16 else torch.float32
+        self.outs = [torch.empty((B, q, H, L.D_V), dtype=odt, device=dev) for _ in range(S)]
+        self.lses = [torch.empty((B, q, H), dtype=torch.float32, device=dev) for _ in range(S)]
+        mdt = odt if merged_out_bf16 is None else (torch.bfloat16 if merged_out_bf16 else torch.float32)
+        self.out = torch.empty((B, q, H, L.D_V), dtype=mdt, device=dev)
+        self.lse = torch.empty((B, q, H), dtype=torch.float32, device=dev)
+        self.local_seq_lens = [torch.empty((B,), dtype=torch.int32, device=dev) for _ in range(S)]
+        self.local_kv_indices = [torch.empty((B, dw.local_max(r)), dtype=torch.int32, device=dev)
+                                 for r in range(S)]
+        nbytes = L.mla_decode_workspace_bytes(B, H, q)
+        self.workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+
+    def fill_nan(self) -> None:
+        for t in self.outs + self.lses + [self.out, self.lse]:
+            t.fill_(float("nan"))
+
+
+def run_metadata(dw: DeviceWorkload, bufs: StepBuffers, shard: int, stream=None) -> int:
+    return L.mla_build_shard_metadata(dw.seq_lens, dw.block_table, dw.max_seq_len, shard, dw.shards,
+                                      bufs.local_seq_lens[shard], bufs.local_kv_indices[shard],
+                                      stream=stream)
+
+
+def run_partial(dw: DeviceWorkload, bufs: StepBuffers, shard: int, use_metadata: bool = True,
+                split_target: int = 0, events=None, stream=None) -> int:
+    return L.mla_decode_partial(
+        dw.q, dw.kv_pages, dw.block_table, dw.seq_lens, shard, dw.shards, dw.q_len,
+        bufs.outs[shard], bufs.lses[shard], bufs.workspace, kv_scale=dw.kv_scale,
+        softmax_scale=dw.softmax_scale, lse_base=dw.lse_base,
+        local_seq_lens=bufs.local_seq_lens[shard] if use_metadata else None,
+        local_kv_indices=bufs.local_kv_indices[shard] if use_metadata else None,
+        split_target=split_target, events=events, stream=stream)
+
+
+def run_merge(dw: DeviceWorkload, bufs: StepBuffers, out_base: int = L.LSE_BASE_E, stream=None) -> None:
+    N = dw.batch * dw.q_len
+    outs = [o.view(N, dw.heads, L.D_V) for o in bufs.outs]
+    lses = [l.view(N, dw.heads) for l in bufs.lses]
+    L.mla_merge_partials(outs, lses, [dw.lse_base] * dw.shards, bufs.out.view(N, dw.heads, L.D_V),
+                         bufs.lse.view(N, dw.heads), lse_out_base=out_base, stream=stream)
+
+
+def run_step(dw: DeviceWorkload, bufs: StepBuffers, use_metadata: bool = True, split_target: int = 0,
+             out_base: int = L.LSE_BASE_E, stream=None) -> None:
+    """Metadata, partial decode of every shard, then the merge."""
+    for r in range(dw.shards):
+        if use_metadata:
+            run_metadata(dw, bufs, r, stream=stream)
+        run_partial(dw, bufs, r, use_metadata=use_metadata, split_target=split_target, stream=stream)
+    run_merge(dw, bufs, out_base=out_base, stream=stream)

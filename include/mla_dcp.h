@@ -1,0 +1,220 @@
+/*
+ * mla_dcp.h -- C ABI of the MI355X (gfx950) paged MLA decode over a
+ * context-sharded KV cache, with the LSE-weighted merge of shard partials.
+ *
+ * Pages cited (address and section heading as printed):
+ *   [DCP decode] prhub.com.cn digest of sgl-project/sglang PR 33926 (the
+ *                trtllm_mla decode path gains DCP support); sections
+ *                "功能与动机" (motivation), "实现拆解" (implementation steps
+ *                1-4) and "关键源码片段" (key code: the DCP metadata helpers).
+ *   [symm_a2a]   github.com sgl-project/sglang PR 33364 "[Attention][DCP] Add
+ *                symm_a2a: single-node symmetric-memory A2A backend for MLA
+ *                decode"; sections Motivation and Modifications.
+ *   [next_n]     prhub.com.cn digest of vllm-project/vllm PR 52164 (native
+ *                next_n decode); section "功能与动机" (motivation).
+ *
+ * Conventions for every entry point:
+ *   - Device pointers point to memory on the current HIP device; the caller
+ *     owns every buffer (inputs, outputs and workspace). The library allocates
+ *     no device memory and keeps no state besides cached device properties.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
+ *     device work is enqueued asynchronously on it, with no host
+ *     synchronisation, so a call can be captured into a HIP graph.
+ *   - Failures return a status code; nothing unwinds across the ABI.
+ *     mla_last_error() returns a message for the calling thread's last
+ *     failure. Argument checks run before any device work, so an
+ *     INVALID_ARGUMENT / UNSUPPORTED return enqueues nothing.
+ *   - Geometry is MLA's: QK dim 576 (latent 512 + rope 64), V dim 512 = the
+ *     first 512 latent dims, page size 64 tokens.
+ *   - An empty shard or request is not an error: it yields (0, -inf).
+ */
+#ifndef MLA_DCP_H
+#define MLA_DCP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+#define MLA_PAGE_SIZE 64
+#define MLA_D_QK 576
+#define MLA_D_V 512
+#define MLA_MAX_SHARDS 16
+#define MLA_MAX_Q_LEN 4
+
+typedef enum mla_status {
+  MLA_STATUS_OK = 0,
+  MLA_STATUS_INVALID_ARGUMENT = 1,   /* null pointer, bad size, out-of-range id */
+  MLA_STATUS_UNSUPPORTED = 2,        /* well-formed but not implemented      */
+  MLA_STATUS_WORKSPACE_TOO_SMALL = 3,
+  MLA_STATUS_DEVICE_ERROR = 4        /* a HIP call or launch failed          */
+} mla_status_t;
+
+typedef enum mla_dtype {
+  MLA_DTYPE_F32 = 0,
+  MLA_DTYPE_BF16 = 1,
+  MLA_DTYPE_FP8_E4M3 = 2             /* OCP e4m3 ("fn"): bias 7, max 448, no inf */
+} mla_dtype_t;
+
+typedef enum mla_lse_base {
+  MLA_LSE_BASE_E = 0,                /* natural log                          */
+  MLA_LSE_BASE_2 = 1                 /* log2                                 */
+} mla_lse_base_t;
+
+/* ------------------------------------------------------------------------
+ * Shard-local metadata.
+ *
+ * Follows [DCP decode] key code (the rank-local length, rank-local max and
+ * page-table-on-the-cyclic-slice helpers) and motivation (token t of a
+ * request belongs to shard t mod S). For shard r of S and each request b of
+ * global length L_b = seq_lens[b]:
+ *   local_seq_lens[b]      = L_b / S + (r < L_b % S)        (tokens it owns)
+ *   local_kv_indices[b][j] = block_table[b][t / 64] * 64 + t % 64
+ *                            with t = j * S + r, for j < local_seq_lens[b];
+ *                            -1 for local_seq_lens[b] <= j < local_kv_stride
+ *   *local_max_out         = max(M / S + (r < M % S), 1) with M = max_seq_len
+ *                            (computed on the host, never 0).
+ * Layout: seq_lens [batch] i32 (device); block_table [batch][max_pages] i32
+ * (device, row-major); local_seq_lens [batch] i32 (device, written);
+ * local_kv_indices [batch][local_kv_stride] i32 (device, written; may be
+ * NULL to skip the index table); local_max_out (host, may be NULL).
+ * Preconditions (not checked on device): seq_lens[b] <= max_seq_len and
+ * seq_lens[b] <= max_pages * 64. local_kv_stride must be >= the local max.
+ * Errors: INVALID_ARGUMENT for null required pointers, batch < 0,
+ * num_shards < 1 or > MLA_MAX_SHARDS, shard_id outside [0, num_shards),
+ * page_size != 64, max_pages < 1, max_seq_len < 0, local_kv_stride < local
+ * max when local_kv_indices is given.
+ * ---------------------------------------------------------------------- */
+mla_status_t mla_build_shard_metadata(const int32_t* seq_lens, const int32_t* block_table,
+                                      int32_t batch, int32_t max_pages, int32_t page_size,
+                                      int32_t max_seq_len, int32_t shard_id, int32_t num_shards,
+                                      int32_t* local_seq_lens, int32_t* local_kv_indices,
+                                      int32_t local_kv_stride, int32_t* local_max_out,
+                                      void* stream);
+
+/* ------------------------------------------------------------------------
+ * Rank-local partial decode.
+ *
+ * Follows [DCP decode] motivation and implementation step 3: each shard
+ * attends over only the tokens it owns and returns its rank-local (out, lse);
+ * a row whose shard owns no visible token is written as the neutral state
+ * out = +0, lse = -inf. Implementation step 4 (first fix): kernels differ in
+ * LSE base; the base written is returned so the merge site can rebase.
+ * [next_n] motivation: q_len > 1 query rows of one request read each KV
+ * tile once, not once per row.
+ *
+ * For request b (global KV length L = seq_lens[b], which includes the q_len
+ * draft rows), query row i in [0, q_len) and head h:
+ *   visible owned tokens O = { t < L : t mod S == r, t <= L - q_len + i }
+ *   s_t = softmax_scale * sum_{d<576} Q[b,i,h,d] * K_t[d]
+ *   out[b,i,h,:] = sum_{t in O} exp(s_t) K_t[0:512] / sum_{t in O} exp(s_t)
+ *   lse[b,i,h]   = log sum_{t in O} exp(s_t)   in `lse_base`
+ * with K_t the latent row of token t (fp8 rows are multiplied by kv_scale).
+ * ---------------------------------------------------------------------- */
+typedef struct mla_decode_args {
+  /* inputs (device) */
+  const void* q;                 /* [batch][q_len][num_heads][576] bf16          */
+  const void* kv_pages;          /* [num_pages][64][576] bf16 or fp8 e4m3        */
+  const int32_t* block_table;    /* [batch][max_pages] i32, page ids             */
+  const int32_t* seq_lens;       /* [batch] i32, global KV length per request    */
+  /* optional shard metadata from mla_build_shard_metadata (both or neither):
+   * when given, KV rows are gathered through local_kv_indices instead of
+   * being derived from block_table. */
+  const int32_t* local_seq_lens;   /* [batch] i32 or NULL                        */
+  const int32_t* local_kv_indices; /* [batch][local_kv_stride] i32 or NULL       */
+  int32_t local_kv_stride;
+  /* sizes */
+  int32_t batch;
+  int32_t num_heads;             /* positive multiple of 16                       */
+  int32_t q_len;                 /* 1 .. MLA_MAX_Q_LEN                            */
+  int32_t max_pages;
+  int32_t num_pages;             /* page ids outside [0, num_pages) read as NaN   */
+  int32_t page_size;             /* must be 64                                    */
+  int32_t shard_id;
+  int32_t num_shards;
+  mla_dtype_t kv_dtype;          /* BF16 or FP8_E4M3                              */
+  float kv_scale;                /* per-tensor dequant scale (fp8); 1 for bf16    */
+  float softmax_scale;
+  mla_lse_base_t lse_base;       /* base requested for `lse`                      */
+  /* outputs (device) */
+  void* out;                     /* [batch][q_len][num_heads][512] f32 or bf16    */
+  mla_dtype_t out_dtype;         /* F32 or BF16                                   */
+  float* lse;                    /* [batch][q_len][num_heads] f32, required       */
+  /* scratch (device), size from mla_decode_workspace_bytes */
+  void* workspace;
+  size_t workspace_bytes;
+  /* tuning: number of KV chunks to split a launch into per row block
+   * (0 = derived from the device's compute-unit count) */
+  int32_t split_target;
+  /* optional hipEvent_t pair recorded around the main attention kernel
+   * (NULL = none); for timing that kernel alone */
+  void* event_begin;
+  void* event_end;
+} mla_decode_args_t;
+
+/* Bytes of workspace mla_decode_partial needs for these sizes (host only,
+ * no device call). Returns 0 for invalid sizes. */
+size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t q_len);
+
+/* Errors: INVALID_ARGUMENT for a null q / kv_pages / block_table / seq_lens /
+ * out / lse / workspace, only one of the two metadata pointers, batch < 0,
+ * num_heads not a positive multiple of 16, q_len outside [1, 4],
+ * page_size != 64, bad shard ids, num_pages < 1, max_pages < 1, a dtype
+ * other than those listed; WORKSPACE_TOO_SMALL; DEVICE_ERROR if a launch
+ * fails. `lse_base_written` (host, may be NULL) receives the base of `lse`,
+ * which is always the requested one. */
+mla_status_t mla_decode_partial(const mla_decode_args_t* args, mla_lse_base_t* lse_base_written,
+                                void* stream);
+
+/* ------------------------------------------------------------------------
+ * Cross-shard merge.
+ *
+ * Follows [symm_a2a] Modifications, fourth kernel (LSE-weighted softmax
+ * reduction over all ranks' partial outputs; also the correction/combine
+ * steps of the ag_rs and a2a backends under Motivation) and [DCP decode]'s
+ * note that the LSE base is handled at the merge site. With lse_r rebased to
+ * a common base, M = max_r lse_r and w_r = exp(lse_r - M):
+ *   out = sum_r w_r out_r / sum_r w_r,  lse = M + log sum_r w_r.
+ * Rows where every shard is neutral (lse_r = -inf) give out = 0, lse = -inf.
+ * Layout: outs[r] -> [rows][num_heads][dv] (in_dtype), lses[r] -> [rows]
+ * [num_heads] f32 in bases[r]; out -> [rows][num_heads][dv] (out_dtype);
+ * lse_out -> [rows][num_heads] f32 in lse_out_base, or NULL.
+ * `outs`, `lses` and `bases` are host arrays of num_shards entries.
+ * Errors: INVALID_ARGUMENT for null arrays / pointers, num_shards outside
+ * [1, MLA_MAX_SHARDS], rows < 0, num_heads < 1, dv not a positive multiple of
+ * 8, dtypes other than F32 / BF16; DEVICE_ERROR if the launch fails.
+ * ---------------------------------------------------------------------- */
+typedef struct mla_merge_args {
+  const void* const* outs;
+  const float* const* lses;
+  const mla_lse_base_t* bases;
+  int32_t num_shards;
+  int32_t rows;                  /* decode tokens (query rows)                  */
+  int32_t num_heads;
+  int32_t dv;
+  mla_dtype_t in_dtype;
+  void* out;
+  mla_dtype_t out_dtype;
+  float* lse_out;
+  mla_lse_base_t lse_out_base;
+} mla_merge_args_t;
+
+mla_status_t mla_merge_partials(const mla_merge_args_t* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Introspection.
+ * ---------------------------------------------------------------------- */
+const char* mla_status_string(mla_status_t status);
+const char* mla_last_error(void);
+int32_t mla_abi_version(void);
+/* sizeof the argument structs as compiled, for binding layout checks */
+size_t mla_sizeof_decode_args(void);
+size_t mla_sizeof_merge_args(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_DCP_H */

@@ -1,0 +1,131 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, its argument structs match the binding, and invalid arguments
+return status codes before any device work (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_attention_paged_amd import _lib as L
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mla_dcp.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        from decode_attention_paged_amd import build
+        build.build()
+    return L.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert "mla_decode_partial" in names and "mla_merge_partials" in names
+    assert "mla_build_shard_metadata" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(L.EXPORTS) <= set(names)
+
+
+def test_struct_layouts_and_version(lib):
+    assert lib.mla_sizeof_decode_args() == ctypes.sizeof(L.DecodeArgs)
+    assert lib.mla_sizeof_merge_args() == ctypes.sizeof(L.MergeArgs)
+    assert lib.mla_abi_version() == 1
+    assert lib.mla_status_string(L.STATUS_INVALID_ARGUMENT) == b"invalid argument"
+
+
+def test_workspace_size_is_host_only(lib):
+    n = lib.mla_decode_workspace_bytes(128, 128, 1)
+    assert n > 128 * 128 * 512 * 4
+    assert lib.mla_decode_workspace_bytes(4, 17, 1) == 0       # heads not a multiple of 16
+    assert lib.mla_decode_workspace_bytes(4, 16, 5) == 0       # q_len > 4
+    assert lib.mla_decode_workspace_bytes(2, 16, 4) < lib.mla_decode_workspace_bytes(2, 32, 4)
+
+
+def _valid_args():
+    a = L.DecodeArgs()
+    fake = 0x1000
+    a.q = a.kv_pages = a.block_table = a.seq_lens = a.out = a.lse = a.workspace = fake
+    a.batch, a.num_heads, a.q_len = 2, 16, 1
+    a.max_pages, a.num_pages, a.page_size = 4, 8, 64
+    a.shard_id, a.num_shards = 0, 4
+    a.kv_dtype, a.out_dtype = L.DTYPE_BF16, L.DTYPE_F32
+    a.kv_scale, a.softmax_scale = 1.0, 0.07
+    a.lse_base = L.LSE_BASE_E
+    a.workspace_bytes = 0
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_heads", 24, L.STATUS_INVALID_ARGUMENT),
+    ("num_heads", 0, L.STATUS_INVALID_ARGUMENT),
+    ("q_len", 0, L.STATUS_INVALID_ARGUMENT),
+    ("q_len", 5, L.STATUS_INVALID_ARGUMENT),
+    ("page_size", 32, L.STATUS_INVALID_ARGUMENT),
+    ("shard_id", 4, L.STATUS_INVALID_ARGUMENT),
+    ("shard_id", -1, L.STATUS_INVALID_ARGUMENT),
+    ("num_shards", 0, L.STATUS_INVALID_ARGUMENT),
+    ("num_shards", 17, L.STATUS_INVALID_ARGUMENT),
+    ("batch", -1, L.STATUS_INVALID_ARGUMENT),
+    ("kv_dtype", L.DTYPE_F32, L.STATUS_INVALID_ARGUMENT),
+    ("out_dtype", L.DTYPE_FP8_E4M3, L.STATUS_INVALID_ARGUMENT),
+    ("lse", None, L.STATUS_INVALID_ARGUMENT),
+    ("softmax_scale", 0.0, L.STATUS_INVALID_ARGUMENT),
+    ("num_pages", 0, L.STATUS_INVALID_ARGUMENT),
+    ("local_seq_lens", 0x2000, L.STATUS_INVALID_ARGUMENT),     # without local_kv_indices
+    ("split_target", 100000, L.STATUS_INVALID_ARGUMENT),
+    ("workspace_bytes", 0, L.STATUS_WORKSPACE_TOO_SMALL),
+])
+def test_decode_argument_errors(lib, field, value, status):
+    a = _valid_args()
+    setattr(a, field, value)
+    st = lib.mla_decode_partial(ctypes.byref(a), None, None)
+    assert st == status, lib.mla_last_error()
+    assert lib.mla_last_error()
+
+
+def test_empty_batch_is_ok_without_device(lib):
+    a = _valid_args()
+    a.batch = 0
+    written = ctypes.c_int(-1)
+    assert lib.mla_decode_partial(ctypes.byref(a), ctypes.byref(written), None) == L.STATUS_OK
+    assert written.value == L.LSE_BASE_E
+
+
+def test_metadata_argument_errors(lib):
+    i32 = ctypes.c_int32
+    lmax = i32(0)
+    f = 0x1000
+    assert lib.mla_build_shard_metadata(f, f, 2, 4, 64, 100, 4, 4, f, f, 40, ctypes.byref(lmax), None) \
+        == L.STATUS_INVALID_ARGUMENT                       # shard_id == num_shards
+    assert lib.mla_build_shard_metadata(f, f, 2, 4, 32, 100, 0, 4, f, f, 40, ctypes.byref(lmax), None) \
+        == L.STATUS_INVALID_ARGUMENT                       # page size
+    assert lib.mla_build_shard_metadata(f, f, 2, 4, 64, 100, 0, 4, f, f, 24, ctypes.byref(lmax), None) \
+        == L.STATUS_INVALID_ARGUMENT                       # stride below local max 25
+    assert lib.mla_build_shard_metadata(f, f, 0, 4, 64, 0, 3, 4, None, None, 0, ctypes.byref(lmax), None) \
+        == L.STATUS_OK                                     # empty batch: only the host local max
+    assert lmax.value == 1
+
+
+def test_merge_argument_errors(lib):
+    a = L.MergeArgs()
+    a.num_shards, a.rows, a.num_heads, a.dv = 0, 1, 1, 512
+    assert lib.mla_merge_partials(ctypes.byref(a), None) == L.STATUS_INVALID_ARGUMENT
+    a.num_shards = 2
+    assert lib.mla_merge_partials(ctypes.byref(a), None) == L.STATUS_INVALID_ARGUMENT   # null arrays
+    outs = (ctypes.c_void_p * 2)(0x1000, None)
+    lses = (ctypes.c_void_p * 2)(0x1000, 0x1000)
+    bases = (ctypes.c_int * 2)(0, 1)
+    a.outs, a.lses, a.bases = outs, lses, bases
+    a.out = 0x1000
+    assert lib.mla_merge_partials(ctypes.byref(a), None) == L.STATUS_INVALID_ARGUMENT   # null shard out
+    a.dv = 500
+    assert lib.mla_merge_partials(ctypes.byref(a), None) == L.STATUS_INVALID_ARGUMENT

@@ -1,0 +1,272 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Inputs are the seeded workloads of ``workloads`` (the five workload shapes,
+scaled down so the oracle finishes in seconds while still spanning several
+32-token tiles, several KV chunks per request and ragged tails; the full
+sizes are checked on sampled requests in test_gpu_fullsize.py). Outputs are
+pre-filled with NaN so an unwritten row fails.
+Tolerances: out and LSE max-abs 2e-2 (bf16 KV) / 6e-2 (fp8 KV), LSE in nats;
+neutral rows exactly (+0, -inf); merge 1e-5 relative (fp32) or within one
+bf16 ulp of the rounded oracle; metadata bit-exact.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as U
+from oracle import mla_oracle as O
+from workloads import make_config, make_merge_inputs, make_workload
+
+pytestmark = pytest.mark.gpu
+
+if U.gpu_available():
+    from decode_attention_paged_amd import _lib as L
+    from decode_attention_paged_amd import step as ST
+
+
+def _flush(msg):
+    print(msg, flush=True)
+
+
+# scaled-down instances of the five workload shapes
+SMALL = {
+    "tiny": dict(index=1),
+    "kimi_like": dict(index=2, batch=3, lens=("uniform", 300, 700)),
+    "deepseek_like_fp8": dict(index=3, batch=2, lens=("uniform", 700, 1500)),
+    "mtp_q4": dict(index=4, batch=2, lens=("uniform", 100, 400)),
+    "skewed": dict(index=5, batch=14, lens=("skewed", 1, 1500)),
+}
+
+
+def _small(name, **extra):
+    spec = dict(SMALL[name])
+    idx = spec.pop("index")
+    spec.update(extra)
+    return make_config(idx, **spec)
+
+
+# --------------------------------------------------------------------------
+# metadata
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 8])
+def test_metadata_bit_exact(S):
+    rng = np.random.default_rng(100 + S)
+    B = 9
+    seq_lens = rng.integers(0, 400, size=B).astype(np.int32)
+    seq_lens[0] = 0
+    seq_lens[1] = 1
+    maxp = int(max(1, ((seq_lens.max() + 63) // 64)))
+    npages = int(sum((L_ + 63) // 64 for L_ in seq_lens))
+    perm = rng.permutation(max(npages, 1)).astype(np.int32)
+    bt = np.full((B, maxp), -1, np.int32)
+    off = 0
+    for b, L_ in enumerate(seq_lens):
+        k = (int(L_) + 63) // 64
+        bt[b, :k] = perm[off:off + k]
+        off += k
+    M = int(seq_lens.max())
+    d_sl = torch.from_numpy(seq_lens).cuda()
+    d_bt = torch.from_numpy(bt).cuda()
+    for r in range(S):
+        _flush(f"metadata S={S} r={r}")
+        lens, lmax, idx = O.shard_metadata(seq_lens, bt, 64, M, r, S)
+        out_l = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+        out_i = torch.full((B, lmax + 3), -7, dtype=torch.int32, device="cuda")
+        got_max = L.mla_build_shard_metadata(d_sl, d_bt, M, r, S, out_l, out_i)
+        torch.cuda.synchronize()
+        assert got_max == lmax
+        assert np.array_equal(out_l.cpu().numpy(), lens)
+        gi = out_i.cpu().numpy()
+        assert np.array_equal(gi[:, :lmax], idx)
+        assert (gi[:, lmax:] == -1).all()
+
+
+def test_metadata_pages_sweep():
+    """The pages' layout sweep (sizes 1,2,3,4,8; lengths 0..40) as one batch."""
+    lens = np.arange(0, 41, dtype=np.int32)
+    bt = np.zeros((41, 1), np.int32)
+    d_sl, d_bt = torch.from_numpy(lens).cuda(), torch.from_numpy(bt).cuda()
+    for S in (1, 2, 3, 4, 8):
+        tot = np.zeros(41, np.int64)
+        per = []
+        for r in range(S):
+            out_l = torch.empty((41,), dtype=torch.int32, device="cuda")
+            L.mla_build_shard_metadata(d_sl, d_bt, 40, r, S, out_l, None)
+            torch.cuda.synchronize()
+            got = out_l.cpu().numpy().astype(np.int64)
+            per.append(got)
+            tot += got
+        assert np.array_equal(tot, lens)
+        for Lg in range(1, 41):
+            grew = [int(per[r][Lg] - per[r][Lg - 1]) for r in range(S)]
+            assert sum(grew) == 1 and grew[(Lg - 1) % S] == 1
+
+
+# --------------------------------------------------------------------------
+# partial decode, per shard
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("use_metadata", [True, False])
+@pytest.mark.parametrize("split_target", [0, 1, 37])
+def test_partial_parity(name, use_metadata, split_target):
+    wl = _small(name)
+    dw = ST.DeviceWorkload.upload(wl)
+    bufs = ST.StepBuffers(dw)
+    bufs.fill_nan()
+    tol = U.TOL[wl.kv_dtype]
+    for r in range(wl.shards):
+        _flush(f"partial {name} meta={use_metadata} split={split_target} shard={r}/{wl.shards}")
+        if use_metadata:
+            ST.run_metadata(dw, bufs, r)
+        base = ST.run_partial(dw, bufs, r, use_metadata=use_metadata, split_target=split_target)
+        assert base == dw.lse_base
+        torch.cuda.synchronize()
+        ref_o, ref_l = O.decode_partial(wl, r, wl.shards, wl.lse_base)
+        U.assert_partial_close(bufs.outs[r], bufs.lses[r], ref_o, ref_l, wl.lse_base, tol,
+                               f"{name} shard {r}")
+
+
+def test_partial_bf16_output():
+    wl = _small("kimi_like")
+    dw = ST.DeviceWorkload.upload(wl, out_dtype="bf16")
+    bufs = ST.StepBuffers(dw)
+    bufs.fill_nan()
+    for r in range(wl.shards):
+        ST.run_metadata(dw, bufs, r)
+        ST.run_partial(dw, bufs, r, split_target=5)
+        torch.cuda.synchronize()
+        ref_o, ref_l = O.decode_partial(wl, r, wl.shards, wl.lse_base)
+        assert bufs.outs[r].dtype == torch.bfloat16
+        U.assert_partial_close(bufs.outs[r], bufs.lses[r], ref_o, ref_l, wl.lse_base, 2e-2, f"bf16 out shard {r}")
+
+
+def test_empty_shards_are_exactly_neutral():
+    # lengths 1..7 with S = 8: shards >= L own nothing
+    wl = make_workload("short", batch=8, heads=32, q_len=1, shards=8, kv_dtype="bf16",
+                       lens=("fixed", (1, 2, 3, 4, 5, 6, 7, 0)), seed=5, lse_base="2")
+    dw = ST.DeviceWorkload.upload(wl)
+    bufs = ST.StepBuffers(dw)
+    bufs.fill_nan()
+    ST.run_step(dw, bufs)
+    torch.cuda.synchronize()
+    for r in range(8):
+        lse = bufs.lses[r].cpu().numpy()
+        out = bufs.outs[r].cpu().numpy()
+        for b, Lb in enumerate(wl.seq_lens):
+            if r >= Lb:
+                assert np.all(np.isneginf(lse[b])) and np.all(out[b] == 0) and not np.signbit(out[b]).any()
+            else:
+                assert np.all(np.isfinite(lse[b]))
+    # the request of length 0 merges to (0, -inf)
+    mo, ml = bufs.out.cpu().numpy(), bufs.lse.cpu().numpy()
+    assert np.all(mo[7] == 0) and np.all(np.isneginf(ml[7]))
+    ref_o, ref_l, _ = O.decode_step(wl)
+    U.assert_partial_close(bufs.out, bufs.lse, ref_o, ref_l, "e", 2e-2, "merged short")
+
+
+def test_bad_page_ids_poison_instead_of_faulting():
+    wl = make_workload("bad", batch=2, heads=16, q_len=1, shards=1, kv_dtype="bf16",
+                       lens=("fixed", (100, 50)), seed=9)
+    wl.block_table[0, 1] = 10_000          # outside the pool
+    dw = ST.DeviceWorkload.upload(wl)
+    bufs = ST.StepBuffers(dw)
+    ST.run_partial(dw, bufs, 0, use_metadata=False)
+    torch.cuda.synchronize()
+    o = bufs.outs[0].cpu().numpy()
+    assert np.isnan(o[0]).any()            # request 0 reads a bad page -> NaN
+    assert not np.isnan(o[1]).any()        # request 1 unaffected
+
+
+# --------------------------------------------------------------------------
+# whole step: metadata -> partials -> merge
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name", list(SMALL))
+def test_step_parity(name):
+    wl = _small(name)
+    dw = ST.DeviceWorkload.upload(wl)
+    bufs = ST.StepBuffers(dw)
+    bufs.fill_nan()
+    _flush(f"step {name}")
+    ST.run_step(dw, bufs)
+    torch.cuda.synchronize()
+    ref_o, ref_l, _ = O.decode_step(wl)
+    U.assert_partial_close(bufs.out, bufs.lse, ref_o, ref_l, "e", U.TOL[wl.kv_dtype], f"step {name}")
+    full_o, full_l = O.decode_full(wl)
+    U.assert_partial_close(bufs.out, bufs.lse, full_o, full_l, "e", U.TOL[wl.kv_dtype], f"unsharded {name}")
+
+
+def test_step_is_deterministic():
+    wl = _small("skewed")
+    dw = ST.DeviceWorkload.upload(wl)
+    a, b = ST.StepBuffers(dw), ST.StepBuffers(dw)
+    ST.run_step(dw, a)
+    ST.run_step(dw, b)
+    torch.cuda.synchronize()
+    assert torch.equal(a.out.view(torch.int32), b.out.view(torch.int32))
+    assert torch.equal(a.lse.view(torch.int32), b.lse.view(torch.int32))
+
+
+# --------------------------------------------------------------------------
+# merge
+# --------------------------------------------------------------------------
+def _merge_ref(mi):
+    outs = [O.decode_bf16(o) if o.dtype == np.uint16 else o.astype(np.float64) for o in mi.outs]
+    return O.merge(outs, [l.astype(np.float64) for l in mi.lses], mi.bases)
+
+
+@pytest.mark.parametrize("T", [1, 8, 16, 32, 64, 128])
+def test_merge_bf16_parity(T):
+    mi = make_merge_inputs(T, neutral_frac=0.05, seed=3000 + T)
+    outs = [torch.from_numpy(o).view(torch.bfloat16).cuda() for o in mi.outs]
+    lses = [torch.from_numpy(l).cuda() for l in mi.lses]
+    out = torch.full((T, 64, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((T, 64), float("nan"), dtype=torch.float32, device="cuda")
+    L.mla_merge_partials(outs, lses, [L.LSE_BASE_E] * 4, out, lse)
+    torch.cuda.synchronize()
+    ro, rl = _merge_ref(mi)
+    go = U.to_np(out)
+    assert np.all(np.abs(go - ro) <= U.bf16_ulp(ro) + 1e-30), "bf16 merge beyond one ulp"
+    gl = U.to_np(lse)
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isneginf(gl), np.isneginf(rl))
+    assert np.all(np.abs(gl[fin] - rl[fin]) <= 1e-5 * np.maximum(1.0, np.abs(rl[fin])))
+
+
+@pytest.mark.parametrize("bases", [("e", "e", "e"), ("2", "e", "2"), ("2", "2", "2")])
+def test_merge_fp32_relative(bases):
+    mi = make_merge_inputs(24, shards=3, heads=16, dv=512, dtype="f32", bases=bases,
+                           neutral_frac=0.1, seed=77)
+    outs = [torch.from_numpy(o).cuda() for o in mi.outs]
+    lses = [torch.from_numpy(l).cuda() for l in mi.lses]
+    code = {"e": L.LSE_BASE_E, "2": L.LSE_BASE_2}
+    out = torch.full((24, 16, 512), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((24, 16), float("nan"), dtype=torch.float32, device="cuda")
+    L.mla_merge_partials(outs, lses, [code[b] for b in bases], out, lse, lse_out_base=L.LSE_BASE_2)
+    torch.cuda.synchronize()
+    ro, rl = _merge_ref(mi)
+    go = U.to_np(out)
+    scale = np.maximum(np.abs(ro).max(axis=-1, keepdims=True), 1e-30)
+    assert np.all(np.abs(go - ro) <= 1e-5 * scale)
+    gl = U.to_np(lse) * math.log(2)       # requested base 2
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isneginf(gl), np.isneginf(rl))
+    assert np.all(np.abs(gl[fin] - rl[fin]) <= 1e-5 * np.maximum(1.0, np.abs(rl[fin])))
+
+
+def test_merge_single_shard_and_neutral_extra():
+    mi = make_merge_inputs(4, shards=1, heads=8, dtype="f32", seed=5)
+    o = torch.from_numpy(mi.outs[0]).cuda()
+    l = torch.from_numpy(mi.lses[0]).cuda()
+    out = torch.empty_like(o)
+    lse = torch.empty_like(l)
+    L.mla_merge_partials([o], [l], [L.LSE_BASE_E], out, lse)
+    z_o = torch.zeros_like(o)
+    z_l = torch.full_like(l, float("-inf"))
+    out2 = torch.empty_like(o)
+    lse2 = torch.empty_like(l)
+    L.mla_merge_partials([o, z_o], [l, z_l], [L.LSE_BASE_E] * 2, out2, lse2)
+    torch.cuda.synchronize()
+    assert torch.allclose(out, o, rtol=1e-6, atol=0)
+    assert torch.equal(out2, out) and torch.equal(lse2, lse)
