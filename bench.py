@@ -50,6 +50,41 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
+class HipEvent:
+    """A hipEvent_t created through the HIP runtime (timing enabled), so the
+    library can record it around one kernel launch on the caller's stream."""
+    _hip = None
+
+    @classmethod
+    def _rt(cls):
+        if cls._hip is None:
+            import ctypes
+            import torch  # noqa: F401  (loads the HIP runtime)
+            cls._hip = ctypes.CDLL("libamdhip64.so")
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self.handle = ctypes.c_void_p()
+        if self._rt().hipEventCreate(ctypes.byref(self.handle)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        self.cuda_event = self.handle.value
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        err = self._rt().hipEventElapsedTime(ctypes.byref(ms), self.handle, end.handle)
+        if err != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({err})")
+        return float(ms.value)
+
+    def __del__(self):
+        try:
+            self._rt().hipEventDestroy(self.handle)
+        except Exception:
+            pass
+
+
 # --------------------------------------------------------------------------
 # algorithmic work of a workload
 # --------------------------------------------------------------------------
@@ -105,7 +140,7 @@ def traffic_from_profile(workload: str):
 # --------------------------------------------------------------------------
 # GPU timing
 # --------------------------------------------------------------------------
-def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True):
+def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True, split_target: int = 0):
     import torch
 
     from decode_attention_paged_amd import step as ST
@@ -121,15 +156,14 @@ def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True):
         dws.append(dataclasses.replace(d0, q=d0.q.clone(), kv_pages=d0.kv_pages.clone()))
     bufs = ST.StepBuffers(dws[0])
     S = wl.shards
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(S)]
-          for _ in range(steps)]
+    ev = [[(HipEvent(), HipEvent()) for _ in range(S)] for _ in range(steps)]
     mev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
 
     def one_step(k, timed):
         dw = dws[k % len(dws)]
         for r in range(S):
             ST.run_metadata(dw, bufs, r)
-            ST.run_partial(dw, bufs, r, events=ev[k][r] if timed else None)
+            ST.run_partial(dw, bufs, r, split_target=split_target, events=ev[k][r] if timed else None)
         if timed:
             mev[k][0].record()
         ST.run_merge(dw, bufs)
@@ -147,7 +181,7 @@ def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = 1e3 * elapsed / steps
-    attn_ms = [[ev[k][r][0].elapsed_time(ev[k][r][1]) for r in range(S)] for k in range(steps)]
+    attn_ms = [[ev[k][r][0].elapsed_ms(ev[k][r][1]) for r in range(S)] for k in range(steps)]
     merge_ms = [mev[k][0].elapsed_time(mev[k][1]) for k in range(steps)]
     tot_bytes = sum(b for b, _ in per_shard)
     tot_flops = sum(f for _, f in per_shard)
@@ -252,6 +286,10 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-merge-sweep", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--split-target", type=int, default=0,
+                    help="KV chunks per launch per row block (0 = library default)")
+    ap.add_argument("--sweep-split", default=None,
+                    help="comma list of split targets to time on the headline workload (details only)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -266,8 +304,14 @@ def main() -> int:
     from decode_attention_paged_amd import _lib as L
     L.load()
 
-    wl, res = bench_workload(args.config, args.steps, args.warmup)
+    wl, res = bench_workload(args.config, args.steps, args.warmup, split_target=args.split_target)
     details = {"headline": res}
+    if args.sweep_split:
+        for tgt in [int(x) for x in args.sweep_split.split(",")]:
+            _, r = bench_workload(args.config, args.steps, args.warmup, split_target=tgt)
+            details[f"split{tgt}"] = r
+            log(f"[bench] split {tgt}: {r['ms_per_step']:.3f} ms/step, attn {r['attn_kernel_mean_us']:.1f} us "
+                f"({100 * r['attn_kernel_hbm_frac']:.1f}% HBM)")
     merge = None if args.no_merge_sweep else bench_merge_sweep()
     if merge:
         details["merge_only"] = merge

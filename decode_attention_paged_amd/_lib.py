@@ -88,6 +88,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
+    # PyTorch ships its own HIP runtime; loading it first makes the library
+    # bind to that same runtime (one runtime per process)
+    import torch  # noqa: F401
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m decode_attention_paged_amd.build`")
     lib = ctypes.CDLL(path)

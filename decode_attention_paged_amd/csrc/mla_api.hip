@@ -1,7 +1,7 @@
 // Host side of the C ABI declared in include/mla_dcp.h: argument checks,
 // workspace layout, launch configuration and error reporting. Every check
 // runs before any device work is enqueued.
-#include "../../include/mla_dcp.h"
+#include "mla_dcp.h"
 #include "mla_internal.h"
 
 #include <math.h>
@@ -182,7 +182,10 @@ mla_status_t mla_decode_partial(const mla_decode_args_t* a, mla_lse_base_t* lse_
   const int32_t row_blocks = (rows + mla::kRowsPerBlock - 1) / mla::kRowsPerBlock;
   int32_t target = a->split_target;
   if (target == 0) {
-    target = cus / row_blocks;
+    // workgroups of up to two waves fit twice per CU (LDS), larger ones once
+    const int32_t rows_per_block = rows < mla::kRowsPerBlock ? rows : mla::kRowsPerBlock;
+    const int32_t per_cu = rows_per_block <= 64 ? 2 : 1;
+    target = cus * per_cu / row_blocks;
     if (target < 1) target = 1;
   }
   if (target > mla::kSplitTargetMax) target = mla::kSplitTargetMax;

@@ -442,6 +442,329 @@ void attn_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 KV: direct HBM -> LDS tiles, V^T read with transposing LDS loads
+// ---------------------------------------------------------------------------
+// A stage holds one 32-token tile chunk-major: 16-byte chunk c (dims
+// 8c .. 8c+7) of tile token t sits at slot 32 c + (t ^ 4 (c & 3)).
+//  * global_load_lds_dwordx4 moves 64 consecutive slots (1 KB) per
+//    instruction = chunks 2q, 2q+1 of all 32 tokens, each lane keeping one
+//    token, so a tile needs two row lookups per lane;
+//  * the QK A operand (lane = token, 8 dims) of k-step kk is the contiguous
+//    1 KB of chunks 2kk, 2kk+1;
+//  * the PV A operand (V^T: lane = dim, 8 tokens) comes from two
+//    ds_read_b64_tr_b16: in each 16-lane group, lane 4r + s supplies dims
+//    4s .. 4s+3 of token r and lane i receives dim i of the four tokens (a
+//    4 x 16 transpose), so V is never copied; the XOR term puts the four
+//    chunks a 32-lane half reads in distinct 64-byte bank segments.
+constexpr int kKTileBytes = kTile * kDqk * 2;   // 36864
+constexpr int kDirectStages = 2;
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i16x4_t lds_read_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)p);
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(size_t)((__attribute__((address_space(3))) const void*)p);
+}
+
+// global_load_lds_dwordx4: 16 bytes per lane from `src` into LDS at
+// lds_base + 16 * lane. Issued as inline assembly so that the compiler's
+// wait-count bookkeeping does not treat every later LDS read as dependent on
+// it (it would wait for the load before reading the other stage). Only the
+// stage that no wave reads until the next barrier is ever the destination,
+// and the caller waits for completion explicitly (s_waitcnt vmcnt(0) +
+// barrier) before any wave reads it; volatile asm is not moved across those
+// barriers. M0 holds the LDS base (one wait state after writing it).
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_base));
+}
+
+// Row indices of a tile are fetched one iteration before they are used and
+// validated only after the loop-top wait, so fetching them never forces a wait
+// on the KV loads in flight. Lanes 0..31 hold token jt + lane.
+constexpr int kRowPastEnd = -2;   // token past the chunk end: loads row 0, masked
+constexpr int kRowBad = -1;       // page outside the pool: loads row 0, score NaN
+
+__device__ __forceinline__ int fetch_row_raw(const DecodeParams& p, int b, int jt, int j1, int lane) {
+  if (lane >= kTile || jt + lane >= j1) return INT_MIN;
+  const int j = jt + lane;
+  if (p.local_kv_indices != nullptr) return p.local_kv_indices[(long long)b * p.local_kv_stride + j];
+  const int t = j * p.num_shards + p.shard;
+  return p.block_table[(long long)b * p.max_pages + (t >> 6)];
+}
+
+__device__ __forceinline__ int resolve_row(const DecodeParams& p, int raw, int jt, int lane) {
+  if (raw == INT_MIN) return kRowPastEnd;
+  long long row;
+  if (p.local_kv_indices != nullptr) {
+    row = raw;
+  } else {
+    const int t = (jt + lane) * p.num_shards + p.shard;
+    row = (raw < 0 || raw >= p.num_pages) ? -1 : (long long)raw * kPage + (t & 63);
+  }
+  return (row < 0 || row >= (long long)p.num_pages * kPage) ? kRowBad : (int)row;
+}
+
+// Direct loads of one tile into a stage. Block q (1 KB) of the stage holds
+// chunks 2q + hi of tokens (lane % 32) ^ 4 (c & 3); `my_row` is the row of
+// token (lane % 32) of the tile, valid in lanes 0..31. prepare() fetches the
+// two source rows this lane needs; issue(i) sends the wave's i-th block.
+template <int kNW>
+struct TileDma {
+  static constexpr int kBlocks = kKTileBytes / 1024;   // 36 instructions of 1 KB
+  static constexpr int kPerWave = kBlocks / kNW;
+  const uint8_t* src_even;
+  const uint8_t* src_odd;
+  uint32_t lds0;
+
+  __device__ __forceinline__ void prepare(const DecodeParams& p, const uint8_t* stage, int my_row) {
+    const int lane = threadIdx.x & 63, hi = lane >> 5;
+    const int r_even = __shfl(my_row, (lane & 31) ^ (4 * hi));
+    const int r_odd = __shfl(my_row, (lane & 31) ^ (8 + 4 * hi));
+    src_even = p.kv + (long long)(r_even >= 0 ? r_even : 0) * (2 * kDqk) + 16 * hi;
+    src_odd = p.kv + (long long)(r_odd >= 0 ? r_odd : 0) * (2 * kDqk) + 16 * hi;
+    lds0 = __builtin_amdgcn_readfirstlane(lds_address(stage));
+  }
+  __device__ __forceinline__ void issue(int i) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int q = wave * kPerWave + i;
+    // the parity of q selects the source row (c & 3 = 2 (q & 1) + hi)
+    const uint8_t* src = ((kPerWave & 1) == 0 ? (i & 1) : (q & 1)) ? src_odd : src_even;
+    lds_dma16(src + 32 * q, __builtin_amdgcn_readfirstlane(lds0 + 1024 * q));
+  }
+  __device__ __forceinline__ void issue_all() const {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) issue(i);
+  }
+};
+
+// PV A operand of step st = 2 db + m: dims 32 db .. + 31 of tokens
+// 16 m .. 16 m + 15 (two transposing loads of four tokens each).
+__device__ __forceinline__ bf16x8_t pv_operand(const uint8_t* ks, const uint32_t (&pv_base)[2], int st) {
+  const int db = st >> 1, m = st & 1;
+  const i16x4_t lo = lds_read_tr16(ks + pv_base[0] + 2048 * db + 256 * m);
+  const i16x4_t hi = lds_read_tr16(ks + pv_base[1] + 2048 * db + 256 * m);
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int kNW>
+__global__ __launch_bounds__(64 * kNW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_direct_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kDirectStages * kKTileBytes];
+  // the last kQInLds k-steps of each lane's Q operands live in LDS rather than
+  // VGPRs (read back once per tile), which keeps the tile loop free of spills
+  constexpr int kQInLds = kNW <= 2 ? 3 : 2;
+  constexpr int kQRegSteps = kDqk / 16 - kQInLds;
+  __shared__ __attribute__((aligned(16))) uint8_t qlds[kNW * kQInLds * 64 * 16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kRowsWG = kNW * kRowsPerWave;
+
+  int item, rbk;
+  if (p.row_blocks == 1) {
+    item = blockIdx.x;
+    rbk = 0;
+  } else {
+    // the row blocks of one chunk get ids congruent mod 8, i.e. the same XCD,
+    // so their repeated reads of the chunk's KV are served by that XCD's L2
+    const int x = blockIdx.x & 7, sx = blockIdx.x >> 3;
+    item = (sx / p.row_blocks) * 8 + x;
+    rbk = sx % p.row_blocks;
+  }
+  if (item >= p.plan[0]) return;
+  const int2 it = p.items[item];
+  const int b = it.x;
+  const int chunk = p.plan[1];
+  const int cnt = local_count(p, b);
+  const int j0 = it.y * chunk;
+  const int j1 = min(cnt, j0 + chunk);
+  const int L = req_len(p, b);
+  const bool single = p.req_info[b].y == 1;
+
+  const int row = rbk * kRowsWG + wave * kRowsPerWave + (lane & 31);
+  const bool row_ok = row < p.rows;
+  const bool wave_active = rbk * kRowsWG + wave * kRowsPerWave < p.rows;
+  int jvis = j1;
+  if (row_ok) {
+    const int i = row / p.heads;
+    const int lim = L - p.q_len + i - p.shard;
+    const int jl = lim >= 0 ? lim / p.num_shards + 1 : 0;
+    jvis = min(j1, jl);
+  }
+
+  // row indices of the first two tiles are requested before the Q loads so
+  // their latency overlaps
+  const int raw0 = fetch_row_raw(p, b, j0, j1, lane);
+  const int raw1 = fetch_row_raw(p, b, j0 + kTile, j1, lane);
+
+  bf16x8_t qreg[kQRegSteps];
+  uint8_t* const qmine = qlds + 16 * (kQInLds * 64 * wave + lane);
+  {
+    const uint16_t* qrow = p.q + ((long long)b * p.rows + (row_ok ? row : 0)) * kDqk + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < kDqk / 16; ++ks) {
+      bf16x8_t x = *(const bf16x8_t*)(qrow + 16 * ks);
+      x = row_ok ? x : bf16x8_t{};
+      if (ks < kQRegSteps) qreg[ks] = x;
+      else *(bf16x8_t*)(qmine + 16 * 64 * (ks - kQRegSteps)) = x;
+    }
+  }
+
+  const int tok = lane & 31, hi = lane >> 5;
+  const int ntiles = j1 > j0 ? (j1 - j0 + kTile - 1) / kTile : 0;
+  // QK operand of k-step kk: slot 32 (2 kk + hi) + (tok ^ (8 (kk & 1) + 4 hi))
+  const uint32_t qk_base[2] = {512u * hi + 16u * (tok ^ (4 * hi)), 512u * hi + 16u * (tok ^ (8 + 4 * hi))};
+  // PV transposing loads: this lane supplies token t = 16 m + 8 k + 4 hi + r,
+  // dims 32 db + 16 g1 + 4 s .. + 3 (chunk 4 db + cl, cl = 2 g1 + (s >> 1))
+  uint32_t pv_base[2];
+  {
+    const int g1 = (lane >> 4) & 1, r = (lane & 15) >> 2, sq = lane & 3;
+    const int cl = 2 * g1 + (sq >> 1);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      pv_base[k] = (uint32_t)(512 * cl + 128 * (k ^ g1) + 64 * (hi ^ (sq >> 1)) + 16 * r + 8 * (sq & 1));
+  }
+
+  f32x16_t o[kDv / 32];
+  float m_ref = kNegInf, m_all = kNegInf, l_sum = 0.f;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+#pragma unroll
+    for (int db = 0; db < kDv / 32; ++db) o[db] = f32x16_t{};
+    l_sum = 0.f;
+    m_ref = attempt == 0 ? kNegInf : m_all;
+    bool overflow = false;
+
+    int rows_cur = kRowPastEnd;
+    int raw_next = INT_MIN;
+    TileDma<kNW> dma;
+    if (ntiles > 0) {
+      rows_cur = resolve_row(p, raw0, j0, lane);
+      dma.prepare(p, smem, rows_cur);
+      dma.issue_all();
+      raw_next = raw1;
+    }
+
+    for (int tile = 0; tile < ntiles; ++tile) {
+      const int jt = j0 + tile * kTile;
+      const bool more = tile + 1 < ntiles;
+      // tokens of this tile whose page is outside the pool poison their scores
+      const uint64_t bad = __ballot(lane < kTile && rows_cur == kRowBad);
+      __builtin_amdgcn_s_waitcnt(0);     // this tile's loads (and the next rows) have landed
+      __syncthreads();                   // ... for every wave; the other stage is free
+      if (more) {
+        rows_cur = resolve_row(p, raw_next, jt + kTile, lane);
+        dma.prepare(p, smem + ((tile + 1) & 1) * kKTileBytes, rows_cur);
+        dma.issue_all();
+        raw_next = fetch_row_raw(p, b, jt + 2 * kTile, j1, lane);
+      }
+      const uint8_t* ks = smem + (tile & 1) * kKTileBytes;
+      // every wave runs the MFMAs (a wave past the last row works on zero
+      // queries and writes nothing): keeping the accumulators out of a
+      // conditional block lets them stay in AGPRs across the tile loop
+      {
+        // S^T[token][row]; K operands are read two steps ahead of their MFMA
+        constexpr int kKSteps = kDqk / 16;
+        constexpr int kAhead = 2;
+        bf16x8_t ka[kAhead];
+#pragma unroll
+        for (int u = 0; u < kAhead; ++u) ka[u] = *(const bf16x8_t*)(ks + qk_base[u & 1] + 1024 * u);
+        f32x16_t s = f32x16_t{};
+#pragma unroll
+        for (int kk = 0; kk < kKSteps; ++kk) {
+          const bf16x8_t a = ka[kk % kAhead];
+          if (kk + kAhead < kKSteps) {
+            const int kn = kk + kAhead;
+            ka[kk % kAhead] = *(const bf16x8_t*)(ks + qk_base[kn & 1] + 1024 * kn);
+          }
+          const bf16x8_t qb = kk < kQRegSteps ? qreg[kk < kQRegSteps ? kk : 0]
+                                              : *(const bf16x8_t*)(qmine + 16 * 64 * (kk - kQRegSteps));
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb, s, 0, 0, 0);
+        }
+        float tmax = kNegInf;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int tl = 8 * (v >> 2) + 4 * hi + (v & 3);
+          const int j = jt + tl;
+          float x = j < jvis ? s[v] * p.scale_log2 : kNegInf;
+          x = ((bad >> tl) & 1) ? __builtin_nanf("") : x;
+          s[v] = x;
+          tmax = fmaxf(tmax, x);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        m_all = fmaxf(m_all, tmax);
+        m_ref = m_ref == kNegInf ? tmax : m_ref;
+        overflow = overflow || tmax > m_ref + kOverflowSlack;
+        const float m_use = m_ref == kNegInf ? 0.f : m_ref;
+        bf16x8_t pb[2];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float pv = exp2_fast(s[v] - m_use);
+          l_sum += pv;
+          pb[v >> 3][v & 7] = (__bf16)pv;
+        }
+        // O^T[dim][row] += V^T[dim][token] P^T[token][row]
+        constexpr int kPvSteps = 2 * (kDv / 32);
+        bf16x8_t va[kAhead];
+#pragma unroll
+        for (int u = 0; u < kAhead; ++u) va[u] = pv_operand(ks, pv_base, u);
+#pragma unroll
+        for (int st = 0; st < kPvSteps; ++st) {
+          const bf16x8_t a = va[st % kAhead];
+          if (st + kAhead < kPvSteps) va[st % kAhead] = pv_operand(ks, pv_base, st + kAhead);
+          o[st >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st & 1], o[st >> 1], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 1);
+#pragma unroll
+        for (int st = 0; st < kPvSteps; ++st) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          if (st + kAhead < kPvSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        }
+      }
+    }
+    if (!__syncthreads_or(overflow ? 1 : 0)) break;
+  }
+
+  if (!wave_active) return;
+  const float l_tot = l_sum + __shfl_xor(l_sum, 32);
+  const bool any = l_tot > 0.f || l_tot != l_tot;
+  const float inv = any ? p.out_scale / l_tot : 0.f;
+  const float lse2 = any ? m_ref + log2_fast(l_tot) : kNegInf;
+  if (!row_ok) return;
+  const long long orow = (long long)b * p.rows + row;
+  const long long prow = (long long)item * p.rows + row;
+  if (single && p.out_bf16) {
+    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+    __bf16* dst = (__bf16*)p.out + orow * kDv + 4 * hi;
+#pragma unroll
+    for (int db = 0; db < kDv / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4_t v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(o[db][4 * g + e] * inv);
+        *(bf16x4_t*)(dst + 32 * db + 8 * g) = v4;
+      }
+  } else {
+    float* dst = (single ? (float*)p.out + orow * kDv : p.part_o + prow * kDv) + 4 * hi;
+#pragma unroll
+    for (int db = 0; db < kDv / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4_t v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = o[db][4 * g + e] * inv;
+        *(f32x4_t*)(dst + 32 * db + 8 * g) = v4;
+      }
+  }
+  if (hi == 0) {
+    if (single) p.lse[orow] = p.lse_base2 ? lse2 : lse2 * kLn2;
+    else p.part_lse[prow] = lse2;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // combine the chunk partials of requests split over several workgroups
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
@@ -505,8 +828,12 @@ hipError_t launch_decode(const DecodeParams& p, bool fp8, hipEvent_t ev_begin, h
     err = hipEventRecord(ev_begin, stream);
     if (err != hipSuccess) return err;
   }
+  const int nw = p.rows >= 128 ? 4 : (p.rows + 31) / 32;
   if (fp8) hipLaunchKernelGGL(attn_kernel<true>, dim3(grid), dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL(attn_kernel<false>, dim3(grid), dim3(256), 0, stream, p);
+  else if (nw == 4) hipLaunchKernelGGL(attn_direct_kernel<4>, dim3(grid), dim3(256), 0, stream, p);
+  else if (nw == 2) hipLaunchKernelGGL(attn_direct_kernel<2>, dim3(grid), dim3(128), 0, stream, p);
+  else if (nw == 3) hipLaunchKernelGGL(attn_direct_kernel<4>, dim3(grid), dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(attn_direct_kernel<1>, dim3(grid), dim3(64), 0, stream, p);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (ev_end) {

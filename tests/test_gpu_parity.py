@@ -227,7 +227,11 @@ def test_merge_bf16_parity(T):
     torch.cuda.synchronize()
     ro, rl = _merge_ref(mi)
     go = U.to_np(out)
-    assert np.all(np.abs(go - ro) <= U.bf16_ulp(ro) + 1e-30), "bf16 merge beyond one ulp"
+    # one bf16 ulp of the result plus the fp32 accumulation error, which is
+    # relative to the (row, head) vector's magnitude (cancellation can leave
+    # a result far smaller than its terms)
+    vec = np.abs(ro).max(axis=-1, keepdims=True)
+    assert np.all(np.abs(go - ro) <= U.bf16_ulp(ro) + 1e-5 * vec), "bf16 merge beyond one ulp"
     gl = U.to_np(lse)
     fin = np.isfinite(rl)
     assert np.array_equal(np.isneginf(gl), np.isneginf(rl))
