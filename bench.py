@@ -290,6 +290,9 @@ def main() -> int:
                     help="KV chunks per launch per row block (0 = library default)")
     ap.add_argument("--sweep-split", default=None,
                     help="comma list of split targets to time on the headline workload (details only)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes 5 times and exit "
+                         "(reference kernel for scaling the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -301,6 +304,16 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.copy_calibration:
+        n = int(args.copy_calibration)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+        return 0
     from decode_attention_paged_amd import _lib as L
     L.load()
 
@@ -336,7 +349,8 @@ def main() -> int:
         roof = dict(bound="hbm", achieved=res["attn_kernel_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=res["attn_kernel_gbs"] / HBM_PEAK_GBS)
     roof["traffic"] = traffic_from_profile(wl.name)
-    roof["kernel"] = "attn_kernel (mla_decode.hip), mean of %d launches" % (args.steps * wl.shards)
+    roof["kernel"] = ("attn_kernel<fp8>" if wl.kv_dtype == "fp8" else "attn_direct_kernel") + \
+        " (mla_decode.hip), mean of %d launches" % (args.steps * wl.shards)
     roof["mean_launch_us"] = res["attn_kernel_mean_us"]
     roof["algorithmic_bytes_per_launch"] = res["attn_kernel_bytes_per_launch"]
 
