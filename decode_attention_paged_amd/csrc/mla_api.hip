@@ -65,13 +65,30 @@ WorkspaceLayout decode_workspace_layout(int32_t batch, int32_t rows) {
   WorkspaceLayout w{};
   const int64_t items = (int64_t)batch + kSplitTargetMax;
   w.max_items = (int32_t)(((items + 7) / 8) * 8);
+  const int32_t rows_blk = stream_rows_per_block(rows);
+  const int64_t nseg = (int64_t)batch * ((rows + rows_blk - 1) / rows_blk);
+  // a segment is cut into pieces only at workgroup boundaries
+  w.max_slots = (int32_t)(nseg + kMaxGrid);
   size_t off = 0;
   w.plan = off;      off = align_up(off + 64, 256);
   w.req_info = off;  off = align_up(off + sizeof(int2) * (size_t)batch, 256);
   w.items = off;     off = align_up(off + sizeof(int2) * (size_t)w.max_items, 256);
-  w.part_lse = off;  off = align_up(off + sizeof(float) * (size_t)w.max_items * rows, 256);
-  w.part_o = off;    off = align_up(off + sizeof(float) * (size_t)w.max_items * rows * kDv, 256);
-  w.total = off;
+  w.req_cnt = off;   off = align_up(off + sizeof(int32_t) * (size_t)batch, 256);
+  w.seg_off = off;   off = align_up(off + sizeof(int32_t) * (size_t)(nseg + 1), 256);
+  w.seg_coff = off;  off = align_up(off + sizeof(int32_t) * (size_t)(nseg + 1), 256);
+  w.seg_info = off;  off = align_up(off + sizeof(int4) * (size_t)nseg, 256);
+  w.wg_start = off;  off = align_up(off + sizeof(int2) * (size_t)kMaxGrid, 256);
+  w.wg_ustart = off; off = align_up(off + sizeof(int32_t) * (size_t)(kMaxGrid + 1), 256);
+  // partial buffers: the fp8 chunked kernel (fp32) and the streaming kernel
+  // (bf16) never run in the same call, so they share one region
+  const size_t region = off;
+  w.part_lse = region;
+  w.part_o = align_up(region + sizeof(float) * (size_t)w.max_items * rows, 256);
+  const size_t end_chunked = align_up(w.part_o + sizeof(float) * (size_t)w.max_items * rows * kDv, 256);
+  w.spart_lse = region;
+  w.spart_o = align_up(region + sizeof(float) * (size_t)w.max_slots * rows_blk, 256);
+  const size_t end_stream = align_up(w.spart_o + sizeof(uint16_t) * (size_t)w.max_slots * rows_blk * kDv, 256);
+  w.total = end_chunked > end_stream ? end_chunked : end_stream;
   return w;
 }
 
@@ -222,9 +239,29 @@ mla_status_t mla_decode_partial(const mla_decode_args_t* a, mla_lse_base_t* lse_
   p.part_o = (float*)(ws + w.part_o);
   p.max_items = w.max_items;
   p.split_target = target;
+  p.req_cnt = (int32_t*)(ws + w.req_cnt);
+  p.seg_off = (int32_t*)(ws + w.seg_off);
+  p.seg_coff = (int32_t*)(ws + w.seg_coff);
+  p.wg_ustart = (int32_t*)(ws + w.wg_ustart);
+  p.seg_info = (int4*)(ws + w.seg_info);
+  p.wg_start = (int2*)(ws + w.wg_start);
+  p.spart_lse = (float*)(ws + w.spart_lse);
+  p.spart_o = (uint16_t*)(ws + w.spart_o);
+  p.rows_blk = mla::stream_rows_per_block(rows);
+  if (a->kv_dtype != MLA_DTYPE_FP8_E4M3) p.row_blocks = (rows + p.rows_blk - 1) / p.rows_blk;
+  {
+    // bf16 KV: one persistent workgroup per CU (a multiple of 8 so that the
+    // workgroup order can follow the XCDs) unless the caller fixes the count
+    int32_t grid = a->split_target > 0 ? a->split_target : ((cus + 7) / 8) * 8;
+    if (grid > mla::kMaxGrid) grid = mla::kMaxGrid;
+    p.grid = grid;
+  }
 
-  hipError_t err = mla::launch_decode(p, a->kv_dtype == MLA_DTYPE_FP8_E4M3, (hipEvent_t)a->event_begin,
-                                      (hipEvent_t)a->event_end, (hipStream_t)stream);
+  hipError_t err = a->kv_dtype == MLA_DTYPE_FP8_E4M3
+                       ? mla::launch_decode(p, true, (hipEvent_t)a->event_begin, (hipEvent_t)a->event_end,
+                                            (hipStream_t)stream)
+                       : mla::launch_decode_stream(p, (hipEvent_t)a->event_begin, (hipEvent_t)a->event_end,
+                                                   (hipStream_t)stream);
   if (err != hipSuccess) return device_fail(err, "decode launch");
   return ok();
 }

@@ -26,21 +26,13 @@
 //           as the A operand of O^T += V^T P^T. The token order inside a
 //           group matches the order of P values that the S^T accumulator
 //           leaves in each lane, so P never leaves registers.
-#include "mla_internal.h"
+#include "mla_device.h"
 
 #include <limits.h>
 
 namespace mla {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
-constexpr float kLn2 = 0.693147180559945309f;
-constexpr float kNegInf = -__builtin_inff();
 // The exponent reference of a row is fixed at the max of the first tile that
 // holds a visible token, so the output accumulator is never rescaled inside
 // the tile loop. Unnormalised probabilities stay below 2^kOverflowSlack; a
@@ -52,27 +44,6 @@ constexpr int kKBytes = kTile * kDqk * 2;        // 36864
 constexpr int kVtBytes = kDv * 4 * 16;           // 32768
 constexpr int kStageBytes = kKBytes + kVtBytes;  // 69632
 constexpr int kChunks = kDqk / 8;                // 72 chunks of 8 dims per row
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
-
-__device__ __forceinline__ int req_len(const DecodeParams& p, int b) {
-  int L = p.seq_lens[b];
-  L = L < 0 ? 0 : L;
-  const int cap = p.max_pages * kPage;   // never read past the block-table row
-  return L > cap ? cap : L;
-}
-
-// Number of tokens of request b the shard owns (before any causal limit).
-__device__ __forceinline__ int local_count(const DecodeParams& p, int b) {
-  if (p.local_seq_lens != nullptr) {
-    int n = p.local_seq_lens[b];
-    n = n < 0 ? 0 : n;
-    return n > p.local_kv_stride ? p.local_kv_stride : n;
-  }
-  const int L = req_len(p, b);
-  return L / p.num_shards + (p.shard < L % p.num_shards ? 1 : 0);
-}
 
 // Physical KV row of the shard's j-th owned token of request b (j < count),
 // or -1 when the page id / row is outside the pool.
@@ -458,29 +429,6 @@ void attn_kernel(DecodeParams p) {
 //    chunks a 32-lane half reads in distinct 64-byte bank segments.
 constexpr int kKTileBytes = kTile * kDqk * 2;   // 36864
 constexpr int kDirectStages = 2;
-
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ i16x4_t lds_read_tr16(const uint8_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)p);
-}
-
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-  return (uint32_t)(size_t)((__attribute__((address_space(3))) const void*)p);
-}
-
-// global_load_lds_dwordx4: 16 bytes per lane from `src` into LDS at
-// lds_base + 16 * lane. Issued as inline assembly so that the compiler's
-// wait-count bookkeeping does not treat every later LDS read as dependent on
-// it (it would wait for the load before reading the other stage). Only the
-// stage that no wave reads until the next barrier is ever the destination,
-// and the caller waits for completion explicitly (s_waitcnt vmcnt(0) +
-// barrier) before any wave reads it; volatile asm is not moved across those
-// barriers. M0 holds the LDS base (one wait state after writing it).
-__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds_base));
-}
 
 // Row indices of a tile are fetched one iteration before they are used and
 // validated only after the loop-top wait, so fetching them never forces a wait

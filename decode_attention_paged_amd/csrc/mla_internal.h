@@ -44,11 +44,34 @@ struct DecodeParams {
   float* part_o;                  // [max_items][rows][512], normalised, scaled
   int32_t max_items;
   int32_t split_target;
+  // persistent schedule of the streaming kernel: the shard's work is the
+  // sequence of units (request b, row block rb, 32-token tile), ordered by
+  // segment s = b * row_blocks + rb and tile; workgroup g takes a contiguous
+  // range of units of about equal cost (tiles plus a charge per segment)
+  int32_t* req_cnt;               // [B] owned tokens per request
+  int32_t* seg_off;               // [B * row_blocks + 1] first unit of each segment
+  int32_t* seg_coff;              // [B * row_blocks + 1] cost offset of each segment
+  int32_t* wg_ustart;             // [grid + 1] first unit of each workgroup
+  int4* seg_info;                 // [B * row_blocks] (slot base, pieces, first workgroup, -)
+  int2* wg_start;                 // [grid] (segment, tile) of each workgroup's first unit
+  uint16_t* spart_o;              // [slots][rows_blk][512] bf16, normalised, scaled
+  float* spart_lse;               // [slots][rows_blk] base 2
+  int32_t rows_blk;               // query rows per workgroup (32, 64 or 128)
+  int32_t grid;                   // persistent workgroups
 };
+
+constexpr int kMaxGrid = 1024;  // persistent workgroups of the streaming kernel
+
+// Query rows one streaming workgroup covers: its four waves are 2 row groups
+// of 32 rows x 2 halves of the dims (rows > 32), or 1 x 4 (rows <= 32); more
+// rows take several row blocks, whose workgroups read the same KV tiles at
+// about the same time (neighbours in the schedule), mostly from cache.
+inline int32_t stream_rows_per_block(int32_t rows) { return rows <= 32 ? 32 : 64; }
 
 struct WorkspaceLayout {
   size_t plan, req_info, items, part_lse, part_o, total;
-  int32_t max_items;
+  size_t req_cnt, seg_off, seg_coff, seg_info, wg_start, wg_ustart, spart_lse, spart_o;
+  int32_t max_items, max_slots;
 };
 WorkspaceLayout decode_workspace_layout(int32_t batch, int32_t rows);
 
@@ -71,6 +94,8 @@ hipError_t launch_metadata(const int32_t* seq_lens, const int32_t* block_table, 
                            int32_t stride, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, bool fp8, hipEvent_t ev_begin, hipEvent_t ev_end,
                          hipStream_t stream);
+hipError_t launch_decode_stream(const DecodeParams& p, hipEvent_t ev_begin, hipEvent_t ev_end,
+                                hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 
 }  // namespace mla

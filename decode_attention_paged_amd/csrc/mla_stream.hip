@@ -1,0 +1,746 @@
+// Rank-local paged MLA decode over bf16 KV: persistent streaming kernel.
+//
+// One shard r of S owns the tokens t = j S + r of every request (prhub.com.cn
+// digest of sgl-project/sglang PR 33926, sections 功能与动机 and 实现拆解
+// step 3); this file computes, for each query row, softmax attention over
+// those tokens and emits the rank-local (out, lse), (0, -inf) where a row
+// sees no owned token.
+//
+// Schedule. The shard's work is a sequence of units (request b, block of
+// query rows rb, 32-token tile), ordered by segment s = b * row_blocks + rb
+// and tile. stream_plan_kernel lays the segments out on device (no host
+// synchronisation) and one workgroup per CU takes an equal contiguous share
+// of the units. A segment that a workgroup holds entirely is finalised in
+// place; a segment cut at workgroup boundaries leaves one bf16 partial per
+// piece, combined by stream_combine_kernel.
+//
+// Workgroup. Four waves: rows_blk / 32 row groups of 32 query rows times
+// 4 / (rows_blk / 32) slices of the 512 V dims. Every wave computes the
+// scores of its 32 rows (S^T = K Q^T, v_mfma_f32_32x32x16_bf16) and the
+// output of its dims slice (O^T += V^T P^T).
+//
+// Pipeline. Tiles move HBM -> LDS with global_load_lds_dwordx4 (no register
+// staging) through four 36 KB stages, so three tiles are in flight while one
+// is computed. The row indices of a tile move into an LDS ring the same way,
+// 2 * 4 - 2 tiles ahead, so every vector-memory operation inside the tile
+// loop is one of these asynchronous copies and the loop waits on exactly the
+// tile it needs (s_waitcnt vmcnt(n) with n counted by the wave).
+#include "mla_device.h"
+
+#include <limits.h>
+
+namespace mla {
+namespace {
+
+constexpr int kStageBytes = kTile * kDqk * 2;      // 36864: one tile
+constexpr int kRopeBase = kTile * 1024;             // rope part of a stage (dims 512..575)
+constexpr int kRing = 8;                           // row-index ring, in tiles
+constexpr int kDmaPerWave = kStageBytes / 1024 / 4;  // 9 copies of 1 KB per wave per tile
+// A row's exponent reference moves up (rescaling its accumulator) only when a
+// tile's max exceeds it by more than this (log2 units), so rescaling is rare
+// and unnormalised probabilities stay below 2^kRescaleSlack.
+constexpr float kRescaleSlack = 8.0f;
+
+constexpr int kPieceCost = 3;     // query load + epilogue of a piece, in tiles
+
+constexpr int kRowPastEnd = -2;   // token past the request's owned range
+constexpr int kRowBad = -1;       // page id or row outside the pool
+
+
+// ---------------------------------------------------------------------------
+// plan
+// ---------------------------------------------------------------------------
+// Block-wide inclusive scan of one int per thread (1024 threads).
+__device__ __forceinline__ int block_scan(int v, int* s_scan) {
+  const int tid = threadIdx.x;
+  s_scan[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int x = tid >= off ? s_scan[tid - off] : 0;
+    __syncthreads();
+    s_scan[tid] += x;
+    __syncthreads();
+  }
+  const int r = s_scan[tid];
+  __syncthreads();
+  return r;
+}
+
+// Last index i in [0, n) with a[i] <= x (a nondecreasing, a[0] <= x).
+__device__ __forceinline__ int last_le(const int32_t* a, int n, long long x) {
+  int lo = 0, hi = n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] <= x) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(1024) void stream_plan_kernel(DecodeParams p) {
+  __shared__ int s_scan[1024];
+  __shared__ int s_scan2[1024];
+  const int tid = threadIdx.x;
+  const int RB = p.row_blocks;
+  const int nseg = p.batch * RB;
+
+  // tiles of every segment, their unit offsets and their cost offsets (a
+  // segment costs its tiles plus kPieceCost for loading its queries)
+  int carry = 0, ccarry = 0;
+  for (int base = 0; base < nseg; base += 1024) {
+    const int s = base + tid;
+    int n = 0;
+    if (s < nseg) {
+      const int b = s / RB;
+      const int cnt = local_count(p, b);
+      if (s - b * RB == 0) p.req_cnt[b] = cnt;
+      n = (cnt + kTile - 1) / kTile;
+    }
+    const int c = n > 0 ? n + kPieceCost : 0;
+    s_scan2[tid] = c;
+    const int inc = block_scan(n, s_scan);
+    // second scan in place over s_scan2 (same pattern)
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int x = tid >= off ? s_scan2[tid - off] : 0;
+      __syncthreads();
+      s_scan2[tid] += x;
+      __syncthreads();
+    }
+    const int cinc = s_scan2[tid];
+    if (s < nseg) {
+      p.seg_off[s] = carry + inc - n;
+      p.seg_coff[s] = ccarry + cinc - c;
+    }
+    carry += s_scan[1023];
+    ccarry += s_scan2[1023];
+    __syncthreads();
+  }
+  const int U = carry, C = ccarry;
+  // workgroups in use: at most one per cost unit, so consecutive workgroup
+  // boundaries differ and only a piece's first workgroup can start inside
+  // its query-load cost
+  const int G = min(p.grid, C);
+  if (tid == 0) {
+    p.seg_off[nseg] = U;
+    p.seg_coff[nseg] = C;
+    p.plan[0] = U;
+    p.plan[1] = G;
+    p.wg_ustart[G] = U;
+  }
+  __syncthreads();
+
+  // first unit of each workgroup: cost boundary g C / G mapped to the unit
+  // sequence (a boundary inside a segment's query cost maps to its first tile)
+  for (int g = tid; g < G; g += 1024) {
+    const long long x = (long long)g * C / G;
+    const int s = last_le(p.seg_coff, nseg + 1, x);
+    const int n = p.seg_off[s + 1] - p.seg_off[s];
+    long long k = x - p.seg_coff[s] - kPieceCost;
+    k = k < 0 ? 0 : (k > n - 1 ? n - 1 : k);
+    p.wg_ustart[g] = p.seg_off[s] + (int)k;
+    p.wg_start[g] = make_int2(s, (int)k);
+  }
+  __syncthreads();
+
+  // pieces of each segment (one per non-empty workgroup it meets) and
+  // partial slots
+  int slots = 0;
+  for (int base = 0; base < nseg; base += 1024) {
+    const int s = base + tid;
+    int np = 0, first = 0;
+    if (s < nseg) {
+      const int o = p.seg_off[s];
+      const int n = p.seg_off[s + 1] - o;
+      if (n > 0) {
+        first = last_le(p.wg_ustart, G, o);
+        np = last_le(p.wg_ustart, G, o + n - 1) - first + 1;
+      }
+    }
+    const int m = np > 1 ? np : 0;
+    const int inc = block_scan(m, s_scan);
+    if (s < nseg) p.seg_info[s] = make_int4(slots + inc - m, np, first, 0);
+    slots += s_scan[1023];
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// streaming attention
+// ---------------------------------------------------------------------------
+// Position in the unit sequence: request, row block, tile, and the request's
+// tile count and owned-token count. Wave-uniform.
+struct Cursor {
+  int b, rb, tile, ntiles, cnt;
+
+  __device__ __forceinline__ void start(const DecodeParams& p, int seg, int t) {
+    b = seg / p.row_blocks;
+    rb = seg - b * p.row_blocks;
+    tile = t;
+    cnt = ld_const(p.req_cnt + b);
+    ntiles = (cnt + kTile - 1) / kTile;
+  }
+  // move to the next unit; only called when one exists
+  __device__ __forceinline__ void advance(const DecodeParams& p) {
+    if (++tile < ntiles) return;
+    tile = 0;
+    for (;;) {
+      if (++rb == p.row_blocks) {
+        rb = 0;
+        ++b;
+        cnt = ld_const(p.req_cnt + b);
+        ntiles = (cnt + kTile - 1) / kTile;
+      }
+      if (ntiles > 0) break;
+    }
+  }
+};
+
+// Row indices of the cursor's tile -> LDS ring slot (32 ints): wave w copies
+// the table entries of tokens 8w .. 8w + 7 (one instruction per wave). Past
+// the owned range it copies the tile's first entry instead; those tokens are
+// masked by the reader.
+__device__ __forceinline__ void fetch_rows(const DecodeParams& p, const Cursor& c, uint32_t slot_lds) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (lane < 8) {
+    int j = c.tile * kTile + 8 * wave + lane;
+    j = j < c.cnt ? j : c.tile * kTile;
+    const int32_t* src;
+    if (p.local_kv_indices != nullptr)
+      src = p.local_kv_indices + (long long)c.b * p.local_kv_stride + j;
+    else
+      src = p.block_table + (long long)c.b * p.max_pages + ((j * p.num_shards + p.shard) >> 6);
+    lds_dma4(src, __builtin_amdgcn_readfirstlane(slot_lds + 32 * wave));
+  }
+}
+
+// KV row of token `tok` of the cursor's tile from its table entry.
+__device__ __forceinline__ int resolve_row(const DecodeParams& p, int tile, int cnt, int tok, int raw) {
+  const int j = tile * kTile + tok;
+  if (j >= cnt) return kRowPastEnd;
+  long long row;
+  if (p.local_kv_indices != nullptr) {
+    row = raw;
+  } else {
+    const int t = j * p.num_shards + p.shard;
+    row = (raw < 0 || raw >= p.num_pages) ? -1 : (long long)raw * kPage + (t & 63);
+  }
+  return (row < 0 || row >= (long long)p.num_pages * kPage) ? kRowBad : (int)row;
+}
+
+// XOR swizzle of the 16-byte chunks inside each 128-byte group, by token:
+// eight consecutive tokens get eight different values, and four consecutive
+// tokens differ in the 32-byte pair they select.
+__host__ __device__ constexpr int chunk_swz(int t) { return 2 * (t & 3) + ((t >> 2) & 1); }
+
+// Copies of one tile into a stage. Stage layout (token-major, swizzled):
+//   chunk c < 64 (dims 8c .. 8c + 7) of token t at byte 1024 t + 16 (c ^ swz(t)),
+//   chunk c >= 64 (rope) at kRopeBase + 128 t + 16 ((c - 64) ^ swz(t)).
+// Wave w moves tokens 8w .. 8w + 7: one copy per token for its first 1 KB
+// (64 lanes over one row, so every copy reads whole 128-byte lines) and one
+// copy for the eight 128-byte rope tails. The row of each token comes from
+// the ring; the main copies take it as a scalar base address.
+__device__ __forceinline__ void issue_tile(const DecodeParams& p, const Cursor& c, uint32_t stage_lds,
+                                           const int32_t* ring_slot) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tk = 8 * wave + (lane >> 3);   // this lane's token for the rope copy
+  const int row = resolve_row(p, c.tile, c.cnt, tk, ring_slot[tk]);
+  const long long rowc = row >= 0 ? row : 0;
+  lds_dma16(p.kv + rowc * (2 * kDqk) + 16 * (64 + ((lane & 7) ^ chunk_swz(lane >> 3))),
+            __builtin_amdgcn_readfirstlane(stage_lds + kRopeBase + 1024 * wave));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = __builtin_amdgcn_readlane((int)rowc, 8 * i);
+    const uint8_t* base = p.kv + (long long)r * (2 * kDqk);
+    lds_dma16_sbase(base, (uint32_t)(16 * (lane ^ chunk_swz(i))),
+                    __builtin_amdgcn_readfirstlane(stage_lds + 1024 * (8 * wave + i)));
+  }
+}
+
+// Wait until at most `after` vector-memory operations of this wave are
+// outstanding, i.e. everything issued before the last `after` ones landed.
+// `after` is wave-uniform; the ladder rounds it down to an encodable
+// immediate (waiting longer is always safe).
+__device__ __forceinline__ void wait_vm_after(int after) {
+  constexpr int P = kDmaPerWave;
+  if (after >= 2 * P + 2) wait_vmcnt<2 * P + 2>();
+  else if (after >= 2 * P + 1) wait_vmcnt<2 * P + 1>();
+  else if (after >= 2 * P) wait_vmcnt<2 * P>();
+  else if (after >= P + 2) wait_vmcnt<P + 2>();
+  else if (after >= P + 1) wait_vmcnt<P + 1>();
+  else if (after >= P) wait_vmcnt<P>();
+  else if (after >= 2) wait_vmcnt<2>();
+  else if (after >= 1) wait_vmcnt<1>();
+  else wait_vmcnt<0>();
+}
+
+// QK A operand of this wave's i-th k-step (see the kernel for the layout).
+template <int kG>
+__device__ __forceinline__ bf16x8_t qk_operand(const uint8_t* ks, uint32_t qk0, uint32_t rope0, int i) {
+  return i / kG < 8 ? *(const bf16x8_t*)(ks + (qk0 ^ (32u * (i % kG))) + 128 * (i / kG))
+                    : *(const bf16x8_t*)(ks + (rope0 ^ (32u * (i % kG))));
+}
+
+// PV operand of step st = 2 db + m (db local to the wave's slice): dims
+// 32 db .. + 31 of tokens 16 m .. 16 m + 15 in the order of the P values,
+// from two transposing loads of four tokens each (the second 8 tokens on).
+__device__ __forceinline__ bf16x8_t pv_operand(const uint8_t* ks, uint32_t pv0, int st) {
+  const int db = st >> 1, m = st & 1;
+  const uint8_t* a = ks + (pv0 ^ (64u * (db & 1))) + 128 * (db >> 1) + 16384 * m;
+  const i16x4_t lo = lds_read_tr16(a);
+  const i16x4_t hi = lds_read_tr16(a + 8192);
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// x * f for an accumulator element held in an AGPR, in place (VALU cannot
+// read AGPRs; keeping the operand constrained to an AGPR stops the compiler
+// from moving the whole accumulator to VGPRs around the rare rescale).
+__device__ __forceinline__ float acc_scale(float x, float f) {
+  float tmp;
+  asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+               : "+a"(x), "=&v"(tmp) : "v"(f));
+  return x;
+}
+
+// max over lanes l and l ^ 32 (the two halves of a wave hold the two token
+// halves of one query row)
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Read an accumulator element held in an AGPR (keeps the compiler from
+// moving the whole accumulator to VGPRs for the epilogue).
+__device__ __forceinline__ float acc_read(float x) {
+  float r;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
+  return r;
+}
+
+template <int kDS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_stream_kernel(DecodeParams p) {
+  constexpr int kRG = 4 / kDS;                 // row groups of 32 rows
+  constexpr int kRowsBlk = 32 * kRG;
+  constexpr int kDb = (kDv / 32) / kDS;        // 32-dim blocks of this wave's V slice
+  constexpr int kNS = 3;                       // stages
+  constexpr int kAheadRows = 2 * kNS - 2;      // tiles whose row indices are fetched ahead
+  // QK: the kDS waves of a row group split the 36 k-steps; wave ds takes the
+  // k-steps kk with kk mod 4 in [kG ds, kG ds + kG) and sums the partial
+  // scores of all kDS waves in one fixed order (so they agree bit for bit)
+  constexpr int kG = 4 / kDS;
+  constexpr int kKS = 9 * kG;                  // k-steps per wave
+  // Q k-steps kept in LDS rather than VGPRs (with 32 rows x 512 dims of
+  // accumulators in AGPRs, this keeps the tile loop spill-free); read back
+  // once per tile
+  constexpr int kQInLds = kDS == 1 ? 12 : 0;
+  constexpr int kQRegSteps = kKS - kQInLds;
+  constexpr int kPvSteps = 2 * kDb;
+  constexpr int kAhead = 2;
+  static_assert(kAheadRows < kRing, "row ring too small");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * kStageBytes];
+  __shared__ __attribute__((aligned(16))) int32_t ring[kRing * kTile];
+  __shared__ __attribute__((aligned(16))) uint8_t qlds[kQInLds > 0 ? 4 * kQInLds * 64 * 16 : 16];
+  __shared__ __attribute__((aligned(16))) f32x4_t xbuf[kDS > 1 ? 4 * 4 * 64 : 1];   // [wave][4][lane]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = wave % kRG, ds = wave / kRG;
+  const int tok = lane & 31, hi = lane >> 5;
+
+  // consecutive workgroups of the unit order run on one XCD (blocks are
+  // dealt to the 8 XCDs round robin), so the L2 of that XCD serves the
+  // repeated reads of a request's Q and KV
+  int g = blockIdx.x;
+  if ((p.grid & 7) == 0) g = (blockIdx.x & 7) * (p.grid >> 3) + (blockIdx.x >> 3);
+  const int G = ld_const(p.plan + 1);   // workgroups in use
+  if (g >= G) return;
+  const int Uw = ld_const(p.wg_ustart + g + 1) - ld_const(p.wg_ustart + g);
+  if (Uw <= 0) return;
+
+  const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_address(smem));
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_address(ring));
+  Cursor cf, ci, cc;
+  {
+    const int2 st = ld_const(p.wg_start + g);
+    cf.start(p, st.x, st.y);
+    ci = cf;
+    cc = cf;
+  }
+
+  // QK operand of this wave's i-th k-step kk = 4 (i / kG) + kG ds + i % kG
+  // (lane: token tok, chunk 2 kk + hi): kk < 32 at
+  // (qk0 ^ 32 (i % kG)) + 128 (i / kG), kk >= 32 (rope) at rope0 ^ 32 (i % kG)
+  // (the XOR only touches the swizzled chunk bits 4..6)
+  const uint32_t qk0 = (uint32_t)(1024 * tok + 16 * ((2 * kG * ds) ^ hi ^ chunk_swz(tok)));
+  const uint32_t rope0 = (uint32_t)(kRopeBase + 128 * tok + 16 * ((2 * kG * ds) ^ hi ^ chunk_swz(tok)));
+  // PV transposing loads: in 16-lane group g, lane 4r + q supplies dims
+  // 32 db + 16 (g & 1) + 4 q .. + 3 of token 16 m + 8 h + 4 (g >> 1) + r
+  // (h = first or second load); pv0 is its address for db = 0, and db = 1
+  // differs in bit 6 only (chunk 4 + y instead of y under the swizzle)
+  uint32_t pv0;
+  {
+    const int g16 = lane >> 4, r = (lane >> 2) & 3, q = lane & 3;
+    const int tl = 4 * (g16 >> 1) + r;
+    const int y = 2 * (g16 & 1) + (q >> 1);
+    pv0 = (uint32_t)(1024 * tl + 16 * (y ^ chunk_swz(tl)) + 8 * (q & 1) + 64 * kDb * ds);
+  }
+
+  uint8_t* const qmine = qlds + 16 * (kQInLds * 64 * wave + lane);
+  bf16x8_t qreg[kQRegSteps];
+  // ops: vector-memory operations this wave has issued; pos[i]: ops right
+  // after issuing the copies of tile t + i
+  int ops = 0;
+  int pos[kNS - 1];
+#pragma unroll
+  for (int i = 0; i < kNS - 1; ++i) pos[i] = 0;
+  int t = 0, stage = 0;   // stage holds tile t
+  while (t < Uw) {
+    const int b = cc.b, rb = cc.rb, tile0 = cc.tile, ntiles = cc.ntiles, cnt = cc.cnt;
+    const int n = min(ntiles - tile0, Uw - t);
+
+    // the piece's queries, this wave's k-steps (rows past the last query row
+    // read as zero); the last kQInLds k-steps go to this wave's LDS slot
+    const int row = rb * kRowsBlk + rg * 32 + tok;
+    const bool row_ok = row < p.rows;
+    {
+      const uint16_t* qrow = p.q + ((long long)b * p.rows + (row_ok ? row : 0)) * kDqk + 8 * hi;
+#pragma unroll
+      for (int i = 0; i < kKS; ++i) {
+        const int kk = 4 * (i / kG) + kG * ds + i % kG;
+        bf16x8_t x = *(const bf16x8_t*)(qrow + 16 * kk);
+        x = row_ok ? x : bf16x8_t{};
+        if (i < kQRegSteps) qreg[i] = x;
+        else *(bf16x8_t*)(qmine + 16 * 64 * (i - kQRegSteps)) = x;
+      }
+    }
+    if (t == 0) {
+      // row indices of the first tiles, in flight with the queries
+#pragma unroll
+      for (int k = 0; k < kAheadRows; ++k) {
+        if (k < Uw) {
+          if (k > 0) cf.advance(p);
+          fetch_rows(p, cf, ring_lds + 4 * kTile * (k % kRing));
+        }
+      }
+    }
+    // the query loads are the only loads the compiler tracks: waiting for
+    // everything here keeps its own waits out of the tile loop (for later
+    // pieces the tile copies in flight land meanwhile)
+    wait_vmcnt<0>();
+    if (t == 0) {
+      __syncthreads();
+      // the first kNS - 1 tiles
+#pragma unroll
+      for (int k = 0; k < kNS - 1; ++k) {
+        if (k < Uw) {
+          if (k > 0) ci.advance(p);
+          issue_tile(p, ci, smem_lds + kStageBytes * k, ring + kTile * k);
+          ops += kDmaPerWave;
+          pos[k] = ops;
+        }
+      }
+    }
+    // owned tokens row (draft i) may see: t = j S + r <= L - q_len + i; the
+    // count is computed per draft index with scalar arithmetic and selected
+    int jvis = 0;
+    {
+      int L = ld_const(p.seq_lens + b);
+      L = L < 0 ? 0 : min(L, p.max_pages * kPage);
+      const int i = (row >= p.heads) + (row >= 2 * p.heads) + (row >= 3 * p.heads);
+      for (int k = 0; k < p.q_len; ++k) {
+        const int lim = L - p.q_len + k - p.shard;
+        const int jl = lim >= 0 ? min(cnt, lim / p.num_shards + 1) : 0;
+        jvis = i == k ? jl : jvis;
+      }
+    }
+    // tiles that end at or before jvis_min need no visibility mask (rows
+    // past the last query row are never written and do not count)
+    int jvis_min = row_ok ? jvis : INT_MAX;
+    jvis_min = min(jvis_min, __shfl_xor(jvis_min, 1));
+    jvis_min = min(jvis_min, __shfl_xor(jvis_min, 2));
+    jvis_min = min(jvis_min, __shfl_xor(jvis_min, 4));
+    jvis_min = min(jvis_min, __shfl_xor(jvis_min, 8));
+    jvis_min = min(jvis_min, __shfl_xor(jvis_min, 16));
+    jvis_min = min(jvis_min, __shfl_xor(jvis_min, 32));
+    jvis_min = __builtin_amdgcn_readfirstlane(jvis_min);
+
+    f32x16_t o[kDb];
+#pragma unroll
+    for (int db = 0; db < kDb; ++db) o[db] = f32x16_t{};
+    float m_ref = kNegInf, l_sum = 0.f;
+
+    for (int k = 0; k < n; ++k, ++t) {
+      // tile t has landed for this wave, then for all waves; the stage of
+      // tile t - 1 is free
+      wait_vm_after(ops - pos[0]);
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i + 1 < kNS - 1; ++i) pos[i] = pos[i + 1];
+      // table entry of this tile's token `tok`, read before any copy of this
+      // iteration is issued
+      const int raw_c = ring[kTile * (t % kRing) + tok];
+      if (t + kAheadRows < Uw) {
+        cf.advance(p);
+        fetch_rows(p, cf, ring_lds + 4 * kTile * ((t + kAheadRows) % kRing));
+        ops += 1;
+      }
+      if (t + kNS - 1 < Uw) {
+        ci.advance(p);
+        const int st_next = stage == 0 ? kNS - 1 : stage - 1;   // stage of tile t - 1
+        issue_tile(p, ci, smem_lds + kStageBytes * st_next, ring + kTile * ((t + kNS - 1) % kRing));
+        ops += kDmaPerWave;
+        pos[kNS - 2] = ops;
+      }
+
+      const uint8_t* ks = smem + kStageBytes * stage;
+      const int tile = tile0 + k;
+      const int jt = tile * kTile;
+      // tokens whose page is outside the pool poison their scores
+      const int rr = resolve_row(p, tile, cnt, tok, raw_c);
+      const uint64_t bad = __ballot(lane < kTile && rr == kRowBad);
+
+      // S^T[token][row] over this wave's k-steps; K operands are read two
+      // steps ahead of their MFMA
+      bf16x8_t ka[kAhead];
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u) ka[u] = qk_operand<kG>(ks, qk0, rope0, u);
+      f32x16_t s = f32x16_t{};
+#pragma unroll
+      for (int i = 0; i < kKS; ++i) {
+        const bf16x8_t a = ka[i % kAhead];
+        if (i + kAhead < kKS) {
+          const int u = i + kAhead;
+          ka[i % kAhead] = qk_operand<kG>(ks, qk0, rope0, u);
+        }
+        const bf16x8_t qb = i < kQRegSteps ? qreg[i < kQRegSteps ? i : 0]
+                                           : *(const bf16x8_t*)(qmine + 16 * 64 * (i - kQRegSteps));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb, s, 0, 0, 0);
+      }
+      if constexpr (kDS > 1) {
+        // sum the row group's partial scores in wave order
+        f32x4_t* mine = xbuf + (wave * 4) * 64 + lane;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) mine[64 * q] = f32x4_t{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
+        __syncthreads();
+        f32x16_t tot = f32x16_t{};
+#pragma unroll
+        for (int d = 0; d < kDS; ++d) {
+          const f32x4_t* src = xbuf + ((d * kRG + rg) * 4) * 64 + lane;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4_t v = src[64 * q];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tot[4 * q + e] += v[e];
+          }
+        }
+        s = tot;
+      }
+
+      // online softmax in base 2 (this lane: one row, 16 tokens: value v is
+      // token 8 (v >> 2) + 4 hi + (v & 3))
+      float tmax = kNegInf;
+      if (jt + kTile <= jvis_min && bad == 0) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          s[v] *= p.scale_log2;
+          tmax = fmaxf(tmax, s[v]);
+        }
+      } else {
+        // masks shifted by 4 hi once so each test is against a constant
+        const int lim = jvis - jt - 4 * hi;
+        const uint32_t badl = (uint32_t)bad >> (4 * hi);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int c = 8 * (v >> 2) + (v & 3);
+          float x = c < lim ? s[v] * p.scale_log2 : kNegInf;
+          x = ((badl >> c) & 1u) ? __builtin_nanf("") : x;
+          s[v] = x;
+          tmax = fmaxf(tmax, x);
+        }
+      }
+      tmax = xor32_max(tmax);
+      const bool grow = m_ref != kNegInf && tmax > m_ref + kRescaleSlack;
+      if (__builtin_expect(__ballot(grow) != 0, 0)) {
+        const float f = grow ? exp2_fast(m_ref - tmax) : 1.f;
+        l_sum *= f;
+        // o[.][v] belongs to row 8 (v >> 2) + 4 hi + (v & 3), whose factor
+        // sits in that row's lane
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float fv = __shfl(f, 8 * (v >> 2) + 4 * hi + (v & 3));
+#pragma unroll
+          for (int db = 0; db < kDb; ++db) o[db][v] = acc_scale(o[db][v], fv);
+        }
+        m_ref = grow ? tmax : m_ref;
+      }
+      m_ref = m_ref == kNegInf ? tmax : m_ref;
+      const float m_use = m_ref == kNegInf ? 0.f : m_ref;
+      bf16x8_t pb[2];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float pv = exp2_fast(s[v] - m_use);
+        l_sum += pv;
+        pb[v >> 3][v & 7] = (__bf16)pv;
+      }
+
+      // O[row][dim] += P[row][token] V[token][dim] over this wave's dims: the
+      // P registers (lane = row) are the A operand and the transposed V reads
+      // (lane = dim) the B operand, both with the same token order in k; the
+      // accumulator then holds 32 consecutive dims across lanes, so the
+      // output stores write whole lines
+      bf16x8_t va[kAhead];
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u) va[u] = pv_operand(ks, pv0, u);
+#pragma unroll
+      for (int st = 0; st < kPvSteps; ++st) {
+        const bf16x8_t a = va[st % kAhead];
+        if (st + kAhead < kPvSteps) va[st % kAhead] = pv_operand(ks, pv0, st + kAhead);
+        o[st >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb[st & 1], a, o[st >> 1], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 1);
+#pragma unroll
+      for (int st = 0; st < kPvSteps; ++st) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        if (st + kAhead < kPvSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
+      stage = stage + 1 == kNS ? 0 : stage + 1;
+    }
+
+    // piece epilogue: o[db][v] is row 8 (v >> 2) + 4 hi + (v & 3) of the
+    // row group, dim 32 (kDb ds + db) + (lane & 31)
+    const float l_tot = xor32_sum(l_sum);
+    const bool any = l_tot > 0.f || l_tot != l_tot;
+    const float inv = any ? p.out_scale / l_tot : 0.f;
+    const float lse2 = any ? m_ref + log2_fast(l_tot) : kNegInf;
+    const bool single = tile0 == 0 && n == ntiles;
+    const int row0 = rb * kRowsBlk + rg * 32;          // first row of the row group
+    const int dim = 32 * kDb * ds + (lane & 31);
+    long long base;                                    // element index of (row0, dim)
+    if (single) {
+      base = ((long long)b * p.rows + row0) * kDv + dim;
+    } else {
+      const int4 si = ld_const(p.seg_info + b * p.row_blocks + rb);
+      base = ((long long)(si.x + g - si.z) * kRowsBlk + rg * 32) * kDv + dim;
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = 8 * (v >> 2) + 4 * hi + (v & 3);
+      const float iv = __shfl(inv, r);
+      if (row0 + r < p.rows) {
+        const long long e0 = base + (long long)r * kDv;
+        if (single && !p.out_bf16) {
+          float* dst = (float*)p.out + e0;
+#pragma unroll
+          for (int db = 0; db < kDb; ++db) dst[32 * db] = acc_read(o[db][v]) * iv;
+        } else {
+          __bf16* dst = single ? (__bf16*)p.out + e0 : (__bf16*)p.spart_o + e0;
+#pragma unroll
+          for (int db = 0; db < kDb; ++db) dst[32 * db] = (__bf16)(acc_read(o[db][v]) * iv);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);   // one row at a time: short live ranges
+    }
+    if (row_ok && ds == 0 && hi == 0) {
+      if (single) {
+        p.lse[(long long)b * p.rows + row] = p.lse_base2 ? lse2 : lse2 * kLn2;
+      } else {
+        const int4 si = ld_const(p.seg_info + b * p.row_blocks + rb);
+        p.spart_lse[(long long)(si.x + g - si.z) * kRowsBlk + (row - rb * kRowsBlk)] = lse2;
+      }
+    }
+    if (t < Uw) {
+      cc.tile = ntiles - 1;
+      cc.advance(p);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// combine the pieces of segments cut at workgroup boundaries; neutral rows
+// for requests with no owned token
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void stream_combine_kernel(DecodeParams p) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (row >= p.rows) return;
+  const int rb = row / p.rows_blk;
+  const int4 si = p.seg_info[b * p.row_blocks + rb];
+  const int np = si.y;
+  if (np == 1) return;
+  const long long orow = (long long)b * p.rows + row;
+  f32x4_t acc0 = f32x4_t{}, acc1 = f32x4_t{};
+  float mx = kNegInf, wsum = 0.f;
+  if (np > 1) {
+    const long long prow0 = (long long)si.x * p.rows_blk + (row - rb * p.rows_blk);
+    for (int c = 0; c < np; ++c) mx = fmaxf(mx, p.spart_lse[prow0 + (long long)c * p.rows_blk]);
+    if (mx != kNegInf) {
+      for (int c = 0; c < np; ++c) {
+        const long long prow = prow0 + (long long)c * p.rows_blk;
+        const float w = exp2_fast(p.spart_lse[prow] - mx);
+        const u32x4_t x = *(const u32x4_t*)(p.spart_o + prow * kDv + 8 * lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc0[e] += w * __uint_as_float(x[e >> 1] << (16 * ((e & 1) ^ 1)) & 0xFFFF0000u);
+          acc1[e] += w * __uint_as_float(x[2 + (e >> 1)] << (16 * ((e & 1) ^ 1)) & 0xFFFF0000u);
+        }
+        wsum += w;
+      }
+    }
+  }
+  const bool any = wsum > 0.f;
+  const float inv = any ? 1.f / wsum : 0.f;
+  acc0 *= inv;
+  acc1 *= inv;
+  if (p.out_bf16) {
+    __bf16* dst = (__bf16*)p.out + orow * kDv + 8 * lane;
+    bf16x8_t v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = (__bf16)acc0[e];
+      v[4 + e] = (__bf16)acc1[e];
+    }
+    *(bf16x8_t*)dst = v;
+  } else {
+    f32x4_t* dst = (f32x4_t*)((float*)p.out + orow * kDv + 8 * lane);
+    dst[0] = acc0;
+    dst[1] = acc1;
+  }
+  if (lane == 0) {
+    const float lse2 = any ? mx + log2_fast(wsum) : kNegInf;
+    p.lse[orow] = p.lse_base2 ? lse2 : lse2 * kLn2;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_stream(const DecodeParams& p, hipEvent_t ev_begin, hipEvent_t ev_end,
+                                hipStream_t stream) {
+  if (p.batch == 0) return hipSuccess;
+  hipLaunchKernelGGL(stream_plan_kernel, dim3(1), dim3(1024), 0, stream, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (ev_begin) {
+    err = hipEventRecord(ev_begin, stream);
+    if (err != hipSuccess) return err;
+  }
+  if (p.rows_blk == 32) hipLaunchKernelGGL(attn_stream_kernel<4>, dim3(p.grid), dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(attn_stream_kernel<2>, dim3(p.grid), dim3(256), 0, stream, p);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (ev_end) {
+    err = hipEventRecord(ev_end, stream);
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(stream_combine_kernel, dim3(p.batch, (p.rows + 3) / 4), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace mla
