@@ -206,8 +206,12 @@ def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True, spl
     return wl, res
 
 
-def bench_merge_sweep(iters: int = 100, warmup: int = 10):
-    """Merge-only: 4 partials of [T, 64, 512] bf16 + fp32 LSE -> [T, 64, 512] bf16."""
+def bench_merge_sweep(replays: int = 20, warmup: int = 5):
+    """Merge-only: 4 partials of [T, 64, 512] bf16 + fp32 LSE -> [T, 64, 512] bf16.
+
+    Timed as graph replays (one merge per input set in the graph, sets rotated
+    so the MALL holds at most a fraction of them); the per-merge time is the
+    replay time / sets, i.e. back-to-back launches without host overhead."""
     import torch
 
     from decode_attention_paged_amd import _lib as L
@@ -217,29 +221,34 @@ def bench_merge_sweep(iters: int = 100, warmup: int = 10):
     for T in MERGE_TOKENS:
         mi = make_merge_inputs(T, seed=4000 + T)
         set_bytes = 4 * T * 64 * (512 * 2 + 4) + T * 64 * 512 * 2 + T * 64 * 4
-        nsets = max(2, min(32, int(math.ceil(600e6 / set_bytes))))
+        nsets = max(2, min(64, int(math.ceil(600e6 / set_bytes))))
         sets = []
-        for s in range(nsets):
+        for s_ in range(nsets):
             outs = [torch.from_numpy(o).view(torch.bfloat16).cuda() for o in mi.outs]
             lses = [torch.from_numpy(l).cuda() for l in mi.lses]
             sets.append((outs, lses, torch.empty((T, 64, 512), dtype=torch.bfloat16, device="cuda"),
                          torch.empty((T, 64), dtype=torch.float32, device="cuda")))
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
         for k in range(warmup):
             o, l, y, yl = sets[k % nsets]
             L.mla_merge_partials(o, l, [L.LSE_BASE_E] * 4, y, yl)
         torch.cuda.synchronize()
-        for k in range(iters):
-            o, l, y, yl = sets[k % nsets]
-            evs[k][0].record()
-            L.mla_merge_partials(o, l, [L.LSE_BASE_E] * 4, y, yl)
-            evs[k][1].record()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for o, l, y, yl in sets:
+                L.mla_merge_partials(o, l, [L.LSE_BASE_E] * 4, y, yl)
+        graph.replay()
         torch.cuda.synchronize()
-        us = sorted(1e3 * a.elapsed_time(b) for a, b in evs)
-        med = statistics.median(us)
-        out[str(T)] = dict(us_median=med, us_min=us[0], bytes=set_bytes,
-                           gbs=set_bytes / (med * 1e-6) / 1e9, sets=nsets)
-        del sets
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(replays)]
+        for a, b in evs:
+            a.record()
+            graph.replay()
+            b.record()
+        torch.cuda.synchronize()
+        per = sorted(1e3 * a.elapsed_time(b) / nsets for a, b in evs)
+        med = statistics.median(per)
+        out[str(T)] = dict(us_median=med, us_min=per[0], bytes=set_bytes,
+                           gbs=set_bytes / (med * 1e-6) / 1e9, sets=nsets, timing="graph replay")
+        del sets, graph
     torch.cuda.empty_cache()
     return out
 
@@ -349,8 +358,11 @@ def main() -> int:
         roof = dict(bound="hbm", achieved=res["attn_kernel_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=res["attn_kernel_gbs"] / HBM_PEAK_GBS)
     roof["traffic"] = traffic_from_profile(wl.name)
-    roof["kernel"] = ("attn_kernel<fp8>" if wl.kv_dtype == "fp8" else "attn_direct_kernel") + \
-        " (mla_decode.hip), mean of %d launches" % (args.steps * wl.shards)
+    if wl.kv_dtype == "fp8":
+        kname = "attn_kernel<true> (mla_decode.hip)"
+    else:
+        kname = "attn_stream_kernel<%d> (mla_stream.hip)" % (4 if wl.heads * wl.q_len <= 32 else 2)
+    roof["kernel"] = kname + ", mean of %d launches" % (args.steps * wl.shards)
     roof["mean_launch_us"] = res["attn_kernel_mean_us"]
     roof["algorithmic_bytes_per_launch"] = res["attn_kernel_bytes_per_launch"]
 
@@ -373,6 +385,9 @@ def main() -> int:
                    "global_batch": wl.batch, "shards": wl.shards},
         "tflops": round(res["tflops"], 3),
         "merge_us": {T: round(v["us_median"], 2) for T, v in merge.items()} if merge else None,
+        "merge_roofline": (dict(bound="hbm", T=128, achieved=round(merge["128"]["gbs"], 1), peak=HBM_PEAK_GBS,
+                                unit="GB/s", frac=round(merge["128"]["gbs"] / HBM_PEAK_GBS, 4))
+                           if merge and "128" in merge else None),
         "roofline": roof,
         "cpu_baseline": cpu,
     }

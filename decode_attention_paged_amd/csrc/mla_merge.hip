@@ -7,7 +7,7 @@
 // sgl-project/sglang PR 33926 notes under its related PRs). Bandwidth-bound:
 // one wave per (row, head) vector, each lane owning 8 consecutive elements,
 // so every shard's vector is read with one coalesced 16- or 32-byte load per
-// lane and the output written once.
+// lane, all shards' loads in flight at once, and the output written once.
 //
 // Metadata: the shard-local lengths and token-granular KV indices of the
 // rank's cyclic slice (prhub.com.cn digest of sgl-project/sglang PR 33926,
@@ -21,26 +21,54 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 constexpr float kNegInf = -__builtin_inff();
 
+// Eight consecutive elements of shard r's partials at element index e, as fp32.
+__device__ __forceinline__ void load8(const MergeParams& p, int r, long long e, f32x4_t& lo, f32x4_t& hi) {
+  if (p.in_bf16) {
+    const bf16x8_t x = *(const bf16x8_t*)((const __bf16*)p.outs[r] + e);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      lo[k] = (float)x[k];
+      hi[k] = (float)x[4 + k];
+    }
+  } else {
+    const f32x4_t* x = (const f32x4_t*)((const float*)p.outs[r] + e);
+    lo = x[0];
+    hi = x[1];
+  }
+}
+
+// kS: shard count rounded up to a power of two (registers for kS vectors).
+template <int kS>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
-  const long long vec = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long vec = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
   if (vec >= p.vectors) return;
   const int lane = threadIdx.x & 63;
+  const int S = p.num_shards;
 
-  float lse2[kMaxShards];
-  float mx = kNegInf;
+  // every load of the wave is issued before any result is used: the shards'
+  // LSEs (scalar loads, the vector index is wave-uniform) and the first
+  // 512-element chunk of every shard's vector (one 16- or 32-byte load per
+  // lane); a shard with weight 0 holds zeros, so loading it is harmless
+  float lse2[kS];
+  f32x4_t x0[kS], x1[kS];
+  const int e_first = 8 * lane;
+  const bool have = e_first < p.dv;
 #pragma unroll
-  for (int r = 0; r < kMaxShards; ++r) {
-    if (r < p.num_shards) {
-      const float v = p.lses[r][vec];
-      lse2[r] = v * p.lse_to_log2[r];     // -inf stays -inf (multiplier > 0)
-      mx = fmaxf(mx, lse2[r]);
+  for (int r = 0; r < kS; ++r) {
+    if (r < S) {
+      lse2[r] = *(const __attribute__((address_space(4))) float*)(p.lses[r] + vec) * p.lse_to_log2[r];
+      if (have) load8(p, r, vec * p.dv + e_first, x0[r], x1[r]);
     }
   }
-  float w[kMaxShards];
+  float mx = kNegInf;
+#pragma unroll
+  for (int r = 0; r < kS; ++r)
+    if (r < S) mx = fmaxf(mx, lse2[r]);   // -inf stays -inf (multiplier > 0)
+  float w[kS];
   float wsum = 0.f;
 #pragma unroll
-  for (int r = 0; r < kMaxShards; ++r) {
-    if (r < p.num_shards) {
+  for (int r = 0; r < kS; ++r) {
+    if (r < S) {
       w[r] = mx == kNegInf ? 0.f : __builtin_amdgcn_exp2f(lse2[r] - mx);
       wsum += w[r];
     }
@@ -48,23 +76,18 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   const bool any = wsum > 0.f;
   const float inv = any ? 1.f / wsum : 0.f;
 
-  for (int e0 = 8 * lane; e0 < p.dv; e0 += 512) {
+  for (int e0 = e_first; e0 < p.dv; e0 += 512) {
+    if (e0 != e_first) {
+#pragma unroll
+      for (int r = 0; r < kS; ++r)
+        if (r < S) load8(p, r, vec * p.dv + e0, x0[r], x1[r]);
+    }
     f32x4_t a0 = f32x4_t{}, a1 = f32x4_t{};
 #pragma unroll
-    for (int r = 0; r < kMaxShards; ++r) {
-      if (r < p.num_shards && w[r] != 0.f) {
-        if (p.in_bf16) {
-          const bf16x8_t x = *(const bf16x8_t*)((const __bf16*)p.outs[r] + vec * p.dv + e0);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            a0[k] += w[r] * (float)x[k];
-            a1[k] += w[r] * (float)x[4 + k];
-          }
-        } else {
-          const f32x4_t* x = (const f32x4_t*)((const float*)p.outs[r] + vec * p.dv + e0);
-          a0 += w[r] * x[0];
-          a1 += w[r] * x[1];
-        }
+    for (int r = 0; r < kS; ++r) {
+      if (r < S && w[r] != 0.f) {
+        a0 += w[r] * x0[r];
+        a1 += w[r] * x1[r];
       }
     }
     a0 *= inv;
@@ -122,7 +145,12 @@ __global__ __launch_bounds__(256) void metadata_kernel(const int32_t* seq_lens, 
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
   if (p.vectors == 0) return hipSuccess;
   const long long blocks = (p.vectors + 3) / 4;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  const dim3 grid((unsigned)blocks), block(256);
+  if (p.num_shards <= 1) hipLaunchKernelGGL(merge_kernel<1>, grid, block, 0, stream, p);
+  else if (p.num_shards <= 2) hipLaunchKernelGGL(merge_kernel<2>, grid, block, 0, stream, p);
+  else if (p.num_shards <= 4) hipLaunchKernelGGL(merge_kernel<4>, grid, block, 0, stream, p);
+  else if (p.num_shards <= 8) hipLaunchKernelGGL(merge_kernel<8>, grid, block, 0, stream, p);
+  else hipLaunchKernelGGL(merge_kernel<16>, grid, block, 0, stream, p);
   return hipGetLastError();
 }
 

@@ -233,29 +233,46 @@ __device__ __forceinline__ int resolve_row(const DecodeParams& p, int tile, int 
 // tokens differ in the 32-byte pair they select.
 __host__ __device__ constexpr int chunk_swz(int t) { return 2 * (t & 3) + ((t >> 2) & 1); }
 
-// Copies of one tile into a stage. Stage layout (token-major, swizzled):
+// Copies of one tile into a stage (issue_tile, or its parts spread over a
+// tile loop iteration). Stage layout (token-major, swizzled):
 //   chunk c < 64 (dims 8c .. 8c + 7) of token t at byte 1024 t + 16 (c ^ swz(t)),
 //   chunk c >= 64 (rope) at kRopeBase + 128 t + 16 ((c - 64) ^ swz(t)).
 // Wave w moves tokens 8w .. 8w + 7: one copy per token for its first 1 KB
 // (64 lanes over one row, so every copy reads whole 128-byte lines) and one
 // copy for the eight 128-byte rope tails. The row of each token comes from
 // the ring; the main copies take it as a scalar base address.
-__device__ __forceinline__ void issue_tile(const DecodeParams& p, const Cursor& c, uint32_t stage_lds,
-                                           const int32_t* ring_slot) {
+// Row of token 8w + (lane >> 3) of the cursor's tile for wave w (0 if the
+// token is past the end or its page is outside the pool).
+__device__ __forceinline__ int tile_rows(const DecodeParams& p, const Cursor& c, const int32_t* ring_slot) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tk = 8 * wave + (lane >> 3);   // this lane's token for the rope copy
+  const int tk = 8 * wave + (lane >> 3);
   const int row = resolve_row(p, c.tile, c.cnt, tk, ring_slot[tk]);
-  const long long rowc = row >= 0 ? row : 0;
-  lds_dma16(p.kv + rowc * (2 * kDqk) + 16 * (64 + ((lane & 7) ^ chunk_swz(lane >> 3))),
+  return row >= 0 ? row : 0;
+}
+__device__ __forceinline__ void copy_rope(const DecodeParams& p, int rowc, uint32_t stage_lds) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  lds_dma16(p.kv + (long long)rowc * (2 * kDqk) + 16 * (64 + ((lane & 7) ^ chunk_swz(lane >> 3))),
             __builtin_amdgcn_readfirstlane(stage_lds + kRopeBase + 1024 * wave));
+}
+template <int kI0, int kI1>
+__device__ __forceinline__ void copy_main(const DecodeParams& p, int rowc, uint32_t stage_lds) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = __builtin_amdgcn_readlane((int)rowc, 8 * i);
+  for (int i = kI0; i < kI1; ++i) {
+    const int r = __builtin_amdgcn_readlane(rowc, 8 * i);
     const uint8_t* base = p.kv + (long long)r * (2 * kDqk);
     lds_dma16_sbase(base, (uint32_t)(16 * (lane ^ chunk_swz(i))),
                     __builtin_amdgcn_readfirstlane(stage_lds + 1024 * (8 * wave + i)));
   }
+}
+__device__ __forceinline__ void issue_tile(const DecodeParams& p, const Cursor& c, uint32_t stage_lds,
+                                           const int32_t* ring_slot) {
+  const int rowc = tile_rows(p, c, ring_slot);
+  copy_rope(p, rowc, stage_lds);
+  copy_main<0, 8>(p, rowc, stage_lds);
 }
 
 // Wait until at most `after` vector-memory operations of this wave are
@@ -341,7 +358,7 @@ void attn_stream_kernel(DecodeParams p) {
   constexpr int kQInLds = kDS == 1 ? 12 : 0;
   constexpr int kQRegSteps = kKS - kQInLds;
   constexpr int kPvSteps = 2 * kDb;
-  constexpr int kAhead = 2;
+  constexpr int kAhead = 4;
   static_assert(kAheadRows < kRing, "row ring too small");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * kStageBytes];
@@ -483,21 +500,8 @@ void attn_stream_kernel(DecodeParams p) {
       __syncthreads();
 #pragma unroll
       for (int i = 0; i + 1 < kNS - 1; ++i) pos[i] = pos[i + 1];
-      // table entry of this tile's token `tok`, read before any copy of this
-      // iteration is issued
+      // table entry of this tile's token `tok`
       const int raw_c = ring[kTile * (t % kRing) + tok];
-      if (t + kAheadRows < Uw) {
-        cf.advance(p);
-        fetch_rows(p, cf, ring_lds + 4 * kTile * ((t + kAheadRows) % kRing));
-        ops += 1;
-      }
-      if (t + kNS - 1 < Uw) {
-        ci.advance(p);
-        const int st_next = stage == 0 ? kNS - 1 : stage - 1;   // stage of tile t - 1
-        issue_tile(p, ci, smem_lds + kStageBytes * st_next, ring + kTile * ((t + kNS - 1) % kRing));
-        ops += kDmaPerWave;
-        pos[kNS - 2] = ops;
-      }
 
       const uint8_t* ks = smem + kStageBytes * stage;
       const int tile = tile0 + k;
@@ -528,6 +532,28 @@ void attn_stream_kernel(DecodeParams p) {
         f32x4_t* mine = xbuf + (wave * 4) * 64 + lane;
 #pragma unroll
         for (int q = 0; q < 4; ++q) mine[64 * q] = f32x4_t{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
+      }
+      // the next copies (into the stage of tile t - 1, free since the loop
+      // top) are issued here, where the wave would otherwise wait for the
+      // other waves' partial scores: a stalled issue costs nothing then
+      if (t + kAheadRows < Uw) {
+        cf.advance(p);
+        fetch_rows(p, cf, ring_lds + 4 * kTile * ((t + kAheadRows) % kRing));
+        ops += 1;
+      }
+      // copies of tile t + kNS - 1, in three parts over the iteration so that
+      // their issue does not stall on a full memory queue
+      const bool more = t + kNS - 1 < Uw;
+      const uint32_t st_next = smem_lds + kStageBytes * (stage == 0 ? kNS - 1 : stage - 1);   // tile t - 1's
+      int rows_next = 0;
+      if (more) {
+        ci.advance(p);
+        rows_next = tile_rows(p, ci, ring + kTile * ((t + kNS - 1) % kRing));
+        copy_rope(p, rows_next, st_next);
+        copy_main<0, 3>(p, rows_next, st_next);
+        ops += 4;
+      }
+      if constexpr (kDS > 1) {
         __syncthreads();
         f32x16_t tot = f32x16_t{};
 #pragma unroll
@@ -590,6 +616,11 @@ void attn_stream_kernel(DecodeParams p) {
         pb[v >> 3][v & 7] = (__bf16)pv;
       }
 
+      if (more) {
+        copy_main<3, 6>(p, rows_next, st_next);
+        ops += 3;
+      }
+
       // O[row][dim] += P[row][token] V[token][dim] over this wave's dims: the
       // P registers (lane = row) are the A operand and the transposed V reads
       // (lane = dim) the B operand, both with the same token order in k; the
@@ -609,6 +640,11 @@ void attn_stream_kernel(DecodeParams p) {
       for (int st = 0; st < kPvSteps; ++st) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
         if (st + kAhead < kPvSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
+      if (more) {
+        copy_main<6, 8>(p, rows_next, st_next);
+        ops += 2;
+        pos[kNS - 2] = ops;
       }
       stage = stage + 1 == kNS ? 0 : stage + 1;
     }
