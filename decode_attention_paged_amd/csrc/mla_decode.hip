@@ -28,6 +28,7 @@
 //           leaves in each lane, so P never leaves registers.
 #include "mla_device.h"
 
+#include <hip/hip_ext.h>
 #include <limits.h>
 
 namespace mla {
@@ -772,22 +773,22 @@ hipError_t launch_decode(const DecodeParams& p, bool fp8, hipEvent_t ev_begin, h
   if (err != hipSuccess) return err;
   const int items = p.batch + p.split_target;
   const int grid = p.row_blocks == 1 ? items : ((items + 7) / 8) * 8 * p.row_blocks;
-  if (ev_begin) {
-    err = hipEventRecord(ev_begin, stream);
-    if (err != hipSuccess) return err;
-  }
   const int nw = p.rows >= 128 ? 4 : (p.rows + 31) / 32;
-  if (fp8) hipLaunchKernelGGL(attn_kernel<true>, dim3(grid), dim3(256), 0, stream, p);
-  else if (nw == 4) hipLaunchKernelGGL(attn_direct_kernel<4>, dim3(grid), dim3(256), 0, stream, p);
-  else if (nw == 2) hipLaunchKernelGGL(attn_direct_kernel<2>, dim3(grid), dim3(128), 0, stream, p);
-  else if (nw == 3) hipLaunchKernelGGL(attn_direct_kernel<4>, dim3(grid), dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL(attn_direct_kernel<1>, dim3(grid), dim3(64), 0, stream, p);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  if (ev_end) {
-    err = hipEventRecord(ev_end, stream);
-    if (err != hipSuccess) return err;
+  void* args[] = {const_cast<DecodeParams*>(&p)};
+  const void* fn;
+  dim3 block(256);
+  if (fp8) fn = reinterpret_cast<const void*>(&attn_kernel<true>);
+  else if (nw == 4 || nw == 3) fn = reinterpret_cast<const void*>(&attn_direct_kernel<4>);
+  else if (nw == 2) {
+    fn = reinterpret_cast<const void*>(&attn_direct_kernel<2>);
+    block = dim3(128);
+  } else {
+    fn = reinterpret_cast<const void*>(&attn_direct_kernel<1>);
+    block = dim3(64);
   }
+  // the events, when given, take the attention kernel's own start and end times
+  err = hipExtLaunchKernel(fn, dim3(grid), block, args, 0, stream, ev_begin, ev_end, 0);
+  if (err != hipSuccess) return err;
   hipLaunchKernelGGL(combine_kernel, dim3(p.batch, (p.rows + 3) / 4), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

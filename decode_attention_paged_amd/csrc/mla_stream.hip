@@ -27,6 +27,8 @@
 // tile it needs (s_waitcnt vmcnt(n) with n counted by the wave).
 #include "mla_device.h"
 
+#include <hip/hip_ext.h>
+
 #include <limits.h>
 
 namespace mla {
@@ -50,20 +52,35 @@ constexpr int kRowBad = -1;       // page id or row outside the pool
 // ---------------------------------------------------------------------------
 // plan
 // ---------------------------------------------------------------------------
-// Block-wide inclusive scan of one int per thread (1024 threads).
-__device__ __forceinline__ int block_scan(int v, int* s_scan) {
-  const int tid = threadIdx.x;
-  s_scan[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int x = tid >= off ? s_scan[tid - off] : 0;
-    __syncthreads();
-    s_scan[tid] += x;
-    __syncthreads();
+// Exclusive scan of a pair of ints per thread over the 1024-thread block
+// (wave scans with shuffles, then the 16 wave totals); `total` gets the sums.
+__device__ __forceinline__ int2 block_excl_scan2(int a, int b, int2* s_wave, int2& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int ia = a, ib = b;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int xa = __shfl_up(ia, off), xb = __shfl_up(ib, off);
+    if (lane >= off) {
+      ia += xa;
+      ib += xb;
+    }
   }
-  const int r = s_scan[tid];
+  if (lane == 63) s_wave[wave] = make_int2(ia, ib);
   __syncthreads();
-  return r;
+  int pa = 0, pb = 0, ta = 0, tb = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const int2 v = s_wave[w];
+    if (w < wave) {
+      pa += v.x;
+      pb += v.y;
+    }
+    ta += v.x;
+    tb += v.y;
+  }
+  __syncthreads();
+  total = make_int2(ta, tb);
+  return make_int2(pa + ia - a, pb + ib - b);
 }
 
 // Last index i in [0, n) with a[i] <= x (a nondecreasing, a[0] <= x).
@@ -77,54 +94,63 @@ __device__ __forceinline__ int last_le(const int32_t* a, int n, long long x) {
   return lo;
 }
 
+__device__ __forceinline__ int seg_tiles(const DecodeParams& p, int s) {
+  const int b = s / p.row_blocks;
+  return (local_count(p, b) + kTile - 1) / kTile;
+}
+
+// One workgroup of 1024 threads; thread i handles a contiguous block of
+// segments. The segment offsets stay in LDS when they fit (the binary
+// searches then cost LDS latency only), else in the workspace.
+constexpr int kPlanLdsSegs = 6144;
+
 __global__ __launch_bounds__(1024) void stream_plan_kernel(DecodeParams p) {
-  __shared__ int s_scan[1024];
-  __shared__ int s_scan2[1024];
+  __shared__ int32_t s_arr[2 * (kPlanLdsSegs + 1)];
+  __shared__ int32_t s_wgu[kMaxGrid + 1];
+  __shared__ int2 s_wave[16];
   const int tid = threadIdx.x;
   const int RB = p.row_blocks;
   const int nseg = p.batch * RB;
+  const bool in_lds = nseg <= kPlanLdsSegs;
+  int32_t* const off = in_lds ? s_arr : p.seg_off;              // unit offset of each segment
+  int32_t* const coff = in_lds ? s_arr + kPlanLdsSegs + 1 : p.seg_coff;   // cost offset
+  const int per = (nseg + 1023) / 1024;
+  const int s0 = min(tid * per, nseg), s1 = min(s0 + per, nseg);
 
-  // tiles of every segment, their unit offsets and their cost offsets (a
-  // segment costs its tiles plus kPieceCost for loading its queries)
-  int carry = 0, ccarry = 0;
-  for (int base = 0; base < nseg; base += 1024) {
-    const int s = base + tid;
-    int n = 0;
-    if (s < nseg) {
-      const int b = s / RB;
-      const int cnt = local_count(p, b);
-      if (s - b * RB == 0) p.req_cnt[b] = cnt;
-      n = (cnt + kTile - 1) / kTile;
-    }
-    const int c = n > 0 ? n + kPieceCost : 0;
-    s_scan2[tid] = c;
-    const int inc = block_scan(n, s_scan);
-    // second scan in place over s_scan2 (same pattern)
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int x = tid >= off ? s_scan2[tid - off] : 0;
-      __syncthreads();
-      s_scan2[tid] += x;
-      __syncthreads();
-    }
-    const int cinc = s_scan2[tid];
-    if (s < nseg) {
-      p.seg_off[s] = carry + inc - n;
-      p.seg_coff[s] = ccarry + cinc - c;
-    }
-    carry += s_scan[1023];
-    ccarry += s_scan2[1023];
-    __syncthreads();
+  // tiles and costs (a segment costs its tiles plus kPieceCost for loading
+  // its queries) of this thread's segments, scanned over the block
+  int su = 0, sc = 0;
+  for (int s = s0; s < s1; ++s) {
+    const int b = s / RB;
+    const int cnt = local_count(p, b);
+    if (s - b * RB == 0) p.req_cnt[b] = cnt;
+    const int n = (cnt + kTile - 1) / kTile;
+    su += n;
+    sc += n > 0 ? n + kPieceCost : 0;
   }
-  const int U = carry, C = ccarry;
+  int2 tot;
+  const int2 ex = block_excl_scan2(su, sc, s_wave, tot);
+  {
+    int u = ex.x, c = ex.y;
+    for (int s = s0; s < s1; ++s) {
+      const int n = seg_tiles(p, s);
+      off[s] = u;
+      coff[s] = c;
+      u += n;
+      c += n > 0 ? n + kPieceCost : 0;
+    }
+  }
+  const int U = tot.x, C = tot.y;
   // workgroups in use: at most one per cost unit, so consecutive workgroup
   // boundaries differ and only a piece's first workgroup can start inside
   // its query-load cost
   const int G = min(p.grid, C);
   if (tid == 0) {
-    p.seg_off[nseg] = U;
-    p.seg_coff[nseg] = C;
+    off[nseg] = U;
+    coff[nseg] = C;
     p.plan[0] = U;
     p.plan[1] = G;
+    s_wgu[G] = U;
     p.wg_ustart[G] = U;
   }
   __syncthreads();
@@ -133,34 +159,37 @@ __global__ __launch_bounds__(1024) void stream_plan_kernel(DecodeParams p) {
   // sequence (a boundary inside a segment's query cost maps to its first tile)
   for (int g = tid; g < G; g += 1024) {
     const long long x = (long long)g * C / G;
-    const int s = last_le(p.seg_coff, nseg + 1, x);
-    const int n = p.seg_off[s + 1] - p.seg_off[s];
-    long long k = x - p.seg_coff[s] - kPieceCost;
+    const int s = last_le(coff, nseg + 1, x);
+    const int n = off[s + 1] - off[s];
+    long long k = x - coff[s] - kPieceCost;
     k = k < 0 ? 0 : (k > n - 1 ? n - 1 : k);
-    p.wg_ustart[g] = p.seg_off[s] + (int)k;
+    s_wgu[g] = off[s] + (int)k;
+    p.wg_ustart[g] = off[s] + (int)k;
     p.wg_start[g] = make_int2(s, (int)k);
   }
   __syncthreads();
 
   // pieces of each segment (one per non-empty workgroup it meets) and
-  // partial slots
-  int slots = 0;
-  for (int base = 0; base < nseg; base += 1024) {
-    const int s = base + tid;
-    int np = 0, first = 0;
-    if (s < nseg) {
-      const int o = p.seg_off[s];
-      const int n = p.seg_off[s + 1] - o;
-      if (n > 0) {
-        first = last_le(p.wg_ustart, G, o);
-        np = last_le(p.wg_ustart, G, o + n - 1) - first + 1;
-      }
+  // partial slots (only for segments cut into several pieces)
+  int ms = 0;
+  for (int s = s0; s < s1; ++s) {
+    const int o = off[s], n = off[s + 1] - o;
+    if (n > 0) {
+      const int np = last_le(s_wgu, G, o + n - 1) - last_le(s_wgu, G, o) + 1;
+      ms += np > 1 ? np : 0;
     }
-    const int m = np > 1 ? np : 0;
-    const int inc = block_scan(m, s_scan);
-    if (s < nseg) p.seg_info[s] = make_int4(slots + inc - m, np, first, 0);
-    slots += s_scan[1023];
-    __syncthreads();
+  }
+  const int2 ex2 = block_excl_scan2(ms, 0, s_wave, tot);
+  int slot = ex2.x;
+  for (int s = s0; s < s1; ++s) {
+    const int o = off[s], n = off[s + 1] - o;
+    int np = 0, first = 0;
+    if (n > 0) {
+      first = last_le(s_wgu, G, o);
+      np = last_le(s_wgu, G, o + n - 1) - first + 1;
+    }
+    p.seg_info[s] = make_int4(slot, np, first, 0);
+    slot += np > 1 ? np : 0;
   }
 }
 
@@ -763,18 +792,13 @@ hipError_t launch_decode_stream(const DecodeParams& p, hipEvent_t ev_begin, hipE
   hipLaunchKernelGGL(stream_plan_kernel, dim3(1), dim3(1024), 0, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (ev_begin) {
-    err = hipEventRecord(ev_begin, stream);
-    if (err != hipSuccess) return err;
-  }
-  if (p.rows_blk == 32) hipLaunchKernelGGL(attn_stream_kernel<4>, dim3(p.grid), dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL(attn_stream_kernel<2>, dim3(p.grid), dim3(256), 0, stream, p);
-  err = hipGetLastError();
+  // the events, when given, take the attention kernel's own start and end
+  // times (recorded with the dispatch, no separate marker packets)
+  void* args[] = {const_cast<DecodeParams*>(&p)};
+  const void* fn = p.rows_blk == 32 ? reinterpret_cast<const void*>(&attn_stream_kernel<4>)
+                                    : reinterpret_cast<const void*>(&attn_stream_kernel<2>);
+  err = hipExtLaunchKernel(fn, dim3(p.grid), dim3(256), args, 0, stream, ev_begin, ev_end, 0);
   if (err != hipSuccess) return err;
-  if (ev_end) {
-    err = hipEventRecord(ev_end, stream);
-    if (err != hipSuccess) return err;
-  }
   hipLaunchKernelGGL(stream_combine_kernel, dim3(p.batch, (p.rows + 3) / 4), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
