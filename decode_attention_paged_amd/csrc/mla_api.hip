@@ -63,32 +63,21 @@ namespace mla {
 
 WorkspaceLayout decode_workspace_layout(int32_t batch, int32_t rows) {
   WorkspaceLayout w{};
-  const int64_t items = (int64_t)batch + kSplitTargetMax;
-  w.max_items = (int32_t)(((items + 7) / 8) * 8);
   const int32_t rows_blk = stream_rows_per_block(rows);
   const int64_t nseg = (int64_t)batch * ((rows + rows_blk - 1) / rows_blk);
   // a segment is cut into pieces only at workgroup boundaries
   w.max_slots = (int32_t)(nseg + kMaxGrid);
   size_t off = 0;
   w.plan = off;      off = align_up(off + 64, 256);
-  w.req_info = off;  off = align_up(off + sizeof(int2) * (size_t)batch, 256);
-  w.items = off;     off = align_up(off + sizeof(int2) * (size_t)w.max_items, 256);
   w.req_cnt = off;   off = align_up(off + sizeof(int32_t) * (size_t)batch, 256);
   w.seg_off = off;   off = align_up(off + sizeof(int32_t) * (size_t)(nseg + 1), 256);
   w.seg_coff = off;  off = align_up(off + sizeof(int32_t) * (size_t)(nseg + 1), 256);
   w.seg_info = off;  off = align_up(off + sizeof(int4) * (size_t)nseg, 256);
   w.wg_start = off;  off = align_up(off + sizeof(int2) * (size_t)kMaxGrid, 256);
   w.wg_ustart = off; off = align_up(off + sizeof(int32_t) * (size_t)(kMaxGrid + 1), 256);
-  // partial buffers: the fp8 chunked kernel (fp32) and the streaming kernel
-  // (bf16) never run in the same call, so they share one region
-  const size_t region = off;
-  w.part_lse = region;
-  w.part_o = align_up(region + sizeof(float) * (size_t)w.max_items * rows, 256);
-  const size_t end_chunked = align_up(w.part_o + sizeof(float) * (size_t)w.max_items * rows * kDv, 256);
-  w.spart_lse = region;
-  w.spart_o = align_up(region + sizeof(float) * (size_t)w.max_slots * rows_blk, 256);
-  const size_t end_stream = align_up(w.spart_o + sizeof(uint16_t) * (size_t)w.max_slots * rows_blk * kDv, 256);
-  w.total = end_chunked > end_stream ? end_chunked : end_stream;
+  w.spart_lse = off; off = align_up(off + sizeof(float) * (size_t)w.max_slots * rows_blk, 256);
+  w.spart_o = off;   off = align_up(off + sizeof(uint16_t) * (size_t)w.max_slots * rows_blk * kDv, 256);
+  w.total = off;
   return w;
 }
 
@@ -181,8 +170,8 @@ mla_status_t mla_decode_partial(const mla_decode_args_t* a, mla_lse_base_t* lse_
     return fail(MLA_STATUS_INVALID_ARGUMENT, "local_seq_lens and local_kv_indices go together");
   if (a->local_kv_indices != nullptr && a->local_kv_stride < 1)
     return fail(MLA_STATUS_INVALID_ARGUMENT, "local_kv_stride must be >= 1 (got %d)", a->local_kv_stride);
-  if (a->split_target < 0 || a->split_target > mla::kSplitTargetMax)
-    return fail(MLA_STATUS_INVALID_ARGUMENT, "split_target must be in [0, %d] (got %d)", mla::kSplitTargetMax, a->split_target);
+  if (a->split_target < 0 || a->split_target > mla::kMaxGrid)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "split_target must be in [0, %d] (got %d)", mla::kMaxGrid, a->split_target);
   if (a->batch > 0) {
     if (!a->q || !a->kv_pages || !a->block_table || !a->seq_lens || !a->out || !a->lse || !a->workspace)
       return fail(MLA_STATUS_INVALID_ARGUMENT, "q, kv_pages, block_table, seq_lens, out, lse and workspace are required");
@@ -196,17 +185,6 @@ mla_status_t mla_decode_partial(const mla_decode_args_t* a, mla_lse_base_t* lse_
 
   int cus = 0;
   if (device_cus(&cus) != 0) return fail(MLA_STATUS_DEVICE_ERROR, "cannot query the current device");
-  const int32_t row_blocks = (rows + mla::kRowsPerBlock - 1) / mla::kRowsPerBlock;
-  int32_t target = a->split_target;
-  if (target == 0) {
-    // workgroups of up to two waves fit twice per CU (LDS), larger ones once
-    const int32_t rows_per_block = rows < mla::kRowsPerBlock ? rows : mla::kRowsPerBlock;
-    const int32_t per_cu = rows_per_block <= 64 ? 2 : 1;
-    target = cus * per_cu / row_blocks;
-    if (target < 1) target = 1;
-  }
-  if (target > mla::kSplitTargetMax) target = mla::kSplitTargetMax;
-
   mla::DecodeParams p{};
   p.q = (const uint16_t*)a->q;
   p.kv = (const uint8_t*)a->kv_pages;
@@ -219,7 +197,6 @@ mla_status_t mla_decode_partial(const mla_decode_args_t* a, mla_lse_base_t* lse_
   p.heads = a->num_heads;
   p.q_len = a->q_len;
   p.rows = rows;
-  p.row_blocks = row_blocks;
   p.max_pages = a->max_pages;
   p.num_pages = a->num_pages;
   p.shard = a->shard_id;
@@ -233,12 +210,6 @@ mla_status_t mla_decode_partial(const mla_decode_args_t* a, mla_lse_base_t* lse_
   p.lse = a->lse;
   uint8_t* ws = (uint8_t*)a->workspace;
   p.plan = (int32_t*)(ws + w.plan);
-  p.req_info = (int2*)(ws + w.req_info);
-  p.items = (int2*)(ws + w.items);
-  p.part_lse = (float*)(ws + w.part_lse);
-  p.part_o = (float*)(ws + w.part_o);
-  p.max_items = w.max_items;
-  p.split_target = target;
   p.req_cnt = (int32_t*)(ws + w.req_cnt);
   p.seg_off = (int32_t*)(ws + w.seg_off);
   p.seg_coff = (int32_t*)(ws + w.seg_coff);
@@ -248,20 +219,18 @@ mla_status_t mla_decode_partial(const mla_decode_args_t* a, mla_lse_base_t* lse_
   p.spart_lse = (float*)(ws + w.spart_lse);
   p.spart_o = (uint16_t*)(ws + w.spart_o);
   p.rows_blk = mla::stream_rows_per_block(rows);
-  if (a->kv_dtype != MLA_DTYPE_FP8_E4M3) p.row_blocks = (rows + p.rows_blk - 1) / p.rows_blk;
+  p.row_blocks = (rows + p.rows_blk - 1) / p.rows_blk;
+  p.kv_fp8 = a->kv_dtype == MLA_DTYPE_FP8_E4M3;
   {
-    // bf16 KV: one persistent workgroup per CU (a multiple of 8 so that the
-    // workgroup order can follow the XCDs) unless the caller fixes the count
+    // one persistent workgroup per CU (a multiple of 8 so that the workgroup
+    // order can follow the XCDs) unless the caller fixes the count
     int32_t grid = a->split_target > 0 ? a->split_target : ((cus + 7) / 8) * 8;
     if (grid > mla::kMaxGrid) grid = mla::kMaxGrid;
     p.grid = grid;
   }
 
-  hipError_t err = a->kv_dtype == MLA_DTYPE_FP8_E4M3
-                       ? mla::launch_decode(p, true, (hipEvent_t)a->event_begin, (hipEvent_t)a->event_end,
-                                            (hipStream_t)stream)
-                       : mla::launch_decode_stream(p, (hipEvent_t)a->event_begin, (hipEvent_t)a->event_end,
-                                                   (hipStream_t)stream);
+  hipError_t err = mla::launch_decode_stream(p, (hipEvent_t)a->event_begin, (hipEvent_t)a->event_end,
+                                             (hipStream_t)stream);
   if (err != hipSuccess) return device_fail(err, "decode launch");
   return ok();
 }

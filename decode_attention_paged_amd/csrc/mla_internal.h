@@ -12,11 +12,6 @@ constexpr int kPage = 64;
 constexpr int kDqk = 576;       // latent 512 + rope 64
 constexpr int kDv = 512;        // V = first 512 latent dims
 constexpr int kTile = 32;       // KV tokens per attention tile
-constexpr int kWaves = 4;       // waves per attention workgroup
-constexpr int kRowsPerWave = 32;
-constexpr int kRowsPerBlock = kWaves * kRowsPerWave;   // 128 query rows
-constexpr int kMinChunk = 64;   // smallest KV chunk one workgroup takes
-constexpr int kSplitTargetMax = 512;
 constexpr int kMaxShards = 16;
 
 // Everything the plan / attention / combine kernels need for one shard.
@@ -37,13 +32,7 @@ struct DecodeParams {
   void* out;
   float* lse;
   // workspace
-  int32_t* plan;                  // [0] items, [1] chunk tokens
-  int2* req_info;                 // [B] (first item, number of items)
-  int2* items;                    // [max_items] (request, chunk index)
-  float* part_lse;                // [max_items][rows] base-2
-  float* part_o;                  // [max_items][rows][512], normalised, scaled
-  int32_t max_items;
-  int32_t split_target;
+  int32_t* plan;                  // [0] units, [1] workgroups in use
   // persistent schedule of the streaming kernel: the shard's work is the
   // sequence of units (request b, row block rb, 32-token tile), ordered by
   // segment s = b * row_blocks + rb and tile; workgroup g takes a contiguous
@@ -56,7 +45,8 @@ struct DecodeParams {
   int2* wg_start;                 // [grid] (segment, tile) of each workgroup's first unit
   uint16_t* spart_o;              // [slots][rows_blk][512] bf16, normalised, scaled
   float* spart_lse;               // [slots][rows_blk] base 2
-  int32_t rows_blk;               // query rows per workgroup (32, 64 or 128)
+  int32_t rows_blk;               // query rows per workgroup (32 or 64)
+  int32_t kv_fp8;                 // KV pages hold e4m3 (else bf16)
   int32_t grid;                   // persistent workgroups
 };
 
@@ -69,9 +59,8 @@ constexpr int kMaxGrid = 1024;  // persistent workgroups of the streaming kernel
 inline int32_t stream_rows_per_block(int32_t rows) { return rows <= 32 ? 32 : 64; }
 
 struct WorkspaceLayout {
-  size_t plan, req_info, items, part_lse, part_o, total;
-  size_t req_cnt, seg_off, seg_coff, seg_info, wg_start, wg_ustart, spart_lse, spart_o;
-  int32_t max_items, max_slots;
+  size_t plan, req_cnt, seg_off, seg_coff, seg_info, wg_start, wg_ustart, spart_lse, spart_o, total;
+  int32_t max_slots;
 };
 WorkspaceLayout decode_workspace_layout(int32_t batch, int32_t rows);
 
@@ -92,8 +81,6 @@ hipError_t launch_metadata(const int32_t* seq_lens, const int32_t* block_table, 
                            int32_t max_pages, int32_t shard, int32_t num_shards,
                            int32_t* local_seq_lens, int32_t* local_kv_indices,
                            int32_t stride, hipStream_t stream);
-hipError_t launch_decode(const DecodeParams& p, bool fp8, hipEvent_t ev_begin, hipEvent_t ev_end,
-                         hipStream_t stream);
 hipError_t launch_decode_stream(const DecodeParams& p, hipEvent_t ev_begin, hipEvent_t ev_end,
                                 hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);

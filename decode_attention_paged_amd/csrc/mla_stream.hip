@@ -36,8 +36,8 @@ namespace {
 
 constexpr int kStageBytes = kTile * kDqk * 2;      // 36864: one tile
 constexpr int kRopeBase = kTile * 1024;             // rope part of a stage (dims 512..575)
-constexpr int kRing = 8;                           // row-index ring, in tiles
-constexpr int kDmaPerWave = kStageBytes / 1024 / 4;  // 9 copies of 1 KB per wave per tile
+constexpr int kStageBytes8 = kTile * kDqk;          // 18432: one fp8 tile as stored
+constexpr int kRing = 16;                          // row-index ring, in tiles
 // A row's exponent reference moves up (rescaling its accumulator) only when a
 // tile's max exceeds it by more than this (log2 units), so rescaling is rare
 // and unnormalised probabilities stay below 2^kRescaleSlack.
@@ -306,19 +306,68 @@ __device__ __forceinline__ void issue_tile(const DecodeParams& p, const Cursor& 
 
 // Wait until at most `after` vector-memory operations of this wave are
 // outstanding, i.e. everything issued before the last `after` ones landed.
-// `after` is wave-uniform; the ladder rounds it down to an encodable
-// immediate (waiting longer is always safe).
-__device__ __forceinline__ void wait_vm_after(int after) {
-  constexpr int P = kDmaPerWave;
-  if (after >= 2 * P + 2) wait_vmcnt<2 * P + 2>();
-  else if (after >= 2 * P + 1) wait_vmcnt<2 * P + 1>();
-  else if (after >= 2 * P) wait_vmcnt<2 * P>();
-  else if (after >= P + 2) wait_vmcnt<P + 2>();
-  else if (after >= P + 1) wait_vmcnt<P + 1>();
-  else if (after >= P) wait_vmcnt<P>();
-  else if (after >= 2) wait_vmcnt<2>();
-  else if (after >= 1) wait_vmcnt<1>();
-  else wait_vmcnt<0>();
+// `after` is wave-uniform; the ladder takes the largest immediate <= after
+// (kMax bounds it; waiting longer is always safe).
+template <int kMax>
+__device__ __forceinline__ void wait_vm_le(int after) {
+  if constexpr (kMax == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (after >= kMax) wait_vmcnt<kMax>();
+    else wait_vm_le<kMax - 1>(after);
+  }
+}
+
+// fp8 tiles: staged as stored (token t at byte 576 t). Wave w moves the 4608
+// bytes of tokens 8w .. 8w + 7; copy i covers bytes 1024 i .. + 1023 of them,
+// lane l the 16-byte chunk (64 i + l) % 36 of token (64 i + l) / 36, and the
+// fifth copy is a half one (32 lanes). rowc: row of token 8w + (lane & 7).
+__device__ __forceinline__ int tile_rows8(const DecodeParams& p, const Cursor& c, const int32_t* ring_slot) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tk = 8 * wave + (lane & 7);
+  const int row = resolve_row(p, c.tile, c.cnt, tk, ring_slot[tk]);
+  return row >= 0 ? row : 0;
+}
+template <int kI0, int kI1>
+__device__ __forceinline__ void copy8(const DecodeParams& p, int rowc, uint32_t stage_lds) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int i = kI0; i < kI1; ++i) {
+    const int g = 64 * i + lane;
+    const int tl = g / 36, ch = g - 36 * tl;
+    const int row = __shfl(rowc, tl);
+    const uint8_t* src = p.kv + (long long)row * kDqk + 16 * ch;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(stage_lds + 4608 * wave + 1024 * i);
+    if (i < 4 || lane < 32) lds_dma16(src, dst);
+  }
+}
+__device__ __forceinline__ void issue_tile8(const DecodeParams& p, const Cursor& c, uint32_t stage_lds,
+                                            const int32_t* ring_slot) {
+  const int rowc = tile_rows8(p, c, ring_slot);
+  copy8<0, 5>(p, rowc, stage_lds);
+}
+
+// fp8 staging -> bf16 stage in the layout of the bf16 tiles (exact: every
+// e4m3 value is a bf16 value; the per-tensor scale is applied to the scores
+// and the output instead). Thread k converts the 8-dim chunks k + 256 j.
+__device__ __forceinline__ void convert_tile8(const uint8_t* stg, uint8_t* dst) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int j = 0; j < kTile * (kDqk / 8) / 256; ++j) {
+    const int unit = threadIdx.x + 256 * j;
+    const int tkn = unit / (kDqk / 8), c = unit - (kDqk / 8) * tkn;
+    const u32x2_t x = *(const u32x2_t*)(stg + kDqk * tkn + 8 * c);
+    const bf16x2_t y0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, false);
+    const bf16x2_t y1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, true);
+    const bf16x2_t y2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, false);
+    const bf16x2_t y3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, true);
+    const bf16x8_t y = {y0[0], y0[1], y1[0], y1[1], y2[0], y2[1], y3[0], y3[1]};
+    const uint32_t a = c < 64 ? (uint32_t)(1024 * tkn + 16 * (c ^ chunk_swz(tkn)))
+                              : (uint32_t)(kRopeBase + 128 * tkn + 16 * ((c - 64) ^ chunk_swz(tkn)));
+    *(bf16x8_t*)(dst + a) = y;
+  }
 }
 
 // QK A operand of this wave's i-th k-step (see the kernel for the layout).
@@ -368,13 +417,19 @@ __device__ __forceinline__ float acc_read(float x) {
   return r;
 }
 
-template <int kDS>
+template <int kDS, bool kFp8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_stream_kernel(DecodeParams p) {
   constexpr int kRG = 4 / kDS;                 // row groups of 32 rows
   constexpr int kRowsBlk = 32 * kRG;
   constexpr int kDb = (kDv / 32) / kDS;        // 32-dim blocks of this wave's V slice
-  constexpr int kNS = 3;                       // stages
+  // stages: copies in flight while one tile is computed, about the same bytes
+  // for both KV types (fp8 tiles are staged as stored and converted to one
+  // bf16 compute stage per tile)
+  constexpr int kNS = kFp8 ? 5 : 3;
+  constexpr int kStg = kFp8 ? kStageBytes8 : kStageBytes;   // bytes of a staged tile
+  constexpr int kCopies = kFp8 ? 5 : 9;                     // copies per wave per tile
+  constexpr int kWaitMax = (kNS - 2) * (kCopies + 1);       // ops after a tile's copies
   constexpr int kAheadRows = 2 * kNS - 2;      // tiles whose row indices are fetched ahead
   // QK: the kDS waves of a row group split the 36 k-steps; wave ds takes the
   // k-steps kk with kk mod 4 in [kG ds, kG ds + kG) and sums the partial
@@ -390,7 +445,7 @@ void attn_stream_kernel(DecodeParams p) {
   constexpr int kAhead = 4;
   static_assert(kAheadRows < kRing, "row ring too small");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * kStg + (kFp8 ? kStageBytes : 0)];
   __shared__ __attribute__((aligned(16))) int32_t ring[kRing * kTile];
   __shared__ __attribute__((aligned(16))) uint8_t qlds[kQInLds > 0 ? 4 * kQInLds * 64 * 16 : 16];
   __shared__ __attribute__((aligned(16))) f32x4_t xbuf[kDS > 1 ? 4 * 4 * 64 : 1];   // [wave][4][lane]
@@ -487,8 +542,9 @@ void attn_stream_kernel(DecodeParams p) {
       for (int k = 0; k < kNS - 1; ++k) {
         if (k < Uw) {
           if (k > 0) ci.advance(p);
-          issue_tile(p, ci, smem_lds + kStageBytes * k, ring + kTile * k);
-          ops += kDmaPerWave;
+          if constexpr (kFp8) issue_tile8(p, ci, smem_lds + kStg * k, ring + kTile * k);
+          else issue_tile(p, ci, smem_lds + kStg * k, ring + kTile * k);
+          ops += kCopies;
           pos[k] = ops;
         }
       }
@@ -525,14 +581,19 @@ void attn_stream_kernel(DecodeParams p) {
     for (int k = 0; k < n; ++k, ++t) {
       // tile t has landed for this wave, then for all waves; the stage of
       // tile t - 1 is free
-      wait_vm_after(ops - pos[0]);
+      wait_vm_le<kWaitMax>(ops - pos[0]);
       __syncthreads();
 #pragma unroll
       for (int i = 0; i + 1 < kNS - 1; ++i) pos[i] = pos[i + 1];
       // table entry of this tile's token `tok`
       const int raw_c = ring[kTile * (t % kRing) + tok];
 
-      const uint8_t* ks = smem + kStageBytes * stage;
+      if constexpr (kFp8) {
+        // the compute stage was last read by tile t - 1 (done at the barrier)
+        convert_tile8(smem + kStg * stage, smem + kNS * kStg);
+        __syncthreads();
+      }
+      const uint8_t* ks = kFp8 ? smem + kNS * kStg : smem + kStageBytes * stage;
       const int tile = tile0 + k;
       const int jt = tile * kTile;
       // tokens whose page is outside the pool poison their scores
@@ -573,14 +634,20 @@ void attn_stream_kernel(DecodeParams p) {
       // copies of tile t + kNS - 1, in three parts over the iteration so that
       // their issue does not stall on a full memory queue
       const bool more = t + kNS - 1 < Uw;
-      const uint32_t st_next = smem_lds + kStageBytes * (stage == 0 ? kNS - 1 : stage - 1);   // tile t - 1's
+      const uint32_t st_next = smem_lds + kStg * (stage == 0 ? kNS - 1 : stage - 1);   // tile t - 1's
       int rows_next = 0;
       if (more) {
         ci.advance(p);
-        rows_next = tile_rows(p, ci, ring + kTile * ((t + kNS - 1) % kRing));
-        copy_rope(p, rows_next, st_next);
-        copy_main<0, 3>(p, rows_next, st_next);
-        ops += 4;
+        if constexpr (kFp8) {
+          rows_next = tile_rows8(p, ci, ring + kTile * ((t + kNS - 1) % kRing));
+          copy8<0, 2>(p, rows_next, st_next);
+          ops += 2;
+        } else {
+          rows_next = tile_rows(p, ci, ring + kTile * ((t + kNS - 1) % kRing));
+          copy_rope(p, rows_next, st_next);
+          copy_main<0, 3>(p, rows_next, st_next);
+          ops += 4;
+        }
       }
       if constexpr (kDS > 1) {
         __syncthreads();
@@ -646,8 +713,13 @@ void attn_stream_kernel(DecodeParams p) {
       }
 
       if (more) {
-        copy_main<3, 6>(p, rows_next, st_next);
-        ops += 3;
+        if constexpr (kFp8) {
+          copy8<2, 4>(p, rows_next, st_next);
+          ops += 2;
+        } else {
+          copy_main<3, 6>(p, rows_next, st_next);
+          ops += 3;
+        }
       }
 
       // O[row][dim] += P[row][token] V[token][dim] over this wave's dims: the
@@ -671,8 +743,13 @@ void attn_stream_kernel(DecodeParams p) {
         if (st + kAhead < kPvSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
       }
       if (more) {
-        copy_main<6, 8>(p, rows_next, st_next);
-        ops += 2;
+        if constexpr (kFp8) {
+          copy8<4, 5>(p, rows_next, st_next);
+          ops += 1;
+        } else {
+          copy_main<6, 8>(p, rows_next, st_next);
+          ops += 2;
+        }
         pos[kNS - 2] = ops;
       }
       stage = stage + 1 == kNS ? 0 : stage + 1;
@@ -795,8 +872,11 @@ hipError_t launch_decode_stream(const DecodeParams& p, hipEvent_t ev_begin, hipE
   // the events, when given, take the attention kernel's own start and end
   // times (recorded with the dispatch, no separate marker packets)
   void* args[] = {const_cast<DecodeParams*>(&p)};
-  const void* fn = p.rows_blk == 32 ? reinterpret_cast<const void*>(&attn_stream_kernel<4>)
-                                    : reinterpret_cast<const void*>(&attn_stream_kernel<2>);
+  const void* fn;
+  if (p.kv_fp8) fn = p.rows_blk == 32 ? reinterpret_cast<const void*>(&attn_stream_kernel<4, true>)
+                                      : reinterpret_cast<const void*>(&attn_stream_kernel<2, true>);
+  else fn = p.rows_blk == 32 ? reinterpret_cast<const void*>(&attn_stream_kernel<4, false>)
+                             : reinterpret_cast<const void*>(&attn_stream_kernel<2, false>);
   err = hipExtLaunchKernel(fn, dim3(p.grid), dim3(256), args, 0, stream, ev_begin, ev_end, 0);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(stream_combine_kernel, dim3(p.batch, (p.rows + 3) / 4), dim3(256), 0, stream, p);

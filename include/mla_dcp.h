@@ -146,11 +146,11 @@ typedef struct mla_decode_args {
   /* scratch (device), size from mla_decode_workspace_bytes */
   void* workspace;
   size_t workspace_bytes;
-  /* tuning: number of KV chunks to split a launch into per row block
-   * (0 = derived from the device's compute-unit count) */
+  /* tuning: number of persistent workgroups the shard's work is spread
+   * over, 1 .. 1024 (0 = one per compute unit) */
   int32_t split_target;
-  /* optional hipEvent_t pair recorded around the main attention kernel
-   * (NULL = none); for timing that kernel alone */
+  /* optional hipEvent_t pair (created with timing) that receive the start
+   * and end times of the attention kernel's dispatch (NULL = none) */
   void* event_begin;
   void* event_end;
 } mla_decode_args_t;
@@ -162,8 +162,9 @@ size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t q_le
 /* Errors: INVALID_ARGUMENT for a null q / kv_pages / block_table / seq_lens /
  * out / lse / workspace, only one of the two metadata pointers, batch < 0,
  * num_heads not a positive multiple of 16, q_len outside [1, 4],
- * page_size != 64, bad shard ids, num_pages < 1, max_pages < 1, a dtype
- * other than those listed; WORKSPACE_TOO_SMALL; DEVICE_ERROR if a launch
+ * page_size != 64, bad shard ids, num_pages < 1, max_pages < 1,
+ * split_target outside [0, 1024], a dtype other than those listed;
+ * WORKSPACE_TOO_SMALL; DEVICE_ERROR if a launch
  * fails. `lse_base_written` (host, may be NULL) receives the base of `lse`,
  * which is always the requested one. */
 mla_status_t mla_decode_partial(const mla_decode_args_t* args, mla_lse_base_t* lse_base_written,
