@@ -42,9 +42,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-FP8_PEAK_TFLOPS = 5000.0
 METRIC = "MLA split-KV decode KV-GB/s + TFLOP/s vs roofline; merge μs (64 heads, D=512)"
-KERNEL_SRC = os.path.join(ROOT, "decode_attention_paged_amd", "csrc", "mla_decode.hip")
+KERNEL_SRC_DIR = os.path.join(ROOT, "decode_attention_paged_amd", "csrc")
 
 
 def log(msg: str) -> None:
@@ -113,8 +112,8 @@ def workload_work(wl):
 
 def kernel_sha() -> str:
     h = hashlib.sha256()
-    for name in sorted(os.listdir(os.path.dirname(KERNEL_SRC))):
-        with open(os.path.join(os.path.dirname(KERNEL_SRC), name), "rb") as f:
+    for name in sorted(os.listdir(KERNEL_SRC_DIR)):
+        with open(os.path.join(KERNEL_SRC_DIR, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
@@ -212,7 +211,9 @@ def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True, spl
         merge_us=1e3 * statistics.median(merge_ms), steps=steps, warmup=warmup, rotated=len(dws),
         metadata_us_per_shard=metadata_us,
     )
-    peak_tf = FP8_PEAK_TFLOPS if wl.kv_dtype == "fp8" else BF16_PEAK_TFLOPS
+    # the contraction runs on bf16 MFMAs for both KV types (fp8 pages are
+    # converted to bf16 in LDS), so its peak is the bf16 one
+    peak_tf = BF16_PEAK_TFLOPS
     res["attn_kernel_hbm_frac"] = achieved_gbs / HBM_PEAK_GBS
     res["attn_kernel_mfma_frac"] = achieved_tflops / peak_tf
     del dws, bufs
@@ -363,19 +364,20 @@ def main() -> int:
                 f"{100 * r['attn_kernel_mfma_frac']:.1f}% MFMA)")
 
     cpu = None if args.no_cpu else cpu_baseline(wl, args.cpu_seconds)
-    mfma_bound = res["attn_kernel_mfma_frac"] > res["attn_kernel_hbm_frac"] and wl.q_len > 1
+    mfma_bound = res["attn_kernel_mfma_frac"] > res["attn_kernel_hbm_frac"]
     if mfma_bound:
-        peak = FP8_PEAK_TFLOPS if wl.kv_dtype == "fp8" else BF16_PEAK_TFLOPS
+        peak = BF16_PEAK_TFLOPS
         roof = dict(bound="mfma", achieved=res["attn_kernel_tflops"], peak=peak, unit="TFLOP/s",
                     frac=res["attn_kernel_tflops"] / peak)
     else:
         roof = dict(bound="hbm", achieved=res["attn_kernel_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=res["attn_kernel_gbs"] / HBM_PEAK_GBS)
     roof["traffic"] = traffic_from_profile(wl.name)
+    ds = 4 if wl.heads * wl.q_len <= 32 else 2
     if wl.kv_dtype == "fp8":
-        kname = "attn_kernel<true> (mla_decode.hip)"
+        kname = "attn_stream_kernel<%d, fp8> (mla_stream.hip)" % ds
     else:
-        kname = "attn_stream_kernel<%d> (mla_stream.hip)" % (4 if wl.heads * wl.q_len <= 32 else 2)
+        kname = "attn_pipe_kernel<%d, local indices> (mla_stream.hip)" % ds
     roof["kernel"] = kname + ", mean of %d launches" % (args.steps * wl.shards)
     roof["mean_launch_us"] = res["attn_kernel_mean_us"]
     roof["algorithmic_bytes_per_launch"] = res["attn_kernel_bytes_per_launch"]

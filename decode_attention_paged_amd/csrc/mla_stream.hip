@@ -1,4 +1,4 @@
-// Rank-local paged MLA decode over bf16 KV: persistent streaming kernel.
+// Rank-local paged MLA decode: persistent streaming kernels.
 //
 // One shard r of S owns the tokens t = j S + r of every request (prhub.com.cn
 // digest of sgl-project/sglang PR 33926, sections 功能与动机 and 实现拆解
@@ -9,27 +9,35 @@
 // Schedule. The shard's work is a sequence of units (request b, block of
 // query rows rb, 32-token tile), ordered by segment s = b * row_blocks + rb
 // and tile. stream_plan_kernel lays the segments out on device (no host
-// synchronisation) and one workgroup per CU takes an equal contiguous share
-// of the units. A segment that a workgroup holds entirely is finalised in
-// place; a segment cut at workgroup boundaries leaves one bf16 partial per
-// piece, combined by stream_combine_kernel.
+// synchronisation) and one workgroup per CU takes a contiguous share of the
+// units of about equal cost. A segment that a workgroup holds entirely is
+// finalised in place; a segment cut at workgroup boundaries leaves one bf16
+// partial per piece, combined by stream_combine_kernel.
 //
 // Workgroup. Four waves: rows_blk / 32 row groups of 32 query rows times
-// 4 / (rows_blk / 32) slices of the 512 V dims. Every wave computes the
-// scores of its 32 rows (S^T = K Q^T, v_mfma_f32_32x32x16_bf16) and the
-// output of its dims slice (O^T += V^T P^T).
+// 4 / (rows_blk / 32) slices of the 512 V dims. The waves of a row group
+// split the 576 QK dims and exchange their partial scores through LDS
+// (S^T = K Q^T, v_mfma_f32_32x32x16_bf16); each wave then accumulates the
+// output of its dims slice.
 //
-// Pipeline. Tiles move HBM -> LDS with global_load_lds_dwordx4 (no register
-// staging) through four 36 KB stages, so three tiles are in flight while one
-// is computed. The row indices of a tile move into an LDS ring the same way,
-// 2 * 4 - 2 tiles ahead, so every vector-memory operation inside the tile
-// loop is one of these asynchronous copies and the loop waits on exactly the
+// bf16 KV (attn_pipe_kernel). Tiles move HBM -> LDS with
+// global_load_lds_dwordx4 (no register staging) through four 36 KB stages;
+// the row of every token comes from the block table by scalar loads, and
+// out-of-pool pages point the copy at a constant NaN row. The loop overlaps
+// two tiles: the scores of tile k + 1 run with tile k's softmax on the VALU
+// and then with tile k's accumulation (O^T += V^T P^T) on the MFMAs.
+//
+// fp8 KV (attn_stream_kernel<.., true>). Tiles are staged as stored (five
+// 18 KB stages), converted to a bf16 compute stage, and the row indices move
+// into an LDS ring 2 * 5 - 2 tiles ahead; every vector-memory operation in
+// the tile loop is an asynchronous copy and the loop waits on exactly the
 // tile it needs (s_waitcnt vmcnt(n) with n counted by the wave).
 #include "mla_device.h"
 
 #include <hip/hip_ext.h>
 
 #include <limits.h>
+#include <type_traits>
 
 namespace mla {
 namespace {
@@ -417,6 +425,41 @@ __device__ __forceinline__ float acc_read(float x) {
   return r;
 }
 
+// Copy j of kCopies for a tile is issued after MFMA slot
+// floor(j * slots / kCopies) of the tile loop (slots: the QK MFMAs, then the
+// PV MFMAs); -1 for slots that issue none.
+__host__ __device__ constexpr int copy_at_slot(int slot, int slots, int copies) {
+  for (int j = 0; j < copies; ++j)
+    if (j * slots / copies == slot) return j;
+  return -1;
+}
+// Copy j of a tile: bf16 tiles move the rope tails (j = 0) and the 1 KB main
+// part of token 8 w + j - 1 (j >= 1); fp8 tiles move 1 KB slice j.
+template <bool kFp8>
+__device__ __forceinline__ void issue_copy(const DecodeParams& p, int j, int rows, uint32_t stage_lds) {
+  if constexpr (kFp8) {
+    switch (j) {
+      case 0: copy8<0, 1>(p, rows, stage_lds); break;
+      case 1: copy8<1, 2>(p, rows, stage_lds); break;
+      case 2: copy8<2, 3>(p, rows, stage_lds); break;
+      case 3: copy8<3, 4>(p, rows, stage_lds); break;
+      default: copy8<4, 5>(p, rows, stage_lds); break;
+    }
+  } else {
+    switch (j) {
+      case 0: copy_rope(p, rows, stage_lds); break;
+      case 1: copy_main<0, 1>(p, rows, stage_lds); break;
+      case 2: copy_main<1, 2>(p, rows, stage_lds); break;
+      case 3: copy_main<2, 3>(p, rows, stage_lds); break;
+      case 4: copy_main<3, 4>(p, rows, stage_lds); break;
+      case 5: copy_main<4, 5>(p, rows, stage_lds); break;
+      case 6: copy_main<5, 6>(p, rows, stage_lds); break;
+      case 7: copy_main<6, 7>(p, rows, stage_lds); break;
+      default: copy_main<7, 8>(p, rows, stage_lds); break;
+    }
+  }
+}
+
 template <int kDS, bool kFp8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_stream_kernel(DecodeParams p) {
@@ -585,8 +628,25 @@ void attn_stream_kernel(DecodeParams p) {
       __syncthreads();
 #pragma unroll
       for (int i = 0; i + 1 < kNS - 1; ++i) pos[i] = pos[i + 1];
-      // table entry of this tile's token `tok`
+      // row indices kAheadRows tiles ahead: issued before this iteration's
+      // tile copies, so that waiting for those copies covers them too
+      if (t + kAheadRows < Uw) {
+        cf.advance(p);
+        fetch_rows(p, cf, ring_lds + 4 * kTile * ((t + kAheadRows) % kRing));
+        ops += 1;
+      }
+      // table entry of this tile's token `tok`, and the rows of tile
+      // t + kNS - 1, whose copies go into the stage of tile t - 1 spread over
+      // the MFMA sequences below (a burst would stall on the memory queue)
       const int raw_c = ring[kTile * (t % kRing) + tok];
+      const bool more = t + kNS - 1 < Uw;
+      const uint32_t st_next = smem_lds + kStg * (stage == 0 ? kNS - 1 : stage - 1);   // tile t - 1's
+      int rows_next = 0;
+      if (more) {
+        ci.advance(p);
+        const int32_t* rs = ring + kTile * ((t + kNS - 1) % kRing);
+        rows_next = kFp8 ? tile_rows8(p, ci, rs) : tile_rows(p, ci, rs);
+      }
 
       if constexpr (kFp8) {
         // the compute stage was last read by tile t - 1 (done at the barrier)
@@ -600,7 +660,7 @@ void attn_stream_kernel(DecodeParams p) {
       const int rr = resolve_row(p, tile, cnt, tok, raw_c);
       const uint64_t bad = __ballot(lane < kTile && rr == kRowBad);
 
-      // S^T[token][row] over this wave's k-steps; K operands are read two
+      // S^T[token][row] over this wave's k-steps; K operands are read kAhead
       // steps ahead of their MFMA
       bf16x8_t ka[kAhead];
 #pragma unroll
@@ -616,40 +676,31 @@ void attn_stream_kernel(DecodeParams p) {
         const bf16x8_t qb = i < kQRegSteps ? qreg[i < kQRegSteps ? i : 0]
                                            : *(const bf16x8_t*)(qmine + 16 * 64 * (i - kQRegSteps));
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb, s, 0, 0, 0);
+        constexpr int kSlots = kKS + kPvSteps;
+        if (copy_at_slot(i, kSlots, kCopies) >= 0 && more) {
+          issue_copy<kFp8>(p, copy_at_slot(i, kSlots, kCopies), rows_next, st_next);
+          ops += 1;
+        }
       }
-      if constexpr (kDS > 1) {
+      if constexpr (kDS == 2) {
+        // the partner wave's partial scores; both waves form s0 + s1
+        // (addition commutes exactly), so they agree bit for bit
+        f32x4_t* mine = xbuf + (wave * 4) * 64 + lane;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) mine[64 * q] = f32x4_t{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
+        __syncthreads();
+        const f32x4_t* src = xbuf + (((1 - ds) * kRG + rg) * 4) * 64 + lane;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4_t v = src[64 * q];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[4 * q + e] += v[e];
+        }
+      } else if constexpr (kDS > 2) {
         // sum the row group's partial scores in wave order
         f32x4_t* mine = xbuf + (wave * 4) * 64 + lane;
 #pragma unroll
         for (int q = 0; q < 4; ++q) mine[64 * q] = f32x4_t{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
-      }
-      // the next copies (into the stage of tile t - 1, free since the loop
-      // top) are issued here, where the wave would otherwise wait for the
-      // other waves' partial scores: a stalled issue costs nothing then
-      if (t + kAheadRows < Uw) {
-        cf.advance(p);
-        fetch_rows(p, cf, ring_lds + 4 * kTile * ((t + kAheadRows) % kRing));
-        ops += 1;
-      }
-      // copies of tile t + kNS - 1, in three parts over the iteration so that
-      // their issue does not stall on a full memory queue
-      const bool more = t + kNS - 1 < Uw;
-      const uint32_t st_next = smem_lds + kStg * (stage == 0 ? kNS - 1 : stage - 1);   // tile t - 1's
-      int rows_next = 0;
-      if (more) {
-        ci.advance(p);
-        if constexpr (kFp8) {
-          rows_next = tile_rows8(p, ci, ring + kTile * ((t + kNS - 1) % kRing));
-          copy8<0, 2>(p, rows_next, st_next);
-          ops += 2;
-        } else {
-          rows_next = tile_rows(p, ci, ring + kTile * ((t + kNS - 1) % kRing));
-          copy_rope(p, rows_next, st_next);
-          copy_main<0, 3>(p, rows_next, st_next);
-          ops += 4;
-        }
-      }
-      if constexpr (kDS > 1) {
         __syncthreads();
         f32x16_t tot = f32x16_t{};
 #pragma unroll
@@ -666,14 +717,13 @@ void attn_stream_kernel(DecodeParams p) {
       }
 
       // online softmax in base 2 (this lane: one row, 16 tokens: value v is
-      // token 8 (v >> 2) + 4 hi + (v & 3))
+      // token 8 (v >> 2) + 4 hi + (v & 3)); the max is taken on the raw
+      // scores (scaling by a positive factor commutes with it exactly) and
+      // the scale is folded into the exponent's FMA
       float tmax = kNegInf;
       if (jt + kTile <= jvis_min && bad == 0) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          s[v] *= p.scale_log2;
-          tmax = fmaxf(tmax, s[v]);
-        }
+        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[v]);
       } else {
         // masks shifted by 4 hi once so each test is against a constant
         const int lim = jvis - jt - 4 * hi;
@@ -681,13 +731,13 @@ void attn_stream_kernel(DecodeParams p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int c = 8 * (v >> 2) + (v & 3);
-          float x = c < lim ? s[v] * p.scale_log2 : kNegInf;
+          float x = c < lim ? s[v] : kNegInf;
           x = ((badl >> c) & 1u) ? __builtin_nanf("") : x;
           s[v] = x;
           tmax = fmaxf(tmax, x);
         }
       }
-      tmax = xor32_max(tmax);
+      tmax = xor32_max(tmax) * p.scale_log2;
       const bool grow = m_ref != kNegInf && tmax > m_ref + kRescaleSlack;
       if (__builtin_expect(__ballot(grow) != 0, 0)) {
         const float f = grow ? exp2_fast(m_ref - tmax) : 1.f;
@@ -703,23 +753,13 @@ void attn_stream_kernel(DecodeParams p) {
         m_ref = grow ? tmax : m_ref;
       }
       m_ref = m_ref == kNegInf ? tmax : m_ref;
-      const float m_use = m_ref == kNegInf ? 0.f : m_ref;
+      const float neg_m = m_ref == kNegInf ? 0.f : -m_ref;
       bf16x8_t pb[2];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float pv = exp2_fast(s[v] - m_use);
+        const float pv = exp2_fast(__builtin_fmaf(s[v], p.scale_log2, neg_m));
         l_sum += pv;
         pb[v >> 3][v & 7] = (__bf16)pv;
-      }
-
-      if (more) {
-        if constexpr (kFp8) {
-          copy8<2, 4>(p, rows_next, st_next);
-          ops += 2;
-        } else {
-          copy_main<3, 6>(p, rows_next, st_next);
-          ops += 3;
-        }
       }
 
       // O[row][dim] += P[row][token] V[token][dim] over this wave's dims: the
@@ -735,23 +775,13 @@ void attn_stream_kernel(DecodeParams p) {
         const bf16x8_t a = va[st % kAhead];
         if (st + kAhead < kPvSteps) va[st % kAhead] = pv_operand(ks, pv0, st + kAhead);
         o[st >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb[st & 1], a, o[st >> 1], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 1);
-#pragma unroll
-      for (int st = 0; st < kPvSteps; ++st) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        if (st + kAhead < kPvSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-      }
-      if (more) {
-        if constexpr (kFp8) {
-          copy8<4, 5>(p, rows_next, st_next);
+        constexpr int kSlots = kKS + kPvSteps;
+        if (copy_at_slot(kKS + st, kSlots, kCopies) >= 0 && more) {
+          issue_copy<kFp8>(p, copy_at_slot(kKS + st, kSlots, kCopies), rows_next, st_next);
           ops += 1;
-        } else {
-          copy_main<6, 8>(p, rows_next, st_next);
-          ops += 2;
         }
-        pos[kNS - 2] = ops;
       }
+      if (more) pos[kNS - 2] = ops;
       stage = stage + 1 == kNS ? 0 : stage + 1;
     }
 
@@ -802,6 +832,557 @@ void attn_stream_kernel(DecodeParams p) {
       cc.advance(p);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// software-pipelined attention over bf16 KV
+// ---------------------------------------------------------------------------
+// Rows that tokens read instead of the pool: zeros for tokens past a
+// request's owned range (finite, and masked by the visibility limit) and NaN
+// for a page id or row outside the pool (poisons the request's result rather
+// than reading out of bounds).
+struct ConstRows {
+  uint32_t zero[kDqk / 2];       // 1152 bytes
+  uint32_t nan_bf16[kDqk / 2];   // bf16 NaN 0x7FC0
+  constexpr ConstRows() : zero(), nan_bf16() {
+    for (int i = 0; i < kDqk / 2; ++i) nan_bf16[i] = 0x7FC07FC0u;
+  }
+};
+__device__ __attribute__((aligned(256))) const ConstRows g_const_rows;
+
+// Table entries for the eight tokens 8 w .. 8 w + 7 a wave copies of a tile,
+// read with scalar loads: the pages they fall in (block table; at most three
+// for up to 16 shards) or their rows (local indices). Indices are clamped to
+// the table row; entries of tokens past the owned range are never used.
+struct TileEntries {
+  int p0;
+  int e0, e1, e2, e3, e4, e5, e6, e7;
+};
+template <bool kLocal>
+__device__ __forceinline__ void load_entries(const DecodeParams& p, const Cursor& c, int wave, TileEntries& te) {
+  const int j0 = c.tile * kTile + 8 * wave;
+  if constexpr (kLocal) {
+    const int32_t* base = p.local_kv_indices + (long long)c.b * p.local_kv_stride;
+    const int last = p.local_kv_stride - 1;
+    te.e0 = ld_const(base + min(j0 + 0, last));
+    te.e1 = ld_const(base + min(j0 + 1, last));
+    te.e2 = ld_const(base + min(j0 + 2, last));
+    te.e3 = ld_const(base + min(j0 + 3, last));
+    te.e4 = ld_const(base + min(j0 + 4, last));
+    te.e5 = ld_const(base + min(j0 + 5, last));
+    te.e6 = ld_const(base + min(j0 + 6, last));
+    te.e7 = ld_const(base + min(j0 + 7, last));
+    te.p0 = 0;
+  } else {
+    te.p0 = (j0 * p.num_shards + p.shard) >> 6;
+    const int32_t* base = p.block_table + (long long)c.b * p.max_pages;
+    const int last = p.max_pages - 1;
+    te.e0 = ld_const(base + min(te.p0 + 0, last));
+    te.e1 = ld_const(base + min(te.p0 + 1, last));
+    te.e2 = ld_const(base + min(te.p0 + 2, last));
+    te.e3 = te.e4 = te.e5 = te.e6 = te.e7 = 0;
+  }
+}
+
+// Source row of token 8 w + (lane >> 3) of the cursor's tile (valid: the
+// tile exists in this workgroup's range).
+template <bool kLocal>
+__device__ __forceinline__ const uint8_t* token_src(const DecodeParams& p, const Cursor& c, bool valid,
+                                                    const TileEntries& te) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tk = lane >> 3;
+  const int j = c.tile * kTile + 8 * wave + tk;
+  const uint8_t* zero = reinterpret_cast<const uint8_t*>(g_const_rows.zero);
+  const uint8_t* nan = reinterpret_cast<const uint8_t*>(g_const_rows.nan_bf16);
+  if (!valid || j >= c.cnt) return zero;
+  if constexpr (kLocal) {
+    // e = entry tk, as a sum of differences (a select chain here is turned
+    // into an indexed load from a stack copy)
+    unsigned e = (unsigned)te.e0;
+    e += tk >= 1 ? (unsigned)te.e1 - (unsigned)te.e0 : 0u;
+    e += tk >= 2 ? (unsigned)te.e2 - (unsigned)te.e1 : 0u;
+    e += tk >= 3 ? (unsigned)te.e3 - (unsigned)te.e2 : 0u;
+    e += tk >= 4 ? (unsigned)te.e4 - (unsigned)te.e3 : 0u;
+    e += tk >= 5 ? (unsigned)te.e5 - (unsigned)te.e4 : 0u;
+    e += tk >= 6 ? (unsigned)te.e6 - (unsigned)te.e5 : 0u;
+    e += tk >= 7 ? (unsigned)te.e7 - (unsigned)te.e6 : 0u;
+    const int ei = (int)e;
+    const bool ok = ei >= 0 && (long long)ei < (long long)p.num_pages * kPage;
+    return ok ? p.kv + (long long)ei * (2 * kDqk) : nan;
+  } else {
+    const int t = j * p.num_shards + p.shard;
+    const int d = (t >> 6) - te.p0;
+    unsigned eu = (unsigned)te.e0;
+    eu += d >= 1 ? (unsigned)te.e1 - (unsigned)te.e0 : 0u;
+    eu += d >= 2 ? (unsigned)te.e2 - (unsigned)te.e1 : 0u;
+    const int e = (int)eu;
+    const bool ok = e >= 0 && e < p.num_pages;
+    return ok ? p.kv + ((long long)e * kPage + (t & 63)) * (2 * kDqk) : nan;
+  }
+}
+
+// Copy j of a bf16 tile into a stage (layout as for the streaming kernel):
+// j = 0 moves the eight rope tails of the wave's tokens, j = 1 + i the 1 KB
+// main part of token 8 w + i (one row per copy, as a scalar base).
+template <int kJ>
+__device__ __forceinline__ void copy_tile_part(const uint8_t* src, uint32_t stage_lds) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if constexpr (kJ == 0) {
+    lds_dma16(src + 16 * (64 + ((lane & 7) ^ chunk_swz(lane >> 3))),
+              __builtin_amdgcn_readfirstlane(stage_lds + kRopeBase + 1024 * wave));
+  } else {
+    constexpr int i = kJ - 1;
+    const uint64_t a = reinterpret_cast<uint64_t>(src);
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)a, 8 * i);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(a >> 32), 8 * i);
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
+    lds_dma16_sbase(base, (uint32_t)(16 * (lane ^ chunk_swz(i))),
+                    __builtin_amdgcn_readfirstlane(stage_lds + 1024 * (8 * wave + i)));
+  }
+}
+__device__ __forceinline__ void copy_tile_part_rt(int j, const uint8_t* src, uint32_t stage_lds) {
+  switch (j) {
+    case 0: copy_tile_part<0>(src, stage_lds); break;
+    case 1: copy_tile_part<1>(src, stage_lds); break;
+    case 2: copy_tile_part<2>(src, stage_lds); break;
+    case 3: copy_tile_part<3>(src, stage_lds); break;
+    case 4: copy_tile_part<4>(src, stage_lds); break;
+    case 5: copy_tile_part<5>(src, stage_lds); break;
+    case 6: copy_tile_part<6>(src, stage_lds); break;
+    case 7: copy_tile_part<7>(src, stage_lds); break;
+    default: copy_tile_part<8>(src, stage_lds); break;
+  }
+}
+
+// The tile loop overlaps two tiles: while the VALU computes tile k's softmax,
+// the MFMAs accumulate tile k - 1's P V. Four stages hold tile k - 1 (V),
+// tile k (K) and two tiles in flight. Every tile barrier issues exactly the
+// nine copies of the tile two ahead (from the zero row past the workgroup's
+// last unit), so the wait before it is a constant vmcnt(9): the only
+// vector-memory operations between two tile barriers are those copies (query
+// loads and output stores are drained at piece starts).
+template <int kDS, bool kLocal>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_pipe_kernel(DecodeParams p) {
+  constexpr int kRG = 4 / kDS;                 // row groups of 32 rows
+  constexpr int kRowsBlk = 32 * kRG;
+  constexpr int kDb = (kDv / 32) / kDS;        // 32-dim blocks of this wave's V slice
+  constexpr int kNS = 4;
+  constexpr int kCopies = 9;
+  constexpr int kG = 4 / kDS;
+  constexpr int kKS = 9 * kG;                  // QK k-steps per wave
+  constexpr int kPvSteps = 2 * kDb;
+  constexpr int kAhead = 4;
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * kStageBytes];
+  __shared__ __attribute__((aligned(16))) f32x4_t xbuf[4 * 4 * 64];   // [wave][4][lane]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = wave % kRG, ds = wave / kRG;
+  const int tok = lane & 31, hi = lane >> 5;
+
+  int g = blockIdx.x;
+  if ((p.grid & 7) == 0) g = (blockIdx.x & 7) * (p.grid >> 3) + (blockIdx.x >> 3);
+  const int G = ld_const(p.plan + 1);
+  if (g >= G) return;
+  const int Uw = ld_const(p.wg_ustart + g + 1) - ld_const(p.wg_ustart + g);
+  if (Uw <= 0) return;
+
+  const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_address(smem));
+  const uint32_t qk0 = (uint32_t)(1024 * tok + 16 * ((2 * kG * ds) ^ hi ^ chunk_swz(tok)));
+  const uint32_t rope0 = (uint32_t)(kRopeBase + 128 * tok + 16 * ((2 * kG * ds) ^ hi ^ chunk_swz(tok)));
+  uint32_t pv0;
+  {
+    const int g16 = lane >> 4, r = (lane >> 2) & 3, q = lane & 3;
+    const int tl = 4 * (g16 >> 1) + r;
+    const int y = 2 * (g16 & 1) + (q >> 1);
+    pv0 = (uint32_t)(1024 * tl + 16 * (y ^ chunk_swz(tl)) + 8 * (q & 1) + 64 * kDb * ds);
+  }
+
+  // cc: the piece being computed; cl: the next tile to copy
+  Cursor cc, cl;
+  {
+    const int2 st = ld_const(p.wg_start + g);
+    cc.start(p, st.x, st.y);
+    cl = cc;
+  }
+  int ncopied = 0;
+  TileEntries te;   // entries of tile ncopied, loaded a barrier ahead
+  load_entries<kLocal>(p, cl, wave, te);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint8_t* src = token_src<kLocal>(p, cl, k < Uw, te);
+    const uint32_t st = smem_lds + kStageBytes * k;
+#pragma unroll
+    for (int j = 0; j < kCopies; ++j) copy_tile_part_rt(j, src, st);
+    ++ncopied;
+    if (ncopied < Uw) {
+      cl.advance(p);
+      load_entries<kLocal>(p, cl, wave, te);
+    }
+  }
+
+  bf16x8_t qreg[kKS];
+  const uint8_t* csrc = nullptr;   // copies of this iteration: sources, stage
+  uint32_t cst = 0;
+  // tile barrier: the tile that the next QK reads has landed in every wave,
+  // and the stage of the tile two back is free for tile ncopied; the table
+  // entries of the tile after it are loaded here for the next barrier
+  auto tile_barrier = [&]() {
+    wait_vmcnt<kCopies>();
+    __syncthreads();
+    csrc = token_src<kLocal>(p, cl, ncopied < Uw, te);
+    cst = __builtin_amdgcn_readfirstlane(smem_lds + kStageBytes * (ncopied & (kNS - 1)));
+    ++ncopied;
+    if (ncopied < Uw) {
+      cl.advance(p);
+      load_entries<kLocal>(p, cl, wave, te);
+    }
+  };
+  // The MFMAs of one iteration form a sequence of kSlots; copy j of the
+  // iteration's tile goes out after MFMA copy_slot(j).
+  constexpr int kSlots = kKS + kPvSteps;
+  auto after_mfma = [&](int m) {
+    if (copy_at_slot(m, kSlots, kCopies) >= 0) copy_tile_part_rt(copy_at_slot(m, kSlots, kCopies), csrc, cst);
+  };
+  // scores: S^T of a tile over this wave's k-steps, one MFMA per step, K
+  // operands read kAhead steps ahead
+  bf16x8_t ka[kAhead];
+  f32x16_t acc;
+  auto qk_start = [&](const uint8_t* ks) {
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) ka[u] = qk_operand<kG>(ks, qk0, rope0, u);
+    acc = f32x16_t{};
+  };
+  auto qk_step = [&](const uint8_t* ks, int i) {
+    const bf16x8_t a = ka[i % kAhead];
+    if (i + kAhead < kKS) ka[i % kAhead] = qk_operand<kG>(ks, qk0, rope0, i + kAhead);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[i], acc, 0, 0, 0);
+  };
+  // this wave's partial scores to the exchange buffer
+  auto xchg_write = [&](const f32x16_t& a) {
+    f32x4_t* mine = xbuf + (wave * 4) * 64 + lane;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mine[64 * q] = f32x4_t{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+  };
+  // the row group's summed scores (after the exchange barrier): both waves
+  // of a pair form s0 + s1 (addition commutes exactly); four waves sum in
+  // wave order from the buffer
+  auto xchg_sum = [&](const f32x16_t& a) {
+    f32x16_t r;
+    if constexpr (kDS == 2) {
+      const f32x4_t* src = xbuf + (((1 - ds) * kRG + rg) * 4) * 64 + lane;
+      f32x4_t v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = src[64 * q];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[4 * q + e] = a[4 * q + e] + v[q][e];
+    } else {
+      r = f32x16_t{};
+#pragma unroll
+      for (int d = 0; d < kDS; ++d) {
+        const f32x4_t* src = xbuf + ((d * kRG + rg) * 4) * 64 + lane;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4_t v = src[64 * q];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r[4 * q + e] += v[e];
+        }
+      }
+    }
+    return r;
+  };
+  // accumulation O^T[dim][row] += V^T[dim][token] P^T[token][row] over
+  // this wave's dims (transposed V reads the A operand, the P registers the
+  // B operand, both with the same token order in k); step s2 covers dim
+  // block s2 % kDb and token half s2 / kDb, so consecutive MFMAs update
+  // different accumulators
+  auto pv_index = [](int s2) { return 2 * (s2 % kDb) + s2 / kDb; };
+  bf16x8_t va[kAhead];
+
+  int t = 0;   // unit index of the current piece's first tile
+  while (t < Uw) {
+    const int b = cc.b, rb = cc.rb, tile0 = cc.tile, ntiles = cc.ntiles, cnt = cc.cnt;
+    const int n = min(ntiles - tile0, Uw - t);
+    const int row = rb * kRowsBlk + rg * 32 + tok;
+    const bool row_ok = row < p.rows;
+    {
+      const uint16_t* qrow = p.q + ((long long)b * p.rows + (row_ok ? row : 0)) * kDqk + 8 * hi;
+#pragma unroll
+      for (int i = 0; i < kKS; ++i) {
+        const int kk = 4 * (i / kG) + kG * ds + i % kG;
+        const bf16x8_t x = *(const bf16x8_t*)(qrow + 16 * kk);
+        qreg[i] = row_ok ? x : bf16x8_t{};
+      }
+    }
+    // the query loads are the only loads the compiler tracks: waiting for
+    // everything here keeps its own waits out of the tile loop
+    wait_vmcnt<0>();
+    // owned tokens row (draft i) may see: t = j S + r <= L - q_len + i
+    int jvis = 0;
+    {
+      int L = ld_const(p.seq_lens + b);
+      L = L < 0 ? 0 : min(L, p.max_pages * kPage);
+      const int i = (row >= p.heads) + (row >= 2 * p.heads) + (row >= 3 * p.heads);
+      for (int k = 0; k < p.q_len; ++k) {
+        const int lim = L - p.q_len + k - p.shard;
+        const int jl = lim >= 0 ? min(cnt, lim / p.num_shards + 1) : 0;
+        jvis = i == k ? jl : jvis;
+      }
+    }
+
+    f32x16_t o[kDb];
+#pragma unroll
+    for (int db = 0; db < kDb; ++db) o[db] = f32x16_t{};
+    float m_ref = kNegInf, l_sum = 0.f;
+
+    auto pv_start = [&](const uint8_t* ks) {
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u) va[u] = pv_operand(ks, pv0, pv_index(u));
+    };
+    auto pv_step = [&](const uint8_t* ks, const bf16x8_t (&pb)[2], int s2) {
+      const int st = pv_index(s2);
+      const bf16x8_t a = va[s2 % kAhead];
+      if (s2 + kAhead < kPvSteps) va[s2 % kAhead] = pv_operand(ks, pv0, pv_index(s2 + kAhead));
+      o[st >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st & 1], o[st >> 1], 0, 0, 0);
+    };
+    // online softmax of tile k in base 2 (lane: one row, 16 tokens; value v
+    // is token 8 (v >> 2) + 4 hi + (v & 3)); tokens at or past the row's
+    // visibility limit are masked; the max is taken on the raw scores
+    // (scaling by a positive factor commutes with it exactly) and the scale
+    // is folded into the exponent's FMA. Split into kQ1 chunks that run
+    // between the score MFMAs of the next tile: chunks 0 and 1 mask and take
+    // the max (and move the reference), the rest exponentiate.
+    constexpr int kQ1 = kKS / 2;            // score steps before the accumulation starts
+    constexpr int kP1 = kPvSteps / 2;       // accumulation steps before the exchange
+    static_assert(kQ1 >= 3, "softmax chunks");
+    float f = 1.f, tmax = kNegInf, neg_m = 0.f;
+    bool grow = false;
+    int lim = 0;
+    auto softmax_chunk = [&](int c, int k, f32x16_t& sc, bf16x8_t (&pb)[2]) {
+      if (c == 0) {
+        lim = jvis - (tile0 + k) * kTile - 4 * hi;
+        tmax = kNegInf;
+      }
+      if (c < 2) {
+#pragma unroll
+        for (int v = 8 * c; v < 8 * c + 8; ++v) {
+          const int cc_ = 8 * (v >> 2) + (v & 3);
+          sc[v] = cc_ < lim ? sc[v] : kNegInf;
+          tmax = fmaxf(tmax, sc[v]);
+        }
+      }
+      if (c == 1) {
+        const float tm = xor32_max(tmax) * p.scale_log2;
+        grow = m_ref != kNegInf && tm > m_ref + kRescaleSlack;
+        f = grow ? exp2_fast(m_ref - tm) : 1.f;
+        l_sum *= f;
+        m_ref = grow || m_ref == kNegInf ? tm : m_ref;
+        neg_m = m_ref == kNegInf ? 0.f : -m_ref;
+      }
+      if (c >= 2) {
+        constexpr int kE = kQ1 - 2;         // exponent chunks
+        const int v0 = (c - 2) * 16 / kE, v1 = (c - 1) * 16 / kE;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          if (v >= v0 && v < v1) {
+            const float pr = exp2_fast(__builtin_fmaf(sc[v], p.scale_log2, neg_m));
+            l_sum += pr;
+            pb[v >> 3][v & 7] = (__bf16)pr;
+          }
+        }
+      }
+      if (c == kQ1 - 1) {
+        // the results exist before the rescale branch (otherwise they are
+        // sunk below it, away from the MFMAs they overlap)
+        asm volatile("" :: "v"(l_sum), "v"(pb[0]), "v"(pb[1]));
+      }
+    };
+    // the rare rescale of the accumulators (every value a lane holds
+    // belongs to its own row)
+    auto rescale = [&]() {
+      if (__builtin_expect(__ballot(grow) != 0, 0)) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+#pragma unroll
+          for (int db = 0; db < kDb; ++db) o[db][v] = acc_scale(o[db][v], f);
+      }
+    };
+
+    // tile 0: its scores; the copies of its barrier all go out here
+    f32x16_t s_cur;
+    {
+      tile_barrier();
+      const uint8_t* ksq = smem + kStageBytes * (t & (kNS - 1));
+      qk_start(ksq);
+#pragma unroll
+      for (int i = 0; i < kKS; ++i) {
+        qk_step(ksq, i);
+        after_mfma(i);
+      }
+      xchg_write(acc);
+      __syncthreads();
+      s_cur = xchg_sum(acc);
+#pragma unroll
+      for (int m = kKS; m < kSlots; ++m) after_mfma(m);
+    }
+    // tiles k + 1 <= n - 1: the scores of tile k + 1 run with the softmax
+    // and then the accumulation of tile k
+    for (int k = 0; k + 1 < n; ++k) {
+      tile_barrier();
+      const uint8_t* ksq = smem + kStageBytes * ((t + k + 1) & (kNS - 1));
+      const uint8_t* ksv = smem + kStageBytes * ((t + k) & (kNS - 1));
+      bf16x8_t pb[2];
+      qk_start(ksq);
+#pragma unroll
+      for (int i = 0; i < kQ1; ++i) {
+        qk_step(ksq, i);
+        after_mfma(i);
+        softmax_chunk(i, k, s_cur, pb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      rescale();
+      pv_start(ksv);
+      // the remaining score steps alternate with the first accumulation
+      // steps (independent MFMAs back to back)
+      constexpr int kMix = (kKS - kQ1) > kP1 ? (kKS - kQ1) : kP1;
+#pragma unroll
+      for (int j = 0; j < kMix; ++j) {
+        if (kQ1 + j < kKS) {
+          qk_step(ksq, kQ1 + j);
+          after_mfma(kQ1 + 2 * j);
+        }
+        if (j < kP1) {
+          pv_step(ksv, pb, j);
+          after_mfma(kQ1 + 2 * j + 1);
+        }
+      }
+      xchg_write(acc);
+      __syncthreads();
+      if constexpr (kDS == 2) {
+        // the partner's partial scores are read first and added after the
+        // accumulation steps, whose MFMAs cover the reads' latency
+        const f32x4_t* src = xbuf + (((1 - ds) * kRG + rg) * 4) * 64 + lane;
+        f32x4_t pv4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pv4[q] = src[64 * q];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s2 = kP1; s2 < kPvSteps; ++s2) {
+          pv_step(ksv, pb, s2);
+          after_mfma(kKS + s2);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s_cur[4 * q + e] = acc[4 * q + e] + pv4[q][e];
+      } else {
+#pragma unroll
+        for (int s2 = kP1; s2 < kPvSteps; ++s2) {
+          pv_step(ksv, pb, s2);
+          after_mfma(kKS + s2);
+        }
+        s_cur = xchg_sum(acc);
+      }
+      // keep the accumulators in AGPRs across iterations (left to itself
+      // the register allocator moves them through VGPRs and spills)
+#pragma unroll
+      for (int db = 0; db < kDb; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) asm volatile("" : "+a"(o[db][v]));
+    }
+    // the last tile of the piece
+    {
+      bf16x8_t pb[2];
+#pragma unroll
+      for (int c = 0; c < kQ1; ++c) softmax_chunk(c, n - 1, s_cur, pb);
+      rescale();
+      const uint8_t* ksv = smem + kStageBytes * ((t + n - 1) & (kNS - 1));
+      pv_start(ksv);
+#pragma unroll
+      for (int s2 = 0; s2 < kPvSteps; ++s2) pv_step(ksv, pb, s2);
+    }
+
+    // piece epilogue: the accumulators hold O^T (V^T is the A operand): lane
+    // l has row rg * 32 + (l & 31) and o[db][v] is its dim
+    // 32 (kDb ds + db) + 8 (v >> 2) + 4 hi + (v & 3)
+    const float l_tot = xor32_sum(l_sum);
+    const bool any = l_tot > 0.f || l_tot != l_tot;
+    const float inv = any ? p.out_scale / l_tot : 0.f;
+    const float lse2 = any ? m_ref + log2_fast(l_tot) : kNegInf;
+    const bool single = tile0 == 0 && n == ntiles;
+    const int row0 = rb * kRowsBlk + rg * 32;          // first row of the row group
+    if (single && !p.out_bf16) {
+      // f32 output: four consecutive dims per lane and store
+      if (row_ok) {
+        float* dst = (float*)p.out + ((long long)b * p.rows + row) * kDv + 32 * kDb * ds + 4 * hi;
+#pragma unroll
+        for (int db = 0; db < kDb; ++db)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4_t x = {acc_read(o[db][4 * q]) * inv, acc_read(o[db][4 * q + 1]) * inv,
+                               acc_read(o[db][4 * q + 2]) * inv, acc_read(o[db][4 * q + 3]) * inv};
+            *(f32x4_t*)(dst + 32 * db + 8 * q) = x;
+          }
+      }
+    } else {
+      // bf16 output through LDS: each wave writes its 32 rows x (kDb * 32)
+      // dims row-major (rows padded to 528 bytes) into the stages of the
+      // piece's last two tiles, free once every wave has passed this
+      // barrier, and stores whole rows (16 bytes a lane)
+      constexpr int kRowPitch = 528;
+      static_assert(2 * 32 * kRowPitch <= kStageBytes, "two waves' rows per stage");
+      __syncthreads();
+      uint8_t* tb = smem + kStageBytes * ((t + n - 1 - (wave >> 1)) & (kNS - 1)) + (wave & 1) * 32 * kRowPitch;
+      typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+      for (int db = 0; db < kDb; ++db)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bf16x4_t x = {(__bf16)(acc_read(o[db][4 * q]) * inv), (__bf16)(acc_read(o[db][4 * q + 1]) * inv),
+                              (__bf16)(acc_read(o[db][4 * q + 2]) * inv), (__bf16)(acc_read(o[db][4 * q + 3]) * inv)};
+          *(bf16x4_t*)(tb + kRowPitch * tok + 2 * (32 * db + 8 * q + 4 * hi)) = x;
+        }
+      __bf16* obase;
+      long long pitch_rows;
+      if (single) {
+        obase = (__bf16*)p.out + ((long long)b * p.rows + row0) * kDv;
+      } else {
+        const int4 si = ld_const(p.seg_info + b * p.row_blocks + rb);
+        obase = (__bf16*)p.spart_o + ((long long)(si.x + g - si.z) * kRowsBlk + rg * 32) * kDv;
+      }
+      (void)pitch_rows;
+      constexpr int kLanesPerRow = kDb * 32 / 8;        // 16-byte pieces of a row's slice
+      constexpr int kRowsPerStore = 64 / kLanesPerRow;
+      const int rr0 = lane / kLanesPerRow, cc = lane % kLanesPerRow;
+#pragma unroll
+      for (int i = 0; i < 32 / kRowsPerStore; ++i) {
+        const int rr = kRowsPerStore * i + rr0;
+        const bf16x8_t x = *(const bf16x8_t*)(tb + kRowPitch * rr + 16 * cc);
+        if (row0 + rr < p.rows) *(bf16x8_t*)(obase + (long long)rr * kDv + 32 * kDb * ds + 8 * cc) = x;
+      }
+    }
+    if (row_ok && ds == 0 && hi == 0) {
+      if (single) {
+        p.lse[(long long)b * p.rows + row] = p.lse_base2 ? lse2 : lse2 * kLn2;
+      } else {
+        const int4 si = ld_const(p.seg_info + b * p.row_blocks + rb);
+        p.spart_lse[(long long)(si.x + g - si.z) * kRowsBlk + (row - rb * kRowsBlk)] = lse2;
+      }
+    }
+    t += n;
+    if (t < Uw) {
+      cc.tile = ntiles - 1;
+      cc.advance(p);
+    }
+  }
+  // no copy may still be writing this workgroup's LDS when it exits
+  wait_vmcnt<0>();
 }
 
 // ---------------------------------------------------------------------------
@@ -875,8 +1456,12 @@ hipError_t launch_decode_stream(const DecodeParams& p, hipEvent_t ev_begin, hipE
   const void* fn;
   if (p.kv_fp8) fn = p.rows_blk == 32 ? reinterpret_cast<const void*>(&attn_stream_kernel<4, true>)
                                       : reinterpret_cast<const void*>(&attn_stream_kernel<2, true>);
-  else fn = p.rows_blk == 32 ? reinterpret_cast<const void*>(&attn_stream_kernel<4, false>)
-                             : reinterpret_cast<const void*>(&attn_stream_kernel<2, false>);
+  else if (p.local_kv_indices != nullptr)
+    fn = p.rows_blk == 32 ? reinterpret_cast<const void*>(&attn_pipe_kernel<4, true>)
+                          : reinterpret_cast<const void*>(&attn_pipe_kernel<2, true>);
+  else
+    fn = p.rows_blk == 32 ? reinterpret_cast<const void*>(&attn_pipe_kernel<4, false>)
+                          : reinterpret_cast<const void*>(&attn_pipe_kernel<2, false>);
   err = hipExtLaunchKernel(fn, dim3(p.grid), dim3(256), args, 0, stream, ev_begin, ev_end, 0);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(stream_combine_kernel, dim3(p.batch, (p.rows + 3) / 4), dim3(256), 0, stream, p);
