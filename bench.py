@@ -182,17 +182,66 @@ def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True, spl
         if timed:
             mev[k][1].record()
 
+    # kernel timing: eager steps, the attention kernel bracketed by events
+    # that take its own dispatch start and end
     log(f"[bench] config {index}: warmup {warmup}")
     for k in range(warmup):
         one_step(k, False)
     torch.cuda.synchronize()
-    log(f"[bench] config {index}: timing {steps} steps")
+    log(f"[bench] config {index}: kernel timing over {steps} eager steps")
     t0 = time.perf_counter()
     for k in range(steps):
         one_step(k, True)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_step = 1e3 * elapsed / steps
+    eager_ms_step = 1e3 * (time.perf_counter() - t0) / steps
+
+    # step timing: the step (every shard's partial on a stream of its own,
+    # joined for the merge) captured as one HIP graph per input set and
+    # replayed; checked bit for bit against the eager step first
+    step_timing = "graph replay, shard partials on concurrent streams"
+    ms_step = None
+    if split_target == 0:
+        try:
+            streams = [torch.cuda.Stream() for _ in range(S)]
+            graphs = []
+            for dw in dws:
+                ST.run_step_concurrent(dw, bufs, streams)      # warm the path before capture
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    ST.run_step_concurrent(dw, bufs, streams)
+                graphs.append(g)
+            torch.cuda.synchronize()
+            for i, dw in enumerate(dws):
+                bufs.fill_nan()
+                for r in range(S):
+                    ST.run_partial(dw, bufs, r)
+                ST.run_merge(dw, bufs)
+                torch.cuda.synchronize()
+                ref_out, ref_lse = bufs.out.clone(), bufs.lse.clone()
+                for _ in range(2):
+                    bufs.fill_nan()
+                    graphs[i].replay()
+                    torch.cuda.synchronize()
+                    if not (torch.equal(bufs.out.view(torch.uint8), ref_out.view(torch.uint8))
+                            and torch.equal(bufs.lse.view(torch.uint8), ref_lse.view(torch.uint8))):
+                        raise RuntimeError("graph replay differs from the eager step")
+            for k in range(warmup):
+                graphs[k % len(graphs)].replay()
+            torch.cuda.synchronize()
+            log(f"[bench] config {index}: timing {steps} steps (graph replay)")
+            t0 = time.perf_counter()
+            for k in range(steps):
+                graphs[k % len(graphs)].replay()
+            torch.cuda.synchronize()
+            ms_step = 1e3 * (time.perf_counter() - t0) / steps
+            del graphs
+        except Exception as e:  # noqa: BLE001 - fall back to the eager step time
+            log(f"[bench] config {index}: graph step unavailable ({e}); eager step time reported")
+            ms_step = None
+    if ms_step is None:
+        ms_step = eager_ms_step
+        step_timing = "eager launches"
     attn_ms = [[ev[k][r][0].elapsed_ms(ev[k][r][1]) for r in range(S)] for k in range(steps)]
     merge_ms = [mev[k][0].elapsed_time(mev[k][1]) for k in range(steps)]
     tot_bytes = sum(b for b, _ in per_shard)
@@ -209,7 +258,7 @@ def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True, spl
         attn_kernel_mean_us=1e3 * mean_launch_ms, attn_kernel_bytes_per_launch=tot_bytes / S,
         attn_kernel_gbs=achieved_gbs, attn_kernel_tflops=achieved_tflops,
         merge_us=1e3 * statistics.median(merge_ms), steps=steps, warmup=warmup, rotated=len(dws),
-        metadata_us_per_shard=metadata_us,
+        metadata_us_per_shard=metadata_us, step_timing=step_timing, eager_ms_per_step=eager_ms_step,
     )
     # the contraction runs on bf16 MFMAs for both KV types (fp8 pages are
     # converted to bf16 in LDS), so its peak is the bf16 one
@@ -393,12 +442,12 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8" if wl.kv_dtype == "fp8" else "bf16",
+        "dtype": "bf16",            # MFMA contraction type (fp8 KV is converted to bf16)
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: batch {wl.batch}, {wl.heads} heads, q_len {wl.q_len}, "
                                f"{wl.shards} cyclic shards, {wl.kv_dtype} KV, page 64, "
                                f"{res['tokens']} context tokens, partials + merge",
-                   "global_batch": wl.batch, "shards": wl.shards},
+                   "global_batch": wl.batch, "shards": wl.shards, "step": res["step_timing"]},
         "tflops": round(res["tflops"], 3),
         "merge_us": {T: round(v["us_median"], 2) for T, v in merge.items()} if merge else None,
         "merge_roofline": (dict(bound="hbm", T=128, achieved=round(merge["128"]["gbs"], 1), peak=HBM_PEAK_GBS,

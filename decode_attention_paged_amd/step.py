@@ -73,6 +73,14 @@ class StepBuffers:
                                  for r in range(S)]
         nbytes = L.mla_decode_workspace_bytes(B, H, q)
         self.workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+        self._nbytes = max(nbytes, 1)
+        self.workspaces = [self.workspace]
+
+    def per_shard_workspaces(self) -> None:
+        """One workspace per shard, so that shard partials may run concurrently."""
+        dev = self.workspace.device
+        while len(self.workspaces) < len(self.outs):
+            self.workspaces.append(torch.empty((self._nbytes,), dtype=torch.uint8, device=dev))
 
     def fill_nan(self) -> None:
         for t in self.outs + self.lses + [self.out, self.lse]:
@@ -87,9 +95,10 @@ def run_metadata(dw: DeviceWorkload, bufs: StepBuffers, shard: int, stream=None)
 
 def run_partial(dw: DeviceWorkload, bufs: StepBuffers, shard: int, use_metadata: bool = True,
                 split_target: int = 0, events=None, stream=None) -> int:
+    ws = bufs.workspaces[shard] if shard < len(bufs.workspaces) else bufs.workspace
     return L.mla_decode_partial(
         dw.q, dw.kv_pages, dw.block_table, dw.seq_lens, shard, dw.shards, dw.q_len,
-        bufs.outs[shard], bufs.lses[shard], bufs.workspace, kv_scale=dw.kv_scale,
+        bufs.outs[shard], bufs.lses[shard], ws, kv_scale=dw.kv_scale,
         softmax_scale=dw.softmax_scale, lse_base=dw.lse_base,
         local_seq_lens=bufs.local_seq_lens[shard] if use_metadata else None,
         local_kv_indices=bufs.local_kv_indices[shard] if use_metadata else None,
@@ -112,3 +121,20 @@ def run_step(dw: DeviceWorkload, bufs: StepBuffers, use_metadata: bool = True, s
             run_metadata(dw, bufs, r, stream=stream)
         run_partial(dw, bufs, r, use_metadata=use_metadata, split_target=split_target, stream=stream)
     run_merge(dw, bufs, out_base=out_base, stream=stream)
+
+
+def run_step_concurrent(dw: DeviceWorkload, bufs: StepBuffers, streams, use_metadata: bool = True,
+                        out_base: int = L.LSE_BASE_E) -> None:
+    """Partials of all shards on their own streams (one workspace each), joined
+    on the current stream, then the merge. Capturable as one HIP graph."""
+    import torch
+    bufs.per_shard_workspaces()
+    cur = torch.cuda.current_stream()
+    for r in range(dw.shards):
+        s = streams[r]
+        s.wait_stream(cur)
+        with torch.cuda.stream(s):
+            run_partial(dw, bufs, r, use_metadata=use_metadata, stream=s)
+    for r in range(dw.shards):
+        cur.wait_stream(streams[r])
+    run_merge(dw, bufs, out_base=out_base, stream=cur)
