@@ -75,6 +75,7 @@ WorkspaceLayout decode_workspace_layout(int32_t batch, int32_t rows) {
   w.seg_info = off;  off = align_up(off + sizeof(int4) * (size_t)nseg, 256);
   w.wg_start = off;  off = align_up(off + sizeof(int2) * (size_t)kMaxGrid, 256);
   w.wg_ustart = off; off = align_up(off + sizeof(int32_t) * (size_t)(kMaxGrid + 1), 256);
+  w.wg_rec = off;    off = align_up(off + sizeof(int32_t) * (size_t)kMaxGrid * kRecInts, 256);
   w.spart_lse = off; off = align_up(off + sizeof(float) * (size_t)w.max_slots * rows_blk, 256);
   w.spart_o = off;   off = align_up(off + sizeof(uint16_t) * (size_t)w.max_slots * rows_blk * kDv, 256);
   w.total = off;
@@ -216,6 +217,7 @@ mla_status_t mla_decode_partial(const mla_decode_args_t* a, mla_lse_base_t* lse_
   p.wg_ustart = (int32_t*)(ws + w.wg_ustart);
   p.seg_info = (int4*)(ws + w.seg_info);
   p.wg_start = (int2*)(ws + w.wg_start);
+  p.wg_rec = (int32_t*)(ws + w.wg_rec);
   p.spart_lse = (float*)(ws + w.spart_lse);
   p.spart_o = (uint16_t*)(ws + w.spart_o);
   p.rows_blk = mla::stream_rows_per_block(rows);

@@ -43,6 +43,10 @@ struct DecodeParams {
   int32_t* wg_ustart;             // [grid + 1] first unit of each workgroup
   int4* seg_info;                 // [B * row_blocks] (slot base, pieces, first workgroup, -)
   int2* wg_start;                 // [grid] (segment, tile) of each workgroup's first unit
+  // [grid][kRecInts] start record of each workgroup: units, first segment and
+  // tile, owned-token count of that request, then the KV rows of the tokens
+  // of its first two tiles (-1: the zero row, -2: the NaN row)
+  int32_t* wg_rec;
   uint16_t* spart_o;              // [slots][rows_blk][512] bf16, normalised, scaled
   float* spart_lse;               // [slots][rows_blk] base 2
   int32_t rows_blk;               // query rows per workgroup (32 or 64)
@@ -51,6 +55,7 @@ struct DecodeParams {
 };
 
 constexpr int kMaxGrid = 1024;  // persistent workgroups of the streaming kernel
+constexpr int kRecInts = 80;    // start record: 8-int header, pad, 2 x 32 rows
 
 // Query rows one streaming workgroup covers: its four waves are 2 row groups
 // of 32 rows x 2 halves of the dims (rows > 32), or 1 x 4 (rows <= 32); more
@@ -59,7 +64,7 @@ constexpr int kMaxGrid = 1024;  // persistent workgroups of the streaming kernel
 inline int32_t stream_rows_per_block(int32_t rows) { return rows <= 32 ? 32 : 64; }
 
 struct WorkspaceLayout {
-  size_t plan, req_cnt, seg_off, seg_coff, seg_info, wg_start, wg_ustart, spart_lse, spart_o, total;
+  size_t plan, req_cnt, seg_off, seg_coff, seg_info, wg_start, wg_ustart, wg_rec, spart_lse, spart_o, total;
   int32_t max_slots;
 };
 WorkspaceLayout decode_workspace_layout(int32_t batch, int32_t rows);

@@ -114,6 +114,7 @@ constexpr int kPlanLdsSegs = 6144;
 
 __global__ __launch_bounds__(1024) void stream_plan_kernel(DecodeParams p) {
   __shared__ int32_t s_arr[2 * (kPlanLdsSegs + 1)];
+  __shared__ int32_t s_cnt[kPlanLdsSegs];           // owned tokens per segment's request
   __shared__ int32_t s_wgu[kMaxGrid + 1];
   __shared__ int2 s_wave[16];
   const int tid = threadIdx.x;
@@ -132,6 +133,7 @@ __global__ __launch_bounds__(1024) void stream_plan_kernel(DecodeParams p) {
     const int b = s / RB;
     const int cnt = local_count(p, b);
     if (s - b * RB == 0) p.req_cnt[b] = cnt;
+    if (in_lds) s_cnt[s] = cnt;
     const int n = (cnt + kTile - 1) / kTile;
     su += n;
     sc += n > 0 ? n + kPieceCost : 0;
@@ -177,6 +179,32 @@ __global__ __launch_bounds__(1024) void stream_plan_kernel(DecodeParams p) {
   }
   __syncthreads();
 
+  // start record of each workgroup: its range, its first unit with the
+  // owned-token count of that request, and the segment (with its count) of
+  // the unit after its first segment, so that the decode kernel resolves
+  // the rows of its first two tiles after a single round of loads
+  for (int w = tid; w < p.grid; w += 1024) {
+    int32_t* rec = p.wg_rec + (long long)w * kRecInts;
+    const int u0 = w < G ? s_wgu[w] : 0, u1 = w < G ? s_wgu[w + 1] : 0;
+    int seg = 0, tile = 0, cnt = 0, seg1 = 0, cnt1 = 0;
+    if (u1 > u0) {
+      seg = last_le(off, nseg + 1, u0);
+      tile = u0 - off[seg];
+      cnt = in_lds ? s_cnt[seg] : local_count(p, seg / RB);
+      const int un = off[seg + 1];          // first unit past the first segment
+      if (un < u1) {
+        seg1 = last_le(off, nseg + 1, un);
+        cnt1 = in_lds ? s_cnt[seg1] : local_count(p, seg1 / RB);
+      }
+    }
+    rec[0] = u1 - u0;
+    rec[1] = seg;
+    rec[2] = tile;
+    rec[3] = cnt;
+    rec[4] = seg1;
+    rec[5] = cnt1;
+  }
+
   // pieces of each segment (one per non-empty workgroup it meets) and
   // partial slots (only for segments cut into several pieces)
   int ms = 0;
@@ -214,6 +242,13 @@ struct Cursor {
     rb = seg - b * p.row_blocks;
     tile = t;
     cnt = ld_const(p.req_cnt + b);
+    ntiles = (cnt + kTile - 1) / kTile;
+  }
+  __device__ __forceinline__ void start_known(const DecodeParams& p, int seg, int t, int count) {
+    b = seg / p.row_blocks;
+    rb = seg - b * p.row_blocks;
+    tile = t;
+    cnt = count;
     ntiles = (cnt + kTile - 1) / kTile;
   }
   // move to the next unit; only called when one exists
@@ -984,13 +1019,18 @@ void attn_pipe_kernel(DecodeParams p) {
   const int rg = wave % kRG, ds = wave / kRG;
   const int tok = lane & 31, hi = lane >> 5;
 
+  // consecutive workgroups of the unit order run on one XCD (blocks are
+  // dealt to the 8 XCDs round robin), so the L2 of that XCD serves the
+  // repeated reads of a request's Q and KV
   int g = blockIdx.x;
   if ((p.grid & 7) == 0) g = (blockIdx.x & 7) * (p.grid >> 3) + (blockIdx.x >> 3);
-  const int G = ld_const(p.plan + 1);
-  if (g >= G) return;
-  const int Uw = ld_const(p.wg_ustart + g + 1) - ld_const(p.wg_ustart + g);
+  // the start record: one round of scalar loads, then one for the table
+  // entries of the first two tiles, before the first copies
+  const int32_t* rec = p.wg_rec + (long long)g * kRecInts;
+  const int Uw = ld_const(rec);
+  const int rec_seg = ld_const(rec + 1), rec_tile = ld_const(rec + 2), rec_cnt = ld_const(rec + 3);
+  const int rec_seg1 = ld_const(rec + 4), rec_cnt1 = ld_const(rec + 5);
   if (Uw <= 0) return;
-
   const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_address(smem));
   const uint32_t qk0 = (uint32_t)(1024 * tok + 16 * ((2 * kG * ds) ^ hi ^ chunk_swz(tok)));
   const uint32_t rope0 = (uint32_t)(kRopeBase + 128 * tok + 16 * ((2 * kG * ds) ^ hi ^ chunk_swz(tok)));
@@ -1003,26 +1043,32 @@ void attn_pipe_kernel(DecodeParams p) {
   }
 
   // cc: the piece being computed; cl: the next tile to copy
+  // cc: the piece being computed; cl: the next tile to copy, te its table
+  // entries. The first two tiles' cursors come from the record (the second
+  // one may start the next segment).
   Cursor cc, cl;
-  {
-    const int2 st = ld_const(p.wg_start + g);
-    cc.start(p, st.x, st.y);
-    cl = cc;
+  cc.start_known(p, rec_seg, rec_tile, rec_cnt);
+  cl = cc;
+  if (1 < Uw) {
+    if (cl.tile + 1 < cl.ntiles) ++cl.tile;
+    else cl.start_known(p, rec_seg1, 0, rec_cnt1);
   }
-  int ncopied = 0;
+  {
+    TileEntries te0, te1;
+    load_entries<kLocal>(p, cc, wave, te0);
+    if (1 < Uw) load_entries<kLocal>(p, cl, wave, te1);
+    const uint8_t* src0 = token_src<kLocal>(p, cc, true, te0);
+#pragma unroll
+    for (int j = 0; j < kCopies; ++j) copy_tile_part_rt(j, src0, smem_lds);
+    const uint8_t* src1 = token_src<kLocal>(p, cl, 1 < Uw, te1);
+#pragma unroll
+    for (int j = 0; j < kCopies; ++j) copy_tile_part_rt(j, src1, smem_lds + kStageBytes);
+  }
+  int ncopied = 2;
   TileEntries te;   // entries of tile ncopied, loaded a barrier ahead
-  load_entries<kLocal>(p, cl, wave, te);
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const uint8_t* src = token_src<kLocal>(p, cl, k < Uw, te);
-    const uint32_t st = smem_lds + kStageBytes * k;
-#pragma unroll
-    for (int j = 0; j < kCopies; ++j) copy_tile_part_rt(j, src, st);
-    ++ncopied;
-    if (ncopied < Uw) {
-      cl.advance(p);
-      load_entries<kLocal>(p, cl, wave, te);
-    }
+  if (2 < Uw) {
+    cl.advance(p);
+    load_entries<kLocal>(p, cl, wave, te);
   }
 
   bf16x8_t qreg[kKS];
