@@ -140,7 +140,8 @@ def traffic_from_profile(workload: str):
 # --------------------------------------------------------------------------
 # GPU timing
 # --------------------------------------------------------------------------
-def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True, split_target: int = 0):
+def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True, split_target: int = 0,
+                   use_graph: bool = True):
     import torch
 
     from decode_attention_paged_amd import step as ST
@@ -200,7 +201,7 @@ def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True, spl
     # replayed; checked bit for bit against the eager step first
     step_timing = "graph replay, shard partials on concurrent streams"
     ms_step = None
-    if split_target == 0:
+    if split_target == 0 and use_graph:
         try:
             streams = [torch.cuda.Stream() for _ in range(S)]
             graphs = []
@@ -358,6 +359,7 @@ def main() -> int:
     ap.add_argument("--details", default=None, help="write per-workload results (JSON) here")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-merge-sweep", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time the step as eager launches")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--split-target", type=int, default=0,
                     help="KV chunks per launch per row block (0 = library default)")
@@ -390,7 +392,8 @@ def main() -> int:
     from decode_attention_paged_amd import _lib as L
     L.load()
 
-    wl, res = bench_workload(args.config, args.steps, args.warmup, split_target=args.split_target)
+    wl, res = bench_workload(args.config, args.steps, args.warmup, split_target=args.split_target,
+                             use_graph=not args.no_graph)
     details = {"headline": res}
     if args.sweep_split:
         for tgt in [int(x) for x in args.sweep_split.split(",")]:
@@ -405,7 +408,8 @@ def main() -> int:
         for idx in (1, 2, 3, 4, 5):
             if idx == args.config:
                 continue
-            _, r = bench_workload(idx, max(3, args.steps // 2), max(1, args.warmup // 2))
+            _, r = bench_workload(idx, max(3, args.steps // 2), max(1, args.warmup // 2),
+                                  use_graph=not args.no_graph)
             details[f"config{idx}"] = r
             log(f"[bench] config {idx} {r['name']}: {r['ms_per_step']:.3f} ms/step, "
                 f"{r['kv_gbs']:.0f} KV-GB/s, {r['tflops']:.1f} TFLOP/s, attn kernel "
