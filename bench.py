@@ -274,9 +274,11 @@ def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True, spl
 def bench_merge_sweep(replays: int = 20, warmup: int = 5):
     """Merge-only: 4 partials of [T, 64, 512] bf16 + fp32 LSE -> [T, 64, 512] bf16.
 
-    Timed as graph replays (one merge per input set in the graph, sets rotated
-    so the MALL holds at most a fraction of them); the per-merge time is the
-    replay time / sets, i.e. back-to-back launches without host overhead."""
+    Two timings per size: the kernel's own dispatch (HIP events recorded with
+    the launch, eager launches over rotated input sets, so the MALL holds at
+    most a fraction of them) — the roofline figure — and graph replays (one
+    merge per input set in the graph): replay time / sets, i.e. back-to-back
+    launches without host overhead, gaps between dispatches included."""
     import torch
 
     from decode_attention_paged_amd import _lib as L
@@ -311,8 +313,17 @@ def bench_merge_sweep(replays: int = 20, warmup: int = 5):
         torch.cuda.synchronize()
         per = sorted(1e3 * a.elapsed_time(b) / nsets for a, b in evs)
         med = statistics.median(per)
+        kevs = [(HipEvent(), HipEvent()) for _ in range(max(replays, nsets))]
+        for k, ev in enumerate(kevs):
+            o, l, y, yl = sets[k % nsets]
+            L.mla_merge_partials(o, l, [L.LSE_BASE_E] * 4, y, yl, events=ev)
+        torch.cuda.synchronize()
+        kus = [1e3 * a.elapsed_ms(b) for a, b in kevs]
+        kmean = statistics.mean(kus)
         out[str(T)] = dict(us_median=med, us_min=per[0], bytes=set_bytes,
-                           gbs=set_bytes / (med * 1e-6) / 1e9, sets=nsets, timing="graph replay")
+                           gbs=set_bytes / (med * 1e-6) / 1e9, sets=nsets, timing="graph replay",
+                           kernel_us_mean=kmean, kernel_us_min=min(kus), kernel_gbs=set_bytes / (kmean * 1e-6) / 1e9,
+                           kernel_launches=len(kus))
         del sets, graph
     torch.cuda.empty_cache()
     return out
@@ -454,8 +465,10 @@ def main() -> int:
                    "global_batch": wl.batch, "shards": wl.shards, "step": res["step_timing"]},
         "tflops": round(res["tflops"], 3),
         "merge_us": {T: round(v["us_median"], 2) for T, v in merge.items()} if merge else None,
-        "merge_roofline": (dict(bound="hbm", T=128, achieved=round(merge["128"]["gbs"], 1), peak=HBM_PEAK_GBS,
-                                unit="GB/s", frac=round(merge["128"]["gbs"] / HBM_PEAK_GBS, 4))
+        "merge_kernel_us": {T: round(v["kernel_us_mean"], 2) for T, v in merge.items()} if merge else None,
+        "merge_roofline": (dict(bound="hbm", T=128, achieved=round(merge["128"]["kernel_gbs"], 1), peak=HBM_PEAK_GBS,
+                                unit="GB/s", frac=round(merge["128"]["kernel_gbs"] / HBM_PEAK_GBS, 4),
+                                kernel_us=round(merge["128"]["kernel_us_mean"], 2))
                            if merge and "128" in merge else None),
         "roofline": roof,
         "cpu_baseline": cpu,

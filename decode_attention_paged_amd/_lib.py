@@ -73,6 +73,8 @@ class MergeArgs(ctypes.Structure):
         ("out_dtype", ctypes.c_int),
         ("lse_out", ctypes.c_void_p),
         ("lse_out_base", ctypes.c_int),
+        ("event_begin", ctypes.c_void_p),
+        ("event_end", ctypes.c_void_p),
     ]
 
 
@@ -210,8 +212,11 @@ def mla_decode_partial(q, kv_pages, block_table, seq_lens, shard_id: int, num_sh
 
 
 def mla_merge_partials(outs: Sequence, lses: Sequence, bases: Sequence[int], out, lse_out=None,
-                       lse_out_base: int = LSE_BASE_E, stream=None) -> None:
-    """LSE-weighted merge of S partials: outs[r] [N, H, Dv], lses[r] [N, H] f32."""
+                       lse_out_base: int = LSE_BASE_E, stream=None, events=None) -> None:
+    """LSE-weighted merge of S partials: outs[r] [N, H, Dv], lses[r] [N, H] f32.
+
+    ``events``: optional pair of timing events that receive the merge
+    kernel's dispatch start and end."""
     lib = load()
     S = len(outs)
     a = MergeArgs()
@@ -224,4 +229,6 @@ def mla_merge_partials(outs: Sequence, lses: Sequence, bases: Sequence[int], out
     a.in_dtype = _dtype_code(outs[0])
     a.out, a.out_dtype = _ptr(out), _dtype_code(out)
     a.lse_out, a.lse_out_base = _ptr(lse_out), int(lse_out_base)
+    if events is not None:
+        a.event_begin, a.event_end = int(events[0].cuda_event), int(events[1].cuda_event)
     _check(lib.mla_merge_partials(ctypes.byref(a), _stream_ptr(stream)))

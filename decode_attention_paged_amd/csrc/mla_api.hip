@@ -271,7 +271,7 @@ mla_status_t mla_merge_partials(const mla_merge_args_t* a, void* stream) {
   p.out = a->out;
   p.lse_out = a->lse_out;
   p.lse_out_from_log2 = a->lse_out_base == MLA_LSE_BASE_E ? 0.69314718055994531f : 1.f;
-  hipError_t err = mla::launch_merge(p, (hipStream_t)stream);
+  hipError_t err = mla::launch_merge(p, (hipEvent_t)a->event_begin, (hipEvent_t)a->event_end, (hipStream_t)stream);
   if (err != hipSuccess) return device_fail(err, "merge launch");
   return ok();
 }

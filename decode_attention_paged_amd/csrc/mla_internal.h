@@ -88,6 +88,6 @@ hipError_t launch_metadata(const int32_t* seq_lens, const int32_t* block_table, 
                            int32_t stride, hipStream_t stream);
 hipError_t launch_decode_stream(const DecodeParams& p, hipEvent_t ev_begin, hipEvent_t ev_end,
                                 hipStream_t stream);
-hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream);
 
 }  // namespace mla

@@ -14,6 +14,8 @@
 // 关键源码片段: the DCP metadata helpers).
 #include "mla_internal.h"
 
+#include <hip/hip_ext.h>
+
 namespace mla {
 namespace {
 
@@ -21,10 +23,28 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 constexpr float kNegInf = -__builtin_inff();
 
+// Vectors per wave (all their loads in flight together) and whether the
+// partials are read and the result written with non-temporal hints (each
+// byte is touched once).
+constexpr int kMergeVecsPerWave = 1;
+constexpr bool kMergeNonTemporal = true;
+constexpr int kMergeWaves = 4;   // waves per workgroup
+
+template <typename T>
+__device__ __forceinline__ T load_stream(const T* p) {
+  if constexpr (kMergeNonTemporal) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <typename T>
+__device__ __forceinline__ void store_stream(T* p, const T& v) {
+  if constexpr (kMergeNonTemporal) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
 // Eight consecutive elements of shard r's partials at element index e, as fp32.
 __device__ __forceinline__ void load8(const MergeParams& p, int r, long long e, f32x4_t& lo, f32x4_t& hi) {
   if (p.in_bf16) {
-    const bf16x8_t x = *(const bf16x8_t*)((const __bf16*)p.outs[r] + e);
+    const bf16x8_t x = load_stream((const bf16x8_t*)((const __bf16*)p.outs[r] + e));
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       lo[k] = (float)x[k];
@@ -32,16 +52,18 @@ __device__ __forceinline__ void load8(const MergeParams& p, int r, long long e, 
     }
   } else {
     const f32x4_t* x = (const f32x4_t*)((const float*)p.outs[r] + e);
-    lo = x[0];
-    hi = x[1];
+    lo = load_stream(x);
+    hi = load_stream(x + 1);
   }
 }
 
-// kS: shard count rounded up to a power of two (registers for kS vectors).
-template <int kS>
-__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
-  const long long vec = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
-  if (vec >= p.vectors) return;
+// kS: shard count rounded up to a power of two (registers for kS vectors);
+// kV: vectors per wave.
+template <int kS, int kV>
+__global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeParams p) {
+  const long long vec0 =
+      (long long)__builtin_amdgcn_readfirstlane((int)(blockIdx.x * kMergeWaves + (threadIdx.x >> 6))) * kV;
+  if (vec0 >= p.vectors) return;
   const int lane = threadIdx.x & 63;
   const int S = p.num_shards;
 
@@ -49,66 +71,75 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   // LSEs (scalar loads, the vector index is wave-uniform) and the first
   // 512-element chunk of every shard's vector (one 16- or 32-byte load per
   // lane); a shard with weight 0 holds zeros, so loading it is harmless
-  float lse2[kS];
-  f32x4_t x0[kS], x1[kS];
+  float lse2[kV][kS];
+  f32x4_t x0[kV][kS], x1[kV][kS];
   const int e_first = 8 * lane;
   const bool have = e_first < p.dv;
 #pragma unroll
-  for (int r = 0; r < kS; ++r) {
-    if (r < S) {
-      lse2[r] = *(const __attribute__((address_space(4))) float*)(p.lses[r] + vec) * p.lse_to_log2[r];
-      if (have) load8(p, r, vec * p.dv + e_first, x0[r], x1[r]);
-    }
-  }
-  float mx = kNegInf;
-#pragma unroll
-  for (int r = 0; r < kS; ++r)
-    if (r < S) mx = fmaxf(mx, lse2[r]);   // -inf stays -inf (multiplier > 0)
-  float w[kS];
-  float wsum = 0.f;
-#pragma unroll
-  for (int r = 0; r < kS; ++r) {
-    if (r < S) {
-      w[r] = mx == kNegInf ? 0.f : __builtin_amdgcn_exp2f(lse2[r] - mx);
-      wsum += w[r];
-    }
-  }
-  const bool any = wsum > 0.f;
-  const float inv = any ? 1.f / wsum : 0.f;
-
-  for (int e0 = e_first; e0 < p.dv; e0 += 512) {
-    if (e0 != e_first) {
-#pragma unroll
-      for (int r = 0; r < kS; ++r)
-        if (r < S) load8(p, r, vec * p.dv + e0, x0[r], x1[r]);
-    }
-    f32x4_t a0 = f32x4_t{}, a1 = f32x4_t{};
+  for (int u = 0; u < kV; ++u) {
+    const long long vec = vec0 + u < p.vectors ? vec0 + u : p.vectors - 1;
 #pragma unroll
     for (int r = 0; r < kS; ++r) {
-      if (r < S && w[r] != 0.f) {
-        a0 += w[r] * x0[r];
-        a1 += w[r] * x1[r];
+      if (r < S) {
+        lse2[u][r] = *(const __attribute__((address_space(4))) float*)(p.lses[r] + vec) * p.lse_to_log2[r];
+        if (have) load8(p, r, vec * p.dv + e_first, x0[u][r], x1[u][r]);
       }
-    }
-    a0 *= inv;
-    a1 *= inv;
-    if (p.out_bf16) {
-      bf16x8_t y;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        y[k] = (__bf16)a0[k];
-        y[4 + k] = (__bf16)a1[k];
-      }
-      *(bf16x8_t*)((__bf16*)p.out + vec * p.dv + e0) = y;
-    } else {
-      f32x4_t* y = (f32x4_t*)((float*)p.out + vec * p.dv + e0);
-      y[0] = a0;
-      y[1] = a1;
     }
   }
-  if (lane == 0 && p.lse_out != nullptr) {
-    const float l2 = any ? mx + __builtin_amdgcn_logf(wsum) : kNegInf;
-    p.lse_out[vec] = l2 * p.lse_out_from_log2;
+#pragma unroll
+  for (int u = 0; u < kV; ++u) {
+    const long long vec = vec0 + u;
+    if (vec >= p.vectors) break;
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < kS; ++r)
+      if (r < S) mx = fmaxf(mx, lse2[u][r]);   // -inf stays -inf (multiplier > 0)
+    float w[kS];
+    float wsum = 0.f;
+#pragma unroll
+    for (int r = 0; r < kS; ++r) {
+      if (r < S) {
+        w[r] = mx == kNegInf ? 0.f : __builtin_amdgcn_exp2f(lse2[u][r] - mx);
+        wsum += w[r];
+      }
+    }
+    const bool any = wsum > 0.f;
+    const float inv = any ? 1.f / wsum : 0.f;
+
+    for (int e0 = e_first; e0 < p.dv; e0 += 512) {
+      if (e0 != e_first) {
+#pragma unroll
+        for (int r = 0; r < kS; ++r)
+          if (r < S) load8(p, r, vec * p.dv + e0, x0[u][r], x1[u][r]);
+      }
+      f32x4_t a0 = f32x4_t{}, a1 = f32x4_t{};
+#pragma unroll
+      for (int r = 0; r < kS; ++r) {
+        if (r < S && w[r] != 0.f) {
+          a0 += w[r] * x0[u][r];
+          a1 += w[r] * x1[u][r];
+        }
+      }
+      a0 *= inv;
+      a1 *= inv;
+      if (p.out_bf16) {
+        bf16x8_t y;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          y[k] = (__bf16)a0[k];
+          y[4 + k] = (__bf16)a1[k];
+        }
+        store_stream((bf16x8_t*)((__bf16*)p.out + vec * p.dv + e0), y);
+      } else {
+        f32x4_t* y = (f32x4_t*)((float*)p.out + vec * p.dv + e0);
+        store_stream(y, a0);
+        store_stream(y + 1, a1);
+      }
+    }
+    if (lane == 0 && p.lse_out != nullptr) {
+      const float l2 = any ? mx + __builtin_amdgcn_logf(wsum) : kNegInf;
+      p.lse_out[vec] = l2 * p.lse_out_from_log2;
+    }
   }
 }
 
@@ -142,16 +173,20 @@ __global__ __launch_bounds__(256) void metadata_kernel(const int32_t* seq_lens, 
 
 }  // namespace
 
-hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
+hipError_t launch_merge(const MergeParams& p, hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream) {
   if (p.vectors == 0) return hipSuccess;
-  const long long blocks = (p.vectors + 3) / 4;
-  const dim3 grid((unsigned)blocks), block(256);
-  if (p.num_shards <= 1) hipLaunchKernelGGL(merge_kernel<1>, grid, block, 0, stream, p);
-  else if (p.num_shards <= 2) hipLaunchKernelGGL(merge_kernel<2>, grid, block, 0, stream, p);
-  else if (p.num_shards <= 4) hipLaunchKernelGGL(merge_kernel<4>, grid, block, 0, stream, p);
-  else if (p.num_shards <= 8) hipLaunchKernelGGL(merge_kernel<8>, grid, block, 0, stream, p);
-  else hipLaunchKernelGGL(merge_kernel<16>, grid, block, 0, stream, p);
-  return hipGetLastError();
+  // more than 8 shards: one vector per wave (registers)
+  const int vpw = p.num_shards <= 8 ? kMergeVecsPerWave : 1;
+  const long long blocks = (p.vectors + kMergeWaves * vpw - 1) / (kMergeWaves * vpw);
+  const void* fn;
+  if (p.num_shards <= 1) fn = reinterpret_cast<const void*>(&merge_kernel<1, kMergeVecsPerWave>);
+  else if (p.num_shards <= 2) fn = reinterpret_cast<const void*>(&merge_kernel<2, kMergeVecsPerWave>);
+  else if (p.num_shards <= 4) fn = reinterpret_cast<const void*>(&merge_kernel<4, kMergeVecsPerWave>);
+  else if (p.num_shards <= 8) fn = reinterpret_cast<const void*>(&merge_kernel<8, kMergeVecsPerWave>);
+  else fn = reinterpret_cast<const void*>(&merge_kernel<16, 1>);
+  // the events, when given, take the kernel's own dispatch start and end
+  void* args[] = {const_cast<MergeParams*>(&p)};
+  return hipExtLaunchKernel(fn, dim3((unsigned)blocks), dim3(64 * kMergeWaves), args, 0, stream, ev_begin, ev_end, 0);
 }
 
 hipError_t launch_metadata(const int32_t* seq_lens, const int32_t* block_table, int32_t batch,

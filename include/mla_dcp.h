@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+#define MLA_ABI_VERSION 2
 #define MLA_PAGE_SIZE 64
 #define MLA_D_QK 576
 #define MLA_D_V 512
@@ -201,6 +201,10 @@ typedef struct mla_merge_args {
   mla_dtype_t out_dtype;
   float* lse_out;
   mla_lse_base_t lse_out_base;
+  /* optional hipEvent_t pair (created with timing) that receive the start
+   * and end times of the merge kernel's dispatch (NULL = none) */
+  void* event_begin;
+  void* event_end;
 } mla_merge_args_t;
 
 mla_status_t mla_merge_partials(const mla_merge_args_t* args, void* stream);
