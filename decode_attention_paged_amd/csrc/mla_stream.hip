@@ -919,13 +919,12 @@ __device__ __forceinline__ void load_entries(const DecodeParams& p, const Cursor
   }
 }
 
-// Source row of token 8 w + (lane >> 3) of the cursor's tile (valid: the
-// tile exists in this workgroup's range).
+// Source row of token 8 w + (lane >> 3) of the cursor's tile for copying
+// wave w (valid: the tile exists in this workgroup's range).
 template <bool kLocal>
 __device__ __forceinline__ const uint8_t* token_src(const DecodeParams& p, const Cursor& c, bool valid,
-                                                    const TileEntries& te) {
+                                                    const TileEntries& te, int wave) {
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tk = lane >> 3;
   const int j = c.tile * kTile + 8 * wave + tk;
   const uint8_t* zero = reinterpret_cast<const uint8_t*>(g_const_rows.zero);
@@ -961,9 +960,8 @@ __device__ __forceinline__ const uint8_t* token_src(const DecodeParams& p, const
 // j = 0 moves the eight rope tails of the wave's tokens, j = 1 + i the 1 KB
 // main part of token 8 w + i (one row per copy, as a scalar base).
 template <int kJ>
-__device__ __forceinline__ void copy_tile_part(const uint8_t* src, uint32_t stage_lds) {
+__device__ __forceinline__ void copy_tile_part(const uint8_t* src, uint32_t stage_lds, int wave) {
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if constexpr (kJ == 0) {
     lds_dma16(src + 16 * (64 + ((lane & 7) ^ chunk_swz(lane >> 3))),
               __builtin_amdgcn_readfirstlane(stage_lds + kRopeBase + 1024 * wave));
@@ -977,17 +975,17 @@ __device__ __forceinline__ void copy_tile_part(const uint8_t* src, uint32_t stag
                     __builtin_amdgcn_readfirstlane(stage_lds + 1024 * (8 * wave + i)));
   }
 }
-__device__ __forceinline__ void copy_tile_part_rt(int j, const uint8_t* src, uint32_t stage_lds) {
+__device__ __forceinline__ void copy_tile_part_rt(int j, const uint8_t* src, uint32_t stage_lds, int wave) {
   switch (j) {
-    case 0: copy_tile_part<0>(src, stage_lds); break;
-    case 1: copy_tile_part<1>(src, stage_lds); break;
-    case 2: copy_tile_part<2>(src, stage_lds); break;
-    case 3: copy_tile_part<3>(src, stage_lds); break;
-    case 4: copy_tile_part<4>(src, stage_lds); break;
-    case 5: copy_tile_part<5>(src, stage_lds); break;
-    case 6: copy_tile_part<6>(src, stage_lds); break;
-    case 7: copy_tile_part<7>(src, stage_lds); break;
-    default: copy_tile_part<8>(src, stage_lds); break;
+    case 0: copy_tile_part<0>(src, stage_lds, wave); break;
+    case 1: copy_tile_part<1>(src, stage_lds, wave); break;
+    case 2: copy_tile_part<2>(src, stage_lds, wave); break;
+    case 3: copy_tile_part<3>(src, stage_lds, wave); break;
+    case 4: copy_tile_part<4>(src, stage_lds, wave); break;
+    case 5: copy_tile_part<5>(src, stage_lds, wave); break;
+    case 6: copy_tile_part<6>(src, stage_lds, wave); break;
+    case 7: copy_tile_part<7>(src, stage_lds, wave); break;
+    default: copy_tile_part<8>(src, stage_lds, wave); break;
   }
 }
 
@@ -1057,12 +1055,12 @@ void attn_pipe_kernel(DecodeParams p) {
     TileEntries te0, te1;
     load_entries<kLocal>(p, cc, wave, te0);
     if (1 < Uw) load_entries<kLocal>(p, cl, wave, te1);
-    const uint8_t* src0 = token_src<kLocal>(p, cc, true, te0);
+    const uint8_t* src0 = token_src<kLocal>(p, cc, true, te0, wave);
 #pragma unroll
-    for (int j = 0; j < kCopies; ++j) copy_tile_part_rt(j, src0, smem_lds);
-    const uint8_t* src1 = token_src<kLocal>(p, cl, 1 < Uw, te1);
+    for (int j = 0; j < kCopies; ++j) copy_tile_part_rt(j, src0, smem_lds, wave);
+    const uint8_t* src1 = token_src<kLocal>(p, cl, 1 < Uw, te1, wave);
 #pragma unroll
-    for (int j = 0; j < kCopies; ++j) copy_tile_part_rt(j, src1, smem_lds + kStageBytes);
+    for (int j = 0; j < kCopies; ++j) copy_tile_part_rt(j, src1, smem_lds + kStageBytes, wave);
   }
   int ncopied = 2;
   TileEntries te;   // entries of tile ncopied, loaded a barrier ahead
@@ -1080,7 +1078,7 @@ void attn_pipe_kernel(DecodeParams p) {
   auto tile_barrier = [&]() {
     wait_vmcnt<kCopies>();
     __syncthreads();
-    csrc = token_src<kLocal>(p, cl, ncopied < Uw, te);
+    csrc = token_src<kLocal>(p, cl, ncopied < Uw, te, wave);
     cst = __builtin_amdgcn_readfirstlane(smem_lds + kStageBytes * (ncopied & (kNS - 1)));
     ++ncopied;
     if (ncopied < Uw) {
@@ -1092,7 +1090,7 @@ void attn_pipe_kernel(DecodeParams p) {
   // iteration's tile goes out after MFMA copy_slot(j).
   constexpr int kSlots = kKS + kPvSteps;
   auto after_mfma = [&](int m) {
-    if (copy_at_slot(m, kSlots, kCopies) >= 0) copy_tile_part_rt(copy_at_slot(m, kSlots, kCopies), csrc, cst);
+    if (copy_at_slot(m, kSlots, kCopies) >= 0) copy_tile_part_rt(copy_at_slot(m, kSlots, kCopies), csrc, cst, wave);
   };
   // scores: S^T of a tile over this wave's k-steps, one MFMA per step, K
   // operands read kAhead steps ahead
@@ -1432,6 +1430,410 @@ void attn_pipe_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// warp-specialised attention over bf16 KV (64-row blocks)
+// ---------------------------------------------------------------------------
+// Eight waves, two per SIMD, in two roles (a second wave per SIMD to issue
+// from while one waits on LDS; the register file holds both):
+//  * waves 0..3 compute scores: wave (rg, ds) forms the partial S^T of row
+//    group rg over half ds of the 576 QK dims; the ds = 1 wave hands its
+//    partial to its partner through LDS, and the ds = 0 wave adds the two,
+//    runs the online softmax (split into chunks between the next tile's
+//    score MFMAs) and writes P (bf16, in the B-operand order of the PV
+//    MFMAs) into the rope part of that tile's stage, which no wave reads
+//    any more, with each row's rescale factor;
+//  * waves 4..7 hold the output: wave 4 + q accumulates O^T for dims
+//    128 q .. 128 q + 127 of all 64 rows (each V element is read from LDS
+//    once per workgroup) and issues the tile copies (nine per barrier, so
+//    the wait before each barrier is a constant vmcnt(9)).
+// Tile i: barrier (tile i landed; copies of tile i + 2 go out) -> scores of
+// tile i with the softmax of tile i - 1 | barrier | P V of tile i - 1.
+constexpr int kWsRows = 64;
+constexpr int kWsStagePitch = 272;     // output staging row: 128 bf16 + 16 bytes
+
+template <bool kLocal>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_ws_kernel(DecodeParams p) {
+  constexpr int kNS = 4;
+  constexpr int kCopies = 9;
+  constexpr int kG = 2;                 // k-steps per 32-dim group of a score wave
+  constexpr int kKS = 18;               // score MFMAs per wave and tile
+  constexpr int kAhead = 4;
+  constexpr int kChunks = 9;            // softmax chunks between score MFMAs
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * kStageBytes];
+  __shared__ __attribute__((aligned(16))) f32x4_t xbuf[2 * 4 * 64];   // [rg][4][lane]
+  __shared__ float fbuf[2 * kWsRows];   // [tile parity][row]: rescale factor of the tile's P
+  __shared__ float lbuf[kWsRows];       // row sums at the end of a piece
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tok = lane & 31, hi = lane >> 5;
+
+  int g = blockIdx.x;
+  if ((p.grid & 7) == 0) g = (blockIdx.x & 7) * (p.grid >> 3) + (blockIdx.x >> 3);
+  const int32_t* rec = p.wg_rec + (long long)g * kRecInts;
+  const int Uw = ld_const(rec);
+  const int rec_seg = ld_const(rec + 1), rec_tile = ld_const(rec + 2), rec_cnt = ld_const(rec + 3);
+  const int rec_seg1 = ld_const(rec + 4), rec_cnt1 = ld_const(rec + 5);
+  if (Uw <= 0) return;
+  const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_address(smem));
+  // P^T of row group r, token half m: 16 bytes per lane at
+  // kRopeBase + 2048 r + 64 row + 16 ((2 m + hi) ^ ((row >> 2) & 3))
+  const uint32_t poff = (uint32_t)(kRopeBase + 64 * tok);
+  const int pswz = (tok >> 2) & 3;
+
+  if (wave < 4) {
+    // ------------------------------------------------------------ scores
+    const int rg = wave & 1, ds = wave >> 1;
+    const uint32_t qk0 = (uint32_t)(1024 * tok + 16 * ((2 * kG * ds) ^ hi ^ chunk_swz(tok)));
+    const uint32_t rope0 = (uint32_t)(kRopeBase + 128 * tok + 16 * ((2 * kG * ds) ^ hi ^ chunk_swz(tok)));
+    Cursor cc;
+    cc.start_known(p, rec_seg, rec_tile, rec_cnt);
+    bf16x8_t qreg[kKS];
+    bf16x8_t ka[kAhead];
+    f32x16_t acc;
+    auto qk_start = [&](const uint8_t* ks) {
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u) ka[u] = qk_operand<kG>(ks, qk0, rope0, u);
+      acc = f32x16_t{};
+    };
+    auto qk_step = [&](const uint8_t* ks, int i) {
+      const bf16x8_t a = ka[i % kAhead];
+      if (i + kAhead < kKS) ka[i % kAhead] = qk_operand<kG>(ks, qk0, rope0, i + kAhead);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[i], acc, 0, 0, 0);
+    };
+    f32x4_t* xmine = xbuf + (rg * 4) * 64 + lane;
+
+    int t = 0;
+    while (t < Uw) {
+      const int b = cc.b, rb = cc.rb, tile0 = cc.tile, ntiles = cc.ntiles, cnt = cc.cnt;
+      const int n = min(ntiles - tile0, Uw - t);
+      const int row = rb * kWsRows + rg * 32 + tok;
+      const bool row_ok = row < p.rows;
+      {
+        const uint16_t* qrow = p.q + ((long long)b * p.rows + (row_ok ? row : 0)) * kDqk + 8 * hi;
+#pragma unroll
+        for (int i = 0; i < kKS; ++i) {
+          const int kk = 4 * (i / kG) + kG * ds + i % kG;
+          const bf16x8_t x = *(const bf16x8_t*)(qrow + 16 * kk);
+          qreg[i] = row_ok ? x : bf16x8_t{};
+        }
+      }
+      wait_vmcnt<0>();
+      // owned tokens row (draft i) may see: t = j S + r <= L - q_len + i
+      int jvis = 0;
+      {
+        int L = ld_const(p.seq_lens + b);
+        L = L < 0 ? 0 : min(L, p.max_pages * kPage);
+        const int i = (row >= p.heads) + (row >= 2 * p.heads) + (row >= 3 * p.heads);
+        for (int k = 0; k < p.q_len; ++k) {
+          const int lim = L - p.q_len + k - p.shard;
+          const int jl = lim >= 0 ? min(cnt, lim / p.num_shards + 1) : 0;
+          jvis = i == k ? jl : jvis;
+        }
+      }
+      float m_ref = kNegInf, l_sum = 0.f;
+      // online softmax of a tile in base 2 (lane: one row, 16 tokens; value
+      // v is token 8 (v >> 2) + 4 hi + (v & 3)); tokens at or past the row's
+      // visibility limit are masked; the max is taken on the raw scores and
+      // the scale folded into the exponent's FMA. Chunks 0 and 1 mask and
+      // take the max (and move the reference), the rest exponentiate.
+      float f = 1.f, tmax = kNegInf, neg_m = 0.f;
+      int lim = 0;
+      auto softmax_chunk = [&](int c, int k, f32x16_t& sc, bf16x8_t (&pb)[2]) {
+        if (c == 0) {
+          lim = jvis - (tile0 + k) * kTile - 4 * hi;
+          tmax = kNegInf;
+        }
+        if (c < 2) {
+#pragma unroll
+          for (int v = 8 * c; v < 8 * c + 8; ++v) {
+            const int cc_ = 8 * (v >> 2) + (v & 3);
+            sc[v] = cc_ < lim ? sc[v] : kNegInf;
+            tmax = fmaxf(tmax, sc[v]);
+          }
+        }
+        if (c == 1) {
+          const float tm = xor32_max(tmax) * p.scale_log2;
+          const bool grow = m_ref != kNegInf && tm > m_ref + kRescaleSlack;
+          f = grow ? exp2_fast(m_ref - tm) : 1.f;
+          l_sum *= f;
+          m_ref = grow || m_ref == kNegInf ? tm : m_ref;
+          neg_m = m_ref == kNegInf ? 0.f : -m_ref;
+        }
+        if (c >= 2) {
+          constexpr int kE = kChunks - 2;
+          const int v0 = (c - 2) * 16 / kE, v1 = (c - 1) * 16 / kE;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            if (v >= v0 && v < v1) {
+              const float pr = exp2_fast(__builtin_fmaf(sc[v], p.scale_log2, neg_m));
+              l_sum += pr;
+              pb[v >> 3][v & 7] = (__bf16)pr;
+            }
+          }
+        }
+      };
+      // P of tile u into the rope part of its stage, and the row's factor
+      auto write_p = [&](int u, const bf16x8_t (&pb)[2]) {
+        uint8_t* st = smem + kStageBytes * (u & (kNS - 1)) + poff + 2048 * rg;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) *(bf16x8_t*)(st + 16 * ((2 * m + hi) ^ pswz)) = pb[m];
+        if (hi == 0) fbuf[(u & 1) * kWsRows + rg * 32 + tok] = f;
+      };
+      auto partner_sum = [&]() {
+        f32x16_t r;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4_t v = xmine[64 * q];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r[4 * q + e] = acc[4 * q + e] + v[e];
+        }
+        return r;
+      };
+
+      f32x16_t s_cur;
+      // tile 0: its scores
+      __syncthreads();   // tile t landed
+      {
+        const uint8_t* ksq = smem + kStageBytes * (t & (kNS - 1));
+        qk_start(ksq);
+#pragma unroll
+        for (int i = 0; i < kKS; ++i) qk_step(ksq, i);
+        if (ds == 1) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) xmine[64 * q] = f32x4_t{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+        }
+      }
+      __syncthreads();   // partials exchanged
+      if (ds == 0) s_cur = partner_sum();
+      for (int k = 0; k + 1 < n; ++k) {
+        __syncthreads();   // tile t + k + 1 landed
+        const uint8_t* ksq = smem + kStageBytes * ((t + k + 1) & (kNS - 1));
+        qk_start(ksq);
+        if (ds == 0) {
+          bf16x8_t pb[2];
+#pragma unroll
+          for (int i = 0; i < kKS; ++i) {
+            qk_step(ksq, i);
+            if (i % 2 == 1) softmax_chunk(i / 2, k, s_cur, pb);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          write_p(t + k, pb);
+        } else {
+#pragma unroll
+          for (int i = 0; i < kKS; ++i) qk_step(ksq, i);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) xmine[64 * q] = f32x4_t{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+        }
+        __syncthreads();   // P of tile t + k and the partials exchanged
+        if (ds == 0) s_cur = partner_sum();
+      }
+      // the last tile's softmax; row sums and LSE of the piece
+      const bool single = tile0 == 0 && n == ntiles;
+      if (ds == 0) {
+        bf16x8_t pb[2];
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) softmax_chunk(c, n - 1, s_cur, pb);
+        write_p(t + n - 1, pb);
+        const float l_tot = xor32_sum(l_sum);
+        if (hi == 0) lbuf[rg * 32 + tok] = l_tot;
+        const bool any = l_tot > 0.f || l_tot != l_tot;
+        const float lse2 = any ? m_ref + log2_fast(l_tot) : kNegInf;
+        if (row_ok && hi == 0) {
+          if (single) {
+            p.lse[(long long)b * p.rows + row] = p.lse_base2 ? lse2 : lse2 * kLn2;
+          } else {
+            const int4 si = ld_const(p.seg_info + b * p.row_blocks + rb);
+            p.spart_lse[(long long)(si.x + g - si.z) * kWsRows + (row - rb * kWsRows)] = lse2;
+          }
+        }
+      }
+      __syncthreads();   // P of the last tile and the row sums written
+      __syncthreads();   // every output wave is done with the stages
+      t += n;
+      if (t < Uw) {
+        cc.tile = ntiles - 1;
+        cc.advance(p);
+      }
+    }
+    wait_vmcnt<0>();
+  } else {
+    // ------------------------------------------------------------ output
+    const int wq = wave - 4;
+    uint32_t pv0;
+    {
+      const int g16 = lane >> 4, r4 = (lane >> 2) & 3, q4 = lane & 3;
+      const int tl = 4 * (g16 >> 1) + r4;
+      const int y = 2 * (g16 & 1) + (q4 >> 1);
+      pv0 = (uint32_t)(1024 * tl + 16 * (y ^ chunk_swz(tl)) + 8 * (q4 & 1) + 256 * wq);
+    }
+    Cursor cc, cl;
+    cc.start_known(p, rec_seg, rec_tile, rec_cnt);
+    cl = cc;
+    if (1 < Uw) {
+      if (cl.tile + 1 < cl.ntiles) ++cl.tile;
+      else cl.start_known(p, rec_seg1, 0, rec_cnt1);
+    }
+    {
+      TileEntries te0, te1;
+      load_entries<kLocal>(p, cc, wq, te0);
+      if (1 < Uw) load_entries<kLocal>(p, cl, wq, te1);
+      const uint8_t* src0 = token_src<kLocal>(p, cc, true, te0, wq);
+#pragma unroll
+      for (int j = 0; j < kCopies; ++j) copy_tile_part_rt(j, src0, smem_lds, wq);
+      const uint8_t* src1 = token_src<kLocal>(p, cl, 1 < Uw, te1, wq);
+#pragma unroll
+      for (int j = 0; j < kCopies; ++j) copy_tile_part_rt(j, src1, smem_lds + kStageBytes, wq);
+    }
+    int ncopied = 2;
+    TileEntries te;
+    if (2 < Uw) {
+      cl.advance(p);
+      load_entries<kLocal>(p, cl, wq, te);
+    }
+    // tile barrier: the next scores' tile has landed in every wave and the
+    // stage of the tile two back is free: the copies of tile ncopied go out
+    auto tile_barrier = [&]() {
+      wait_vmcnt<kCopies>();
+      __syncthreads();
+      const uint8_t* csrc = token_src<kLocal>(p, cl, ncopied < Uw, te, wq);
+      const uint32_t cst = __builtin_amdgcn_readfirstlane(smem_lds + kStageBytes * (ncopied & (kNS - 1)));
+#pragma unroll
+      for (int j = 0; j < kCopies; ++j) copy_tile_part_rt(j, csrc, cst, wq);
+      ++ncopied;
+      if (ncopied < Uw) {
+        cl.advance(p);
+        load_entries<kLocal>(p, cl, wq, te);
+      }
+    };
+    f32x16_t o[4][2];
+    bf16x8_t va[8];
+    auto load_v = [&](const uint8_t* ks) {
+#pragma unroll
+      for (int st = 0; st < 8; ++st) va[st] = pv_operand(ks, pv0, st);
+    };
+    // O^T[dim][row] += V^T[dim][token] P^T[token][row] for both row groups,
+    // after the rows' rescale (f = 1 unless the reference moved)
+    auto pv_tile = [&](const uint8_t* ks, int u) {
+      const float f0 = fbuf[(u & 1) * kWsRows + tok];
+      const float f1 = fbuf[(u & 1) * kWsRows + 32 + tok];
+      bf16x8_t pp[2][2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          pp[r][m] = *(const bf16x8_t*)(ks + poff + 2048 * r + 16 * ((2 * m + hi) ^ pswz));
+      if (__builtin_expect(__ballot(f0 != 1.f) != 0, 0)) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db][0] *= f0;
+      }
+      if (__builtin_expect(__ballot(f1 != 1.f) != 0, 0)) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db][1] *= f1;
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 2; ++r)
+            o[db][r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[2 * db + m], pp[r][m], o[db][r], 0, 0, 0);
+    };
+
+    int t = 0;
+    while (t < Uw) {
+      const int b = cc.b, rb = cc.rb, tile0 = cc.tile, ntiles = cc.ntiles;
+      const int n = min(ntiles - tile0, Uw - t);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) o[db][r] = f32x16_t{};
+      tile_barrier();    // tile t landed
+      __syncthreads();   // partials exchanged
+      for (int k = 0; k + 1 < n; ++k) {
+        tile_barrier();  // tile t + k + 1 landed
+        const uint8_t* ksv = smem + kStageBytes * ((t + k) & (kNS - 1));
+        load_v(ksv);
+        __syncthreads();   // P of tile t + k written
+        pv_tile(ksv, t + k);
+      }
+      {
+        const uint8_t* ksv = smem + kStageBytes * ((t + n - 1) & (kNS - 1));
+        load_v(ksv);
+        __syncthreads();   // P of the last tile and the row sums written
+        pv_tile(ksv, t + n - 1);
+      }
+      const float l0 = lbuf[tok], l1 = lbuf[32 + tok];
+      __syncthreads();   // every output wave is done with the stages
+      // epilogue: lane l holds rows r * 32 + (l & 31); o[db][r][v] is dim
+      // 128 wq + 32 db + 8 (v >> 2) + 4 hi + (v & 3)
+      float inv[2];
+      {
+        const bool a0 = l0 > 0.f || l0 != l0, a1 = l1 > 0.f || l1 != l1;
+        inv[0] = a0 ? p.out_scale / l0 : 0.f;
+        inv[1] = a1 ? p.out_scale / l1 : 0.f;
+      }
+      const bool single = tile0 == 0 && n == ntiles;
+      const int row0 = rb * kWsRows;
+      if (single && !p.out_bf16) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int row = row0 + r * 32 + tok;
+          if (row < p.rows) {
+            float* dst = (float*)p.out + ((long long)b * p.rows + row) * kDv + 128 * wq + 4 * hi;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const f32x4_t x = {o[db][r][4 * q] * inv[r], o[db][r][4 * q + 1] * inv[r],
+                                   o[db][r][4 * q + 2] * inv[r], o[db][r][4 * q + 3] * inv[r]};
+                *(f32x4_t*)(dst + 32 * db + 8 * q) = x;
+              }
+          }
+        }
+      } else {
+        // bf16 rows through LDS (the stages of the piece's last two tiles are
+        // free): 64 rows x 128 dims per wave, stored 16 bytes a lane
+        uint8_t* sb = smem + kStageBytes * ((t + n - 1 - (wq >> 1)) & (kNS - 1)) + (wq & 1) * (kWsRows * kWsStagePitch);
+        typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const bf16x4_t x = {(__bf16)(o[db][r][4 * q] * inv[r]), (__bf16)(o[db][r][4 * q + 1] * inv[r]),
+                                  (__bf16)(o[db][r][4 * q + 2] * inv[r]), (__bf16)(o[db][r][4 * q + 3] * inv[r])};
+              *(bf16x4_t*)(sb + kWsStagePitch * (r * 32 + tok) + 2 * (32 * db + 8 * q + 4 * hi)) = x;
+            }
+        __bf16* obase;
+        if (single) {
+          obase = (__bf16*)p.out + ((long long)b * p.rows + row0) * kDv;
+        } else {
+          const int4 si = ld_const(p.seg_info + b * p.row_blocks + rb);
+          obase = (__bf16*)p.spart_o + ((long long)(si.x + g - si.z) * kWsRows) * kDv;
+        }
+        const int rr0 = lane >> 4, c16 = lane & 15;
+#pragma unroll
+        for (int i = 0; i < kWsRows / 4; ++i) {
+          const int rr = 4 * i + rr0;
+          const bf16x8_t x = *(const bf16x8_t*)(sb + kWsStagePitch * rr + 16 * c16);
+          if (row0 + rr < p.rows) *(bf16x8_t*)(obase + (long long)rr * kDv + 128 * wq + 8 * c16) = x;
+        }
+      }
+      t += n;
+      if (t < Uw) {
+        cc.tile = ntiles - 1;
+        cc.advance(p);
+      }
+    }
+    // no copy may still be writing this workgroup's LDS when it exits
+    wait_vmcnt<0>();
+  }
+}
+
+// ---------------------------------------------------------------------------
 // combine the pieces of segments cut at workgroup boundaries; neutral rows
 // for requests with no owned token
 // ---------------------------------------------------------------------------
@@ -1490,6 +1892,9 @@ __global__ __launch_bounds__(256) void stream_combine_kernel(DecodeParams p) {
 
 }  // namespace
 
+// 64-row blocks of bf16 KV run the warp-specialised kernel
+constexpr bool kUseWs = true;
+
 hipError_t launch_decode_stream(const DecodeParams& p, hipEvent_t ev_begin, hipEvent_t ev_end,
                                 hipStream_t stream) {
   if (p.batch == 0) return hipSuccess;
@@ -1504,11 +1909,14 @@ hipError_t launch_decode_stream(const DecodeParams& p, hipEvent_t ev_begin, hipE
                                       : reinterpret_cast<const void*>(&attn_stream_kernel<2, true>);
   else if (p.local_kv_indices != nullptr)
     fn = p.rows_blk == 32 ? reinterpret_cast<const void*>(&attn_pipe_kernel<4, true>)
+         : kUseWs         ? reinterpret_cast<const void*>(&attn_ws_kernel<true>)
                           : reinterpret_cast<const void*>(&attn_pipe_kernel<2, true>);
   else
     fn = p.rows_blk == 32 ? reinterpret_cast<const void*>(&attn_pipe_kernel<4, false>)
+         : kUseWs         ? reinterpret_cast<const void*>(&attn_ws_kernel<false>)
                           : reinterpret_cast<const void*>(&attn_pipe_kernel<2, false>);
-  err = hipExtLaunchKernel(fn, dim3(p.grid), dim3(256), args, 0, stream, ev_begin, ev_end, 0);
+  const bool ws = kUseWs && !p.kv_fp8 && p.rows_blk == kWsRows;
+  err = hipExtLaunchKernel(fn, dim3(p.grid), dim3(ws ? 512 : 256), args, 0, stream, ev_begin, ev_end, 0);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(stream_combine_kernel, dim3(p.batch, (p.rows + 3) / 4), dim3(256), 0, stream, p);
   return hipGetLastError();
