@@ -3,8 +3,10 @@
 
 A step is one pass of the whole path over one batch: for each of the S
 shards the rank-local partial decode, then the LSE-weighted merge of the S
-partials. The shard-local metadata is built once per decode step (not per
-layer) and is timed separately (metadata_us_per_shard in the details). Inputs are synthetic (seeded, shaped
+partials. The shard-local metadata and each shard's work schedule
+(mla_decode_plan) are built once per decode step (not per layer) and are
+timed separately (metadata_us_per_shard, plan_us_per_shard in the details);
+every partial of the step reuses its shard's schedule. Inputs are synthetic (seeded, shaped
 like the pages' workloads) and already resident in HBM when timing starts;
 two copies of the KV pool and queries are alternated so the 256 MB
 Infinity Cache cannot serve repeated reads.
@@ -172,11 +174,24 @@ def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True, spl
         mdev[r][1].record()
     torch.cuda.synchronize()
     metadata_us = statistics.median(1e3 * a.elapsed_time(b) for a, b in mdev)
+    # so is each shard's work schedule (one per workspace, reused by every
+    # layer's partial decode): built and timed here, reused by the steps
+    bufs.per_shard_workspaces()
+    for r in range(S):
+        ST.run_plan(dws[0], bufs, r, split_target=split_target)
+    torch.cuda.synchronize()
+    for r in range(S):
+        mdev[r][0].record()
+        ST.run_plan(dws[0], bufs, r, split_target=split_target)
+        mdev[r][1].record()
+    torch.cuda.synchronize()
+    plan_us = statistics.median(1e3 * a.elapsed_time(b) for a, b in mdev)
 
     def one_step(k, timed):
         dw = dws[k % len(dws)]
         for r in range(S):
-            ST.run_partial(dw, bufs, r, split_target=split_target, events=ev[k][r] if timed else None)
+            ST.run_partial(dw, bufs, r, split_target=split_target, events=ev[k][r] if timed else None,
+                           reuse_plan=True)
         if timed:
             mev[k][0].record()
         ST.run_merge(dw, bufs)
@@ -206,17 +221,17 @@ def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True, spl
             streams = [torch.cuda.Stream() for _ in range(S)]
             graphs = []
             for dw in dws:
-                ST.run_step_concurrent(dw, bufs, streams)      # warm the path before capture
+                ST.run_step_concurrent(dw, bufs, streams, reuse_plan=True)   # warm the path before capture
                 torch.cuda.synchronize()
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g):
-                    ST.run_step_concurrent(dw, bufs, streams)
+                    ST.run_step_concurrent(dw, bufs, streams, reuse_plan=True)
                 graphs.append(g)
             torch.cuda.synchronize()
             for i, dw in enumerate(dws):
                 bufs.fill_nan()
                 for r in range(S):
-                    ST.run_partial(dw, bufs, r)
+                    ST.run_partial(dw, bufs, r, reuse_plan=True)
                 ST.run_merge(dw, bufs)
                 torch.cuda.synchronize()
                 ref_out, ref_lse = bufs.out.clone(), bufs.lse.clone()
@@ -259,7 +274,8 @@ def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True, spl
         attn_kernel_mean_us=1e3 * mean_launch_ms, attn_kernel_bytes_per_launch=tot_bytes / S,
         attn_kernel_gbs=achieved_gbs, attn_kernel_tflops=achieved_tflops,
         merge_us=1e3 * statistics.median(merge_ms), steps=steps, warmup=warmup, rotated=len(dws),
-        metadata_us_per_shard=metadata_us, step_timing=step_timing, eager_ms_per_step=eager_ms_step,
+        metadata_us_per_shard=metadata_us, plan_us_per_shard=plan_us, step_timing=step_timing,
+        eager_ms_per_step=eager_ms_step,
     )
     # the contraction runs on bf16 MFMAs for both KV types (fp8 pages are
     # converted to bf16 in LDS), so its peak is the bf16 one
@@ -440,8 +456,10 @@ def main() -> int:
     ds = 4 if wl.heads * wl.q_len <= 32 else 2
     if wl.kv_dtype == "fp8":
         kname = "attn_stream_kernel<%d, fp8> (mla_stream.hip)" % ds
+    elif ds == 2:
+        kname = "attn_ws_kernel<local indices> (mla_stream.hip)"
     else:
-        kname = "attn_pipe_kernel<%d, local indices> (mla_stream.hip)" % ds
+        kname = "attn_pipe_kernel<4, local indices> (mla_stream.hip)"
     roof["kernel"] = kname + ", mean of %d launches" % (args.steps * wl.shards)
     roof["mean_launch_us"] = res["attn_kernel_mean_us"]
     roof["algorithmic_bytes_per_launch"] = res["attn_kernel_bytes_per_launch"]
@@ -462,7 +480,9 @@ def main() -> int:
         "config": {"workload": f"{wl.name}: batch {wl.batch}, {wl.heads} heads, q_len {wl.q_len}, "
                                f"{wl.shards} cyclic shards, {wl.kv_dtype} KV, page 64, "
                                f"{res['tokens']} context tokens, partials + merge",
-                   "global_batch": wl.batch, "shards": wl.shards, "step": res["step_timing"]},
+                   "global_batch": wl.batch, "shards": wl.shards, "step": res["step_timing"],
+                   "per_decode_step": "shard metadata %.1f us + schedule %.1f us per shard, not in the step"
+                                      % (res["metadata_us_per_shard"], res["plan_us_per_shard"])},
         "tflops": round(res["tflops"], 3),
         "merge_us": {T: round(v["us_median"], 2) for T, v in merge.items()} if merge else None,
         "merge_kernel_us": {T: round(v["kernel_us_mean"], 2) for T, v in merge.items()} if merge else None,

@@ -56,6 +56,7 @@ class DecodeArgs(ctypes.Structure):
         ("split_target", ctypes.c_int32),
         ("event_begin", ctypes.c_void_p),
         ("event_end", ctypes.c_void_p),
+        ("reuse_plan", ctypes.c_int32),
     ]
 
 
@@ -78,7 +79,7 @@ class MergeArgs(ctypes.Structure):
     ]
 
 
-EXPORTS = ("mla_build_shard_metadata", "mla_decode_workspace_bytes", "mla_decode_partial",
+EXPORTS = ("mla_build_shard_metadata", "mla_decode_workspace_bytes", "mla_decode_partial", "mla_decode_plan",
            "mla_merge_partials", "mla_status_string", "mla_last_error", "mla_abi_version",
            "mla_sizeof_decode_args", "mla_sizeof_merge_args")
 
@@ -104,6 +105,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_decode_workspace_bytes.restype = sz
     lib.mla_decode_partial.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_int), vp]
     lib.mla_decode_partial.restype = ctypes.c_int
+    lib.mla_decode_plan.argtypes = [ctypes.POINTER(DecodeArgs), vp]
+    lib.mla_decode_plan.restype = ctypes.c_int
     lib.mla_merge_partials.argtypes = [ctypes.POINTER(MergeArgs), vp]
     lib.mla_merge_partials.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
@@ -175,19 +178,9 @@ def mla_decode_workspace_bytes(batch: int, num_heads: int, q_len: int) -> int:
     return int(load().mla_decode_workspace_bytes(int(batch), int(num_heads), int(q_len)))
 
 
-def mla_decode_partial(q, kv_pages, block_table, seq_lens, shard_id: int, num_shards: int, q_len: int,
-                       out, lse, workspace, *, kv_scale: float = 1.0, softmax_scale: float,
-                       lse_base: int = LSE_BASE_E, local_seq_lens=None, local_kv_indices=None,
-                       split_target: int = 0, events=None, stream=None) -> int:
-    """Rank-local (out, lse) of one shard; returns the LSE base written.
-
-    q [B, q_len, H, 576] bf16; kv_pages [P, 64, 576] bf16 or uint8 (e4m3);
-    block_table [B, max_pages] i32; seq_lens [B] i32; out [B, q_len, H, 512]
-    f32 or bf16; lse [B, q_len, H] f32; workspace uint8 of at least
-    mla_decode_workspace_bytes(B, H, q_len). ``events`` = optional pair of
-    torch.cuda.Event recorded around the attention kernel.
-    """
-    lib = load()
+def _decode_args(q, kv_pages, block_table, seq_lens, shard_id, num_shards, q_len, out, lse, workspace,
+                 kv_scale, softmax_scale, lse_base, local_seq_lens, local_kv_indices, split_target, events,
+                 reuse_plan):
     a = DecodeArgs()
     B, ql, H = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
     if ql != q_len:
@@ -206,9 +199,43 @@ def mla_decode_partial(q, kv_pages, block_table, seq_lens, shard_id: int, num_sh
     a.split_target = int(split_target)
     if events is not None:
         a.event_begin, a.event_end = int(events[0].cuda_event), int(events[1].cuda_event)
+    a.reuse_plan = 1 if reuse_plan else 0
+    return a
+
+
+def mla_decode_partial(q, kv_pages, block_table, seq_lens, shard_id: int, num_shards: int, q_len: int,
+                       out, lse, workspace, *, kv_scale: float = 1.0, softmax_scale: float,
+                       lse_base: int = LSE_BASE_E, local_seq_lens=None, local_kv_indices=None,
+                       split_target: int = 0, events=None, reuse_plan: bool = False, stream=None) -> int:
+    """Rank-local (out, lse) of one shard; returns the LSE base written.
+
+    q [B, q_len, H, 576] bf16; kv_pages [P, 64, 576] bf16 or uint8 (e4m3);
+    block_table [B, max_pages] i32; seq_lens [B] i32; out [B, q_len, H, 512]
+    f32 or bf16; lse [B, q_len, H] f32; workspace uint8 of at least
+    mla_decode_workspace_bytes(B, H, q_len). ``events`` = optional pair of
+    timing events recorded around the attention kernel. ``reuse_plan``: the
+    workspace holds the schedule mla_decode_plan built for the same inputs.
+    """
+    lib = load()
+    a = _decode_args(q, kv_pages, block_table, seq_lens, shard_id, num_shards, q_len, out, lse, workspace,
+                     kv_scale, softmax_scale, lse_base, local_seq_lens, local_kv_indices, split_target, events,
+                     reuse_plan)
     written = ctypes.c_int(-1)
     _check(lib.mla_decode_partial(ctypes.byref(a), ctypes.byref(written), _stream_ptr(stream)))
     return int(written.value)
+
+
+def mla_decode_plan(q, kv_pages, block_table, seq_lens, shard_id: int, num_shards: int, q_len: int,
+                    out, lse, workspace, *, kv_scale: float = 1.0, softmax_scale: float,
+                    lse_base: int = LSE_BASE_E, local_seq_lens=None, local_kv_indices=None,
+                    split_target: int = 0, stream=None) -> None:
+    """The work schedule of mla_decode_partial with the same arguments, into
+    ``workspace`` (built once per decode step, reused with reuse_plan)."""
+    lib = load()
+    a = _decode_args(q, kv_pages, block_table, seq_lens, shard_id, num_shards, q_len, out, lse, workspace,
+                     kv_scale, softmax_scale, lse_base, local_seq_lens, local_kv_indices, split_target, None,
+                     False)
+    _check(lib.mla_decode_plan(ctypes.byref(a), _stream_ptr(stream)))
 
 
 def mla_merge_partials(outs: Sequence, lses: Sequence, bases: Sequence[int], out, lse_out=None,

@@ -140,7 +140,12 @@ size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t q_le
   return mla::decode_workspace_layout(batch, num_heads * q_len).total;
 }
 
-mla_status_t mla_decode_partial(const mla_decode_args_t* a, mla_lse_base_t* lse_base_written, void* stream) {
+}  // extern "C"
+
+// Validates the arguments and fills the kernels' parameters; `launch` is
+// false when there is nothing to run (batch 0).
+static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams& p, bool& launch) {
+  launch = false;
   if (a == nullptr) return fail(MLA_STATUS_INVALID_ARGUMENT, "args is NULL");
   if (a->batch < 0) return fail(MLA_STATUS_INVALID_ARGUMENT, "batch must be >= 0 (got %d)", a->batch);
   if (a->num_heads < 16 || a->num_heads % 16 != 0)
@@ -171,6 +176,8 @@ mla_status_t mla_decode_partial(const mla_decode_args_t* a, mla_lse_base_t* lse_
     return fail(MLA_STATUS_INVALID_ARGUMENT, "local_seq_lens and local_kv_indices go together");
   if (a->local_kv_indices != nullptr && a->local_kv_stride < 1)
     return fail(MLA_STATUS_INVALID_ARGUMENT, "local_kv_stride must be >= 1 (got %d)", a->local_kv_stride);
+  if (a->reuse_plan != 0 && a->reuse_plan != 1)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "reuse_plan must be 0 or 1 (got %d)", a->reuse_plan);
   if (a->split_target < 0 || a->split_target > mla::kMaxGrid)
     return fail(MLA_STATUS_INVALID_ARGUMENT, "split_target must be in [0, %d] (got %d)", mla::kMaxGrid, a->split_target);
   if (a->batch > 0) {
@@ -181,12 +188,11 @@ mla_status_t mla_decode_partial(const mla_decode_args_t* a, mla_lse_base_t* lse_
   const mla::WorkspaceLayout w = mla::decode_workspace_layout(a->batch, rows);
   if (a->batch > 0 && a->workspace_bytes < w.total)
     return fail(MLA_STATUS_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", w.total, a->workspace_bytes);
-  if (lse_base_written) *lse_base_written = a->lse_base;
   if (a->batch == 0) return ok();
 
   int cus = 0;
   if (device_cus(&cus) != 0) return fail(MLA_STATUS_DEVICE_ERROR, "cannot query the current device");
-  mla::DecodeParams p{};
+  p = mla::DecodeParams{};
   p.q = (const uint16_t*)a->q;
   p.kv = (const uint8_t*)a->kv_pages;
   p.block_table = a->block_table;
@@ -224,16 +230,41 @@ mla_status_t mla_decode_partial(const mla_decode_args_t* a, mla_lse_base_t* lse_
   p.row_blocks = (rows + p.rows_blk - 1) / p.rows_blk;
   p.kv_fp8 = a->kv_dtype == MLA_DTYPE_FP8_E4M3;
   {
-    // one persistent workgroup per CU (a multiple of 8 so that the workgroup
-    // order can follow the XCDs) unless the caller fixes the count
-    int32_t grid = a->split_target > 0 ? a->split_target : ((cus + 7) / 8) * 8;
+    // one persistent workgroup per CU but one in 16 (a multiple of 8 so that
+    // the workgroup order can follow the XCDs) unless the caller fixes the
+    // count: the free CUs run the small kernels of concurrent shards (their
+    // combine) alongside, which shortens a step of concurrent partials
+    int32_t grid = a->split_target > 0 ? a->split_target : ((cus - cus / 16) / 8) * 8;
+    if (grid < 8) grid = 8;
     if (grid > mla::kMaxGrid) grid = mla::kMaxGrid;
     p.grid = grid;
   }
+  launch = true;
+  return ok();
+}
 
-  hipError_t err = mla::launch_decode_stream(p, (hipEvent_t)a->event_begin, (hipEvent_t)a->event_end,
-                                             (hipStream_t)stream);
+extern "C" {
+
+mla_status_t mla_decode_partial(const mla_decode_args_t* a, mla_lse_base_t* lse_base_written, void* stream) {
+  mla::DecodeParams p;
+  bool launch = false;
+  const mla_status_t st = prepare_decode(a, p, launch);
+  if (st != MLA_STATUS_OK) return st;
+  if (lse_base_written) *lse_base_written = a->lse_base;
+  if (!launch) return ok();
+  hipError_t err = mla::launch_decode_stream(p, a->reuse_plan == 0, (hipEvent_t)a->event_begin,
+                                             (hipEvent_t)a->event_end, (hipStream_t)stream);
   if (err != hipSuccess) return device_fail(err, "decode launch");
+  return ok();
+}
+
+mla_status_t mla_decode_plan(const mla_decode_args_t* a, void* stream) {
+  mla::DecodeParams p;
+  bool launch = false;
+  const mla_status_t st = prepare_decode(a, p, launch);
+  if (st != MLA_STATUS_OK || !launch) return st;
+  hipError_t err = mla::launch_decode_plan(p, (hipStream_t)stream);
+  if (err != hipSuccess) return device_fail(err, "plan launch");
   return ok();
 }
 

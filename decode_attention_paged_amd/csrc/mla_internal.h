@@ -86,7 +86,8 @@ hipError_t launch_metadata(const int32_t* seq_lens, const int32_t* block_table, 
                            int32_t max_pages, int32_t shard, int32_t num_shards,
                            int32_t* local_seq_lens, int32_t* local_kv_indices,
                            int32_t stride, hipStream_t stream);
-hipError_t launch_decode_stream(const DecodeParams& p, hipEvent_t ev_begin, hipEvent_t ev_end,
+hipError_t launch_decode_plan(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_stream(const DecodeParams& p, bool run_plan, hipEvent_t ev_begin, hipEvent_t ev_end,
                                 hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream);
 

@@ -1895,11 +1895,16 @@ __global__ __launch_bounds__(256) void stream_combine_kernel(DecodeParams p) {
 // 64-row blocks of bf16 KV run the warp-specialised kernel
 constexpr bool kUseWs = true;
 
-hipError_t launch_decode_stream(const DecodeParams& p, hipEvent_t ev_begin, hipEvent_t ev_end,
-                                hipStream_t stream) {
+hipError_t launch_decode_plan(const DecodeParams& p, hipStream_t stream) {
   if (p.batch == 0) return hipSuccess;
   hipLaunchKernelGGL(stream_plan_kernel, dim3(1), dim3(1024), 0, stream, p);
-  hipError_t err = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_stream(const DecodeParams& p, bool run_plan, hipEvent_t ev_begin, hipEvent_t ev_end,
+                                hipStream_t stream) {
+  if (p.batch == 0) return hipSuccess;
+  hipError_t err = run_plan ? launch_decode_plan(p, stream) : hipSuccess;
   if (err != hipSuccess) return err;
   // the events, when given, take the attention kernel's own start and end
   // times (recorded with the dispatch, no separate marker packets)

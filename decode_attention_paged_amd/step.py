@@ -93,16 +93,31 @@ def run_metadata(dw: DeviceWorkload, bufs: StepBuffers, shard: int, stream=None)
                                       stream=stream)
 
 
-def run_partial(dw: DeviceWorkload, bufs: StepBuffers, shard: int, use_metadata: bool = True,
-                split_target: int = 0, events=None, stream=None) -> int:
-    ws = bufs.workspaces[shard] if shard < len(bufs.workspaces) else bufs.workspace
-    return L.mla_decode_partial(
+def _workspace(bufs: StepBuffers, shard: int):
+    return bufs.workspaces[shard] if shard < len(bufs.workspaces) else bufs.workspace
+
+
+def run_plan(dw: DeviceWorkload, bufs: StepBuffers, shard: int, use_metadata: bool = True,
+             split_target: int = 0, stream=None) -> None:
+    """The shard's work schedule into its workspace (once per decode step)."""
+    L.mla_decode_plan(
         dw.q, dw.kv_pages, dw.block_table, dw.seq_lens, shard, dw.shards, dw.q_len,
-        bufs.outs[shard], bufs.lses[shard], ws, kv_scale=dw.kv_scale,
+        bufs.outs[shard], bufs.lses[shard], _workspace(bufs, shard), kv_scale=dw.kv_scale,
         softmax_scale=dw.softmax_scale, lse_base=dw.lse_base,
         local_seq_lens=bufs.local_seq_lens[shard] if use_metadata else None,
         local_kv_indices=bufs.local_kv_indices[shard] if use_metadata else None,
-        split_target=split_target, events=events, stream=stream)
+        split_target=split_target, stream=stream)
+
+
+def run_partial(dw: DeviceWorkload, bufs: StepBuffers, shard: int, use_metadata: bool = True,
+                split_target: int = 0, events=None, reuse_plan: bool = False, stream=None) -> int:
+    return L.mla_decode_partial(
+        dw.q, dw.kv_pages, dw.block_table, dw.seq_lens, shard, dw.shards, dw.q_len,
+        bufs.outs[shard], bufs.lses[shard], _workspace(bufs, shard), kv_scale=dw.kv_scale,
+        softmax_scale=dw.softmax_scale, lse_base=dw.lse_base,
+        local_seq_lens=bufs.local_seq_lens[shard] if use_metadata else None,
+        local_kv_indices=bufs.local_kv_indices[shard] if use_metadata else None,
+        split_target=split_target, events=events, reuse_plan=reuse_plan, stream=stream)
 
 
 def run_merge(dw: DeviceWorkload, bufs: StepBuffers, out_base: int = L.LSE_BASE_E, stream=None) -> None:
@@ -124,9 +139,10 @@ def run_step(dw: DeviceWorkload, bufs: StepBuffers, use_metadata: bool = True, s
 
 
 def run_step_concurrent(dw: DeviceWorkload, bufs: StepBuffers, streams, use_metadata: bool = True,
-                        out_base: int = L.LSE_BASE_E) -> None:
+                        out_base: int = L.LSE_BASE_E, reuse_plan: bool = False) -> None:
     """Partials of all shards on their own streams (one workspace each), joined
-    on the current stream, then the merge. Capturable as one HIP graph."""
+    on the current stream, then the merge. Capturable as one HIP graph.
+    ``reuse_plan``: every shard's workspace holds its schedule (run_plan)."""
     import torch
     bufs.per_shard_workspaces()
     cur = torch.cuda.current_stream()
@@ -134,7 +150,7 @@ def run_step_concurrent(dw: DeviceWorkload, bufs: StepBuffers, streams, use_meta
         s = streams[r]
         s.wait_stream(cur)
         with torch.cuda.stream(s):
-            run_partial(dw, bufs, r, use_metadata=use_metadata, stream=s)
+            run_partial(dw, bufs, r, use_metadata=use_metadata, reuse_plan=reuse_plan, stream=s)
     for r in range(dw.shards):
         cur.wait_stream(streams[r])
     run_merge(dw, bufs, out_base=out_base, stream=cur)

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 2
+#define MLA_ABI_VERSION 3
 #define MLA_PAGE_SIZE 64
 #define MLA_D_QK 576
 #define MLA_D_V 512
@@ -147,12 +147,20 @@ typedef struct mla_decode_args {
   void* workspace;
   size_t workspace_bytes;
   /* tuning: number of persistent workgroups the shard's work is spread
-   * over, 1 .. 1024 (0 = one per compute unit) */
+   * over, 1 .. 1024 (0 = one per compute unit but one in 16, rounded down
+   * to a multiple of 8) */
   int32_t split_target;
   /* optional hipEvent_t pair (created with timing) that receive the start
    * and end times of the attention kernel's dispatch (NULL = none) */
   void* event_begin;
   void* event_end;
+  /* 0: build the work schedule in this call (a small kernel before the
+   * attention kernel). 1: `workspace` already holds the schedule that
+   * mla_decode_plan built for the same batch, num_heads, q_len, shard_id,
+   * num_shards, max_pages, split_target, metadata pointers and the same
+   * contents of seq_lens / local_seq_lens (the schedule depends on nothing
+   * else), so one schedule serves every layer of a decode step. */
+  int32_t reuse_plan;
 } mla_decode_args_t;
 
 /* Bytes of workspace mla_decode_partial needs for these sizes (host only,
@@ -169,6 +177,16 @@ size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t q_le
  * which is always the requested one. */
 mla_status_t mla_decode_partial(const mla_decode_args_t* args, mla_lse_base_t* lse_base_written,
                                 void* stream);
+
+/* Builds the work schedule of a partial decode into args->workspace without
+ * running the decode (same arguments and errors as mla_decode_partial; the
+ * inputs are not read beyond seq_lens / local_seq_lens and the output
+ * pointers not written). A later mla_decode_partial with reuse_plan = 1 and
+ * the same workspace skips the schedule. Like the shard metadata it is built
+ * once per decode step and serves every layer: the schedule is the
+ * workgroups' shares of (request, row block, 32-token tile) units, balanced
+ * by cost, with the pieces of requests cut at workgroup boundaries. */
+mla_status_t mla_decode_plan(const mla_decode_args_t* args, void* stream);
 
 /* ------------------------------------------------------------------------
  * Cross-shard merge.

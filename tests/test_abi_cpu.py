@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 def test_struct_layouts_and_version(lib):
     assert lib.mla_sizeof_decode_args() == ctypes.sizeof(L.DecodeArgs)
     assert lib.mla_sizeof_merge_args() == ctypes.sizeof(L.MergeArgs)
-    assert lib.mla_abi_version() == 2
+    assert lib.mla_abi_version() == 3
     assert lib.mla_status_string(L.STATUS_INVALID_ARGUMENT) == b"invalid argument"
 
 
