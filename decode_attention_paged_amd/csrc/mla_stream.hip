@@ -879,8 +879,10 @@ void attn_stream_kernel(DecodeParams p) {
 struct ConstRows {
   uint32_t zero[kDqk / 2];       // 1152 bytes
   uint32_t nan_bf16[kDqk / 2];   // bf16 NaN 0x7FC0
-  constexpr ConstRows() : zero(), nan_bf16() {
+  uint32_t nan_fp8[kDqk / 4];    // e4m3 NaN 0x7F
+  constexpr ConstRows() : zero(), nan_bf16(), nan_fp8() {
     for (int i = 0; i < kDqk / 2; ++i) nan_bf16[i] = 0x7FC07FC0u;
+    for (int i = 0; i < kDqk / 4; ++i) nan_fp8[i] = 0x7F7F7F7Fu;
   }
 };
 __device__ __attribute__((aligned(256))) const ConstRows g_const_rows;
@@ -921,14 +923,16 @@ __device__ __forceinline__ void load_entries(const DecodeParams& p, const Cursor
 
 // Source row of token 8 w + (lane >> 3) of the cursor's tile for copying
 // wave w (valid: the tile exists in this workgroup's range).
-template <bool kLocal>
+template <bool kLocal, bool kFp8 = false>
 __device__ __forceinline__ const uint8_t* token_src(const DecodeParams& p, const Cursor& c, bool valid,
                                                     const TileEntries& te, int wave) {
+  constexpr long long kRowBytes = kFp8 ? kDqk : 2 * kDqk;
   const int lane = threadIdx.x & 63;
   const int tk = lane >> 3;
   const int j = c.tile * kTile + 8 * wave + tk;
   const uint8_t* zero = reinterpret_cast<const uint8_t*>(g_const_rows.zero);
-  const uint8_t* nan = reinterpret_cast<const uint8_t*>(g_const_rows.nan_bf16);
+  const uint8_t* nan = kFp8 ? reinterpret_cast<const uint8_t*>(g_const_rows.nan_fp8)
+                            : reinterpret_cast<const uint8_t*>(g_const_rows.nan_bf16);
   if (!valid || j >= c.cnt) return zero;
   if constexpr (kLocal) {
     // e = entry tk, as a sum of differences (a select chain here is turned
@@ -943,7 +947,7 @@ __device__ __forceinline__ const uint8_t* token_src(const DecodeParams& p, const
     e += tk >= 7 ? (unsigned)te.e7 - (unsigned)te.e6 : 0u;
     const int ei = (int)e;
     const bool ok = ei >= 0 && (long long)ei < (long long)p.num_pages * kPage;
-    return ok ? p.kv + (long long)ei * (2 * kDqk) : nan;
+    return ok ? p.kv + (long long)ei * kRowBytes : nan;
   } else {
     const int t = j * p.num_shards + p.shard;
     const int d = (t >> 6) - te.p0;
@@ -952,7 +956,7 @@ __device__ __forceinline__ const uint8_t* token_src(const DecodeParams& p, const
     eu += d >= 2 ? (unsigned)te.e2 - (unsigned)te.e1 : 0u;
     const int e = (int)eu;
     const bool ok = e >= 0 && e < p.num_pages;
-    return ok ? p.kv + ((long long)e * kPage + (t & 63)) * (2 * kDqk) : nan;
+    return ok ? p.kv + ((long long)e * kPage + (t & 63)) * kRowBytes : nan;
   }
 }
 
@@ -1430,7 +1434,68 @@ void attn_pipe_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// warp-specialised attention over bf16 KV (64-row blocks)
+// fp8 tiles for the warp-specialised kernel: staged as stored, converted to
+// bf16 in registers (exact: every e4m3 value is a bf16 value)
+// ---------------------------------------------------------------------------
+// Stage layout (18 KB): main chunk c (16 dims) of token t at
+// 512 t + 16 (c ^ fp8_swz(t, c)), rope chunk r at kRope8 + 64 t +
+// 16 (r ^ ((t >> 2) & 3)). The swizzle makes the 16-byte K reads of 16
+// tokens and the transposing V reads of each half wave conflict free.
+constexpr int kStage8 = kTile * kDqk;        // 18432
+constexpr int kRope8 = kTile * 512;          // rope part of an fp8 stage
+__host__ __device__ constexpr int fp8_swz(int t, int c) { return (t & 15) ^ (4 * (c & 1)); }
+
+__device__ __forceinline__ bf16x8_t cvt_fp8x8(uint32_t w0, uint32_t w1) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t y0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2_t y1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2_t y2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2_t y3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return bf16x8_t{y0[0], y0[1], y1[0], y1[1], y2[0], y2[1], y3[0], y3[1]};
+}
+
+// Copy j of an fp8 tile for copying wave w (tokens 8 w .. 8 w + 7; srcw:
+// per lane the row of token 8 w + (lane >> 3)): j < 4 moves the 512-byte
+// main parts of tokens 8 w + 2 j and + 1 (one per half wave), j = 4 the
+// eight 64-byte rope tails (a half copy, 32 lanes).
+template <int kJ>
+__device__ __forceinline__ void copy8_tile_part(const uint8_t* srcw, uint32_t stage_lds, int wave) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t a = reinterpret_cast<uint64_t>(srcw);
+  if constexpr (kJ < 4) {
+    const uint32_t lo0 = __builtin_amdgcn_readlane((uint32_t)a, 16 * kJ);
+    const uint32_t hi0 = __builtin_amdgcn_readlane((uint32_t)(a >> 32), 16 * kJ);
+    const uint32_t lo1 = __builtin_amdgcn_readlane((uint32_t)a, 16 * kJ + 8);
+    const uint32_t hi1 = __builtin_amdgcn_readlane((uint32_t)(a >> 32), 16 * kJ + 8);
+    const bool second = lane >= 32;
+    const uint64_t row = second ? (((uint64_t)hi1 << 32) | lo1) : (((uint64_t)hi0 << 32) | lo0);
+    const int t = 8 * wave + 2 * kJ + (second ? 1 : 0);
+    const int pos = lane & 31, x = (pos ^ t) & 15;
+    const int c = pos ^ (t & 15) ^ (4 * (x & 1));
+    lds_dma16(reinterpret_cast<const uint8_t*>(row) + 16 * c,
+              __builtin_amdgcn_readfirstlane(stage_lds + 512 * (8 * wave + 2 * kJ)));
+  } else {
+    const int tl = (lane >> 2) & 7;
+    const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)a, 8 * tl);
+    const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(a >> 32), 8 * tl);
+    const uint8_t* row = reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
+    const int t = 8 * wave + tl;
+    const int r = (lane & 3) ^ ((t >> 2) & 3);
+    if (lane < 32) lds_dma16(row + 512 + 16 * r, __builtin_amdgcn_readfirstlane(stage_lds + kRope8 + 512 * wave));
+  }
+}
+__device__ __forceinline__ void copy8_tile_part_rt(int j, const uint8_t* srcw, uint32_t stage_lds, int wave) {
+  switch (j) {
+    case 0: copy8_tile_part<0>(srcw, stage_lds, wave); break;
+    case 1: copy8_tile_part<1>(srcw, stage_lds, wave); break;
+    case 2: copy8_tile_part<2>(srcw, stage_lds, wave); break;
+    case 3: copy8_tile_part<3>(srcw, stage_lds, wave); break;
+    default: copy8_tile_part<4>(srcw, stage_lds, wave); break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// warp-specialised attention (64-row blocks)
 // ---------------------------------------------------------------------------
 // Eight waves, two per SIMD, in two roles (a second wave per SIMD to issue
 // from while one waits on LDS; the register file holds both):
@@ -1447,20 +1512,29 @@ void attn_pipe_kernel(DecodeParams p) {
 //    the wait before each barrier is a constant vmcnt(9)).
 // Tile i: barrier (tile i landed; copies of tile i + 2 go out) -> scores of
 // tile i with the softmax of tile i - 1 | barrier | P V of tile i - 1.
+// fp8 KV (kFp8): tiles stay fp8 in LDS (18 KB stages, five copies per wave
+// and tile) and are converted in registers; K is read 16 bytes (two k-steps)
+// per lane, V with ds_read_b64_tr_b8; P goes to a buffer of its own (the
+// fp8 rope part is too small) and the output is staged in a region of its
+// own.
 constexpr int kWsRows = 64;
 constexpr int kWsStagePitch = 272;     // output staging row: 128 bf16 + 16 bytes
 
-template <bool kLocal>
+template <bool kLocal, bool kFp8>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_ws_kernel(DecodeParams p) {
   constexpr int kNS = 4;
-  constexpr int kCopies = 9;
+  constexpr int kStageB = kFp8 ? kStage8 : kStageBytes;
+  constexpr int kCopies = kFp8 ? 5 : 9;
   constexpr int kG = 2;                 // k-steps per 32-dim group of a score wave
   constexpr int kKS = 18;               // score MFMAs per wave and tile
   constexpr int kAhead = 4;
   constexpr int kChunks = 9;            // softmax chunks between score MFMAs
+  constexpr int kPBytes = kWsRows * 32 * 2;                      // P of one tile (bf16)
+  constexpr int kStgBytes = 4 * kWsRows * kWsStagePitch;         // output staging (fp8)
+  constexpr int kSmem = kNS * kStageB + (kFp8 ? 2 * kPBytes + kStgBytes : 0);
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
   __shared__ __attribute__((aligned(16))) f32x4_t xbuf[2 * 4 * 64];   // [rg][4][lane]
   __shared__ float fbuf[2 * kWsRows];   // [tile parity][row]: rescale factor of the tile's P
   __shared__ float lbuf[kWsRows];       // row sums at the end of a piece
@@ -1477,9 +1551,14 @@ void attn_ws_kernel(DecodeParams p) {
   const int rec_seg1 = ld_const(rec + 4), rec_cnt1 = ld_const(rec + 5);
   if (Uw <= 0) return;
   const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_address(smem));
-  // P^T of row group r, token half m: 16 bytes per lane at
-  // kRopeBase + 2048 r + 64 row + 16 ((2 m + hi) ^ ((row >> 2) & 3))
-  const uint32_t poff = (uint32_t)(kRopeBase + 64 * tok);
+  // P^T of tile u, row group r, token half m: 16 bytes per lane at
+  // p_area(u) + 2048 r + 64 row + 16 ((2 m + hi) ^ ((row >> 2) & 3)), in the
+  // rope part of the tile's stage (bf16) or a buffer per tile parity (fp8)
+  auto p_area = [&](int u) -> uint8_t* {
+    if constexpr (kFp8) return smem + kNS * kStageB + (u & 1) * kPBytes;
+    else return smem + kStageB * (u & (kNS - 1)) + kRopeBase;
+  };
+  const uint32_t poff = (uint32_t)(64 * tok);
   const int pswz = (tok >> 2) & 3;
 
   if (wave < 4) {
@@ -1487,20 +1566,42 @@ void attn_ws_kernel(DecodeParams p) {
     const int rg = wave & 1, ds = wave >> 1;
     const uint32_t qk0 = (uint32_t)(1024 * tok + 16 * ((2 * kG * ds) ^ hi ^ chunk_swz(tok)));
     const uint32_t rope0 = (uint32_t)(kRopeBase + 128 * tok + 16 * ((2 * kG * ds) ^ hi ^ chunk_swz(tok)));
+    // fp8: score step i = 2 j + u uses 16-dim chunk 2 m + hi of the lane's
+    // token, m = 2 j + ds (m = 16, 17: rope), its 8-byte half u; the query
+    // registers follow the same order of the dims
+    const uint32_t qk8 = (uint32_t)(512 * tok + 16 * (hi ^ (tok & 15) ^ (4 * hi)));
+    const uint32_t rope8 = (uint32_t)(kRope8 + 64 * tok + 16 * ((2 * ds + hi) ^ ((tok >> 2) & 3)));
     Cursor cc;
     cc.start_known(p, rec_seg, rec_tile, rec_cnt);
     bf16x8_t qreg[kKS];
     bf16x8_t ka[kAhead];
+    u32x4_t kraw[2];
     f32x16_t acc;
+    auto k8_load = [&](const uint8_t* ks, int j) -> u32x4_t {
+      const int m = 2 * j + ds;
+      return m < 16 ? *(const u32x4_t*)(ks + (qk8 ^ (32u * (uint32_t)m))) : *(const u32x4_t*)(ks + rope8);
+    };
     auto qk_start = [&](const uint8_t* ks) {
+      if constexpr (kFp8) {
+        kraw[0] = k8_load(ks, 0);
+        kraw[1] = k8_load(ks, 1);
+      } else {
 #pragma unroll
-      for (int u = 0; u < kAhead; ++u) ka[u] = qk_operand<kG>(ks, qk0, rope0, u);
+        for (int u = 0; u < kAhead; ++u) ka[u] = qk_operand<kG>(ks, qk0, rope0, u);
+      }
       acc = f32x16_t{};
     };
     auto qk_step = [&](const uint8_t* ks, int i) {
-      const bf16x8_t a = ka[i % kAhead];
-      if (i + kAhead < kKS) ka[i % kAhead] = qk_operand<kG>(ks, qk0, rope0, i + kAhead);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[i], acc, 0, 0, 0);
+      if constexpr (kFp8) {
+        const int j = i >> 1, u = i & 1;
+        const bf16x8_t a = cvt_fp8x8(kraw[j & 1][2 * u], kraw[j & 1][2 * u + 1]);
+        if (u == 1 && j + 2 < kKS / 2) kraw[j & 1] = k8_load(ks, j + 2);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[i], acc, 0, 0, 0);
+      } else {
+        const bf16x8_t a = ka[i % kAhead];
+        if (i + kAhead < kKS) ka[i % kAhead] = qk_operand<kG>(ks, qk0, rope0, i + kAhead);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[i], acc, 0, 0, 0);
+      }
     };
     f32x4_t* xmine = xbuf + (rg * 4) * 64 + lane;
 
@@ -1511,11 +1612,13 @@ void attn_ws_kernel(DecodeParams p) {
       const int row = rb * kWsRows + rg * 32 + tok;
       const bool row_ok = row < p.rows;
       {
-        const uint16_t* qrow = p.q + ((long long)b * p.rows + (row_ok ? row : 0)) * kDqk + 8 * hi;
+        const uint16_t* qrow = p.q + ((long long)b * p.rows + (row_ok ? row : 0)) * kDqk;
 #pragma unroll
         for (int i = 0; i < kKS; ++i) {
-          const int kk = 4 * (i / kG) + kG * ds + i % kG;
-          const bf16x8_t x = *(const bf16x8_t*)(qrow + 16 * kk);
+          int d0;
+          if constexpr (kFp8) d0 = 32 * (2 * (i >> 1) + ds) + 16 * hi + 8 * (i & 1);
+          else d0 = 16 * (4 * (i / kG) + kG * ds + i % kG) + 8 * hi;
+          const bf16x8_t x = *(const bf16x8_t*)(qrow + d0);
           qreg[i] = row_ok ? x : bf16x8_t{};
         }
       }
@@ -1576,7 +1679,7 @@ void attn_ws_kernel(DecodeParams p) {
       };
       // P of tile u into the rope part of its stage, and the row's factor
       auto write_p = [&](int u, const bf16x8_t (&pb)[2]) {
-        uint8_t* st = smem + kStageBytes * (u & (kNS - 1)) + poff + 2048 * rg;
+        uint8_t* st = p_area(u) + poff + 2048 * rg;
 #pragma unroll
         for (int m = 0; m < 2; ++m) *(bf16x8_t*)(st + 16 * ((2 * m + hi) ^ pswz)) = pb[m];
         if (hi == 0) fbuf[(u & 1) * kWsRows + rg * 32 + tok] = f;
@@ -1596,7 +1699,7 @@ void attn_ws_kernel(DecodeParams p) {
       // tile 0: its scores
       __syncthreads();   // tile t landed
       {
-        const uint8_t* ksq = smem + kStageBytes * (t & (kNS - 1));
+        const uint8_t* ksq = smem + kStageB * (t & (kNS - 1));
         qk_start(ksq);
 #pragma unroll
         for (int i = 0; i < kKS; ++i) qk_step(ksq, i);
@@ -1609,7 +1712,7 @@ void attn_ws_kernel(DecodeParams p) {
       if (ds == 0) s_cur = partner_sum();
       for (int k = 0; k + 1 < n; ++k) {
         __syncthreads();   // tile t + k + 1 landed
-        const uint8_t* ksq = smem + kStageBytes * ((t + k + 1) & (kNS - 1));
+        const uint8_t* ksq = smem + kStageB * ((t + k + 1) & (kNS - 1));
         qk_start(ksq);
         if (ds == 0) {
           bf16x8_t pb[2];
@@ -1668,6 +1771,25 @@ void attn_ws_kernel(DecodeParams p) {
       const int y = 2 * (g16 & 1) + (q4 >> 1);
       pv0 = (uint32_t)(1024 * tl + 16 * (y ^ chunk_swz(tl)) + 8 * (q4 & 1) + 256 * wq);
     }
+    // fp8 V^T operands (ds_read_b64_tr_b8): lane i of each 16-lane group G
+    // points at the 8 dims 32 db + 16 (G & 1) + 8 (i & 1) (of the wave's
+    // slice) of token 8 (e >> 2) + 4 (G >> 1) + (e & 3), e = i >> 1 (+ 16 for
+    // the second token half), so that lane l receives 8 tokens of dim l & 31
+    // in the order of the P values
+    uint32_t pv8[4];
+    {
+      const int G = lane >> 4, i = lane & 15, e = i >> 1;
+      const int tl = 8 * (e >> 2) + 4 * (G >> 1) + (e & 3);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int c = 8 * wq + 2 * db + (G & 1);
+        pv8[db] = (uint32_t)(512 * tl + 16 * (c ^ fp8_swz(tl, c)) + 8 * (i & 1));
+      }
+    }
+    auto copy_part = [&](int j, const uint8_t* src, uint32_t st) {
+      if constexpr (kFp8) copy8_tile_part_rt(j, src, st, wq);
+      else copy_tile_part_rt(j, src, st, wq);
+    };
     Cursor cc, cl;
     cc.start_known(p, rec_seg, rec_tile, rec_cnt);
     cl = cc;
@@ -1679,12 +1801,12 @@ void attn_ws_kernel(DecodeParams p) {
       TileEntries te0, te1;
       load_entries<kLocal>(p, cc, wq, te0);
       if (1 < Uw) load_entries<kLocal>(p, cl, wq, te1);
-      const uint8_t* src0 = token_src<kLocal>(p, cc, true, te0, wq);
+      const uint8_t* src0 = token_src<kLocal, kFp8>(p, cc, true, te0, wq);
 #pragma unroll
-      for (int j = 0; j < kCopies; ++j) copy_tile_part_rt(j, src0, smem_lds, wq);
-      const uint8_t* src1 = token_src<kLocal>(p, cl, 1 < Uw, te1, wq);
+      for (int j = 0; j < kCopies; ++j) copy_part(j, src0, smem_lds);
+      const uint8_t* src1 = token_src<kLocal, kFp8>(p, cl, 1 < Uw, te1, wq);
 #pragma unroll
-      for (int j = 0; j < kCopies; ++j) copy_tile_part_rt(j, src1, smem_lds + kStageBytes, wq);
+      for (int j = 0; j < kCopies; ++j) copy_part(j, src1, smem_lds + kStageB);
     }
     int ncopied = 2;
     TileEntries te;
@@ -1697,10 +1819,10 @@ void attn_ws_kernel(DecodeParams p) {
     auto tile_barrier = [&]() {
       wait_vmcnt<kCopies>();
       __syncthreads();
-      const uint8_t* csrc = token_src<kLocal>(p, cl, ncopied < Uw, te, wq);
-      const uint32_t cst = __builtin_amdgcn_readfirstlane(smem_lds + kStageBytes * (ncopied & (kNS - 1)));
+      const uint8_t* csrc = token_src<kLocal, kFp8>(p, cl, ncopied < Uw, te, wq);
+      const uint32_t cst = __builtin_amdgcn_readfirstlane(smem_lds + kStageB * (ncopied & (kNS - 1)));
 #pragma unroll
-      for (int j = 0; j < kCopies; ++j) copy_tile_part_rt(j, csrc, cst, wq);
+      for (int j = 0; j < kCopies; ++j) copy_part(j, csrc, cst);
       ++ncopied;
       if (ncopied < Uw) {
         cl.advance(p);
@@ -1711,19 +1833,29 @@ void attn_ws_kernel(DecodeParams p) {
     bf16x8_t va[8];
     auto load_v = [&](const uint8_t* ks) {
 #pragma unroll
-      for (int st = 0; st < 8; ++st) va[st] = pv_operand(ks, pv0, st);
+      for (int st = 0; st < 8; ++st) {
+        if constexpr (kFp8) {
+          typedef int32_t i32x2_t __attribute__((ext_vector_type(2)));
+          const i32x2_t x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (__attribute__((address_space(3))) i32x2_t*)(ks + pv8[st >> 1] + 8192 * (st & 1)));
+          va[st] = cvt_fp8x8((uint32_t)x[0], (uint32_t)x[1]);
+        } else {
+          va[st] = pv_operand(ks, pv0, st);
+        }
+      }
     };
     // O^T[dim][row] += V^T[dim][token] P^T[token][row] for both row groups,
     // after the rows' rescale (f = 1 unless the reference moved)
-    auto pv_tile = [&](const uint8_t* ks, int u) {
+    auto pv_tile = [&](int u) {
       const float f0 = fbuf[(u & 1) * kWsRows + tok];
       const float f1 = fbuf[(u & 1) * kWsRows + 32 + tok];
+      const uint8_t* pa = p_area(u) + poff;
       bf16x8_t pp[2][2];
 #pragma unroll
       for (int r = 0; r < 2; ++r)
 #pragma unroll
         for (int m = 0; m < 2; ++m)
-          pp[r][m] = *(const bf16x8_t*)(ks + poff + 2048 * r + 16 * ((2 * m + hi) ^ pswz));
+          pp[r][m] = *(const bf16x8_t*)(pa + 2048 * r + 16 * ((2 * m + hi) ^ pswz));
       if (__builtin_expect(__ballot(f0 != 1.f) != 0, 0)) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) o[db][0] *= f0;
@@ -1753,16 +1885,16 @@ void attn_ws_kernel(DecodeParams p) {
       __syncthreads();   // partials exchanged
       for (int k = 0; k + 1 < n; ++k) {
         tile_barrier();  // tile t + k + 1 landed
-        const uint8_t* ksv = smem + kStageBytes * ((t + k) & (kNS - 1));
+        const uint8_t* ksv = smem + kStageB * ((t + k) & (kNS - 1));
         load_v(ksv);
         __syncthreads();   // P of tile t + k written
-        pv_tile(ksv, t + k);
+        pv_tile(t + k);
       }
       {
-        const uint8_t* ksv = smem + kStageBytes * ((t + n - 1) & (kNS - 1));
+        const uint8_t* ksv = smem + kStageB * ((t + n - 1) & (kNS - 1));
         load_v(ksv);
         __syncthreads();   // P of the last tile and the row sums written
-        pv_tile(ksv, t + n - 1);
+        pv_tile(t + n - 1);
       }
       const float l0 = lbuf[tok], l1 = lbuf[32 + tok];
       __syncthreads();   // every output wave is done with the stages
@@ -1793,9 +1925,12 @@ void attn_ws_kernel(DecodeParams p) {
           }
         }
       } else {
-        // bf16 rows through LDS (the stages of the piece's last two tiles are
-        // free): 64 rows x 128 dims per wave, stored 16 bytes a lane
-        uint8_t* sb = smem + kStageBytes * ((t + n - 1 - (wq >> 1)) & (kNS - 1)) + (wq & 1) * (kWsRows * kWsStagePitch);
+        // bf16 rows through LDS (bf16: the stages of the piece's last two
+        // tiles, which are free; fp8: a region of its own): 64 rows x 128
+        // dims per wave, stored 16 bytes a lane
+        uint8_t* sb;
+        if constexpr (kFp8) sb = smem + kNS * kStageB + 2 * kPBytes + wq * (kWsRows * kWsStagePitch);
+        else sb = smem + kStageB * ((t + n - 1 - (wq >> 1)) & (kNS - 1)) + (wq & 1) * (kWsRows * kWsStagePitch);
         typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 #pragma unroll
         for (int r = 0; r < 2; ++r)
@@ -1892,8 +2027,9 @@ __global__ __launch_bounds__(256) void stream_combine_kernel(DecodeParams p) {
 
 }  // namespace
 
-// 64-row blocks of bf16 KV run the warp-specialised kernel
+// 64-row blocks run the warp-specialised kernel (fp8 KV too)
 constexpr bool kUseWs = true;
+constexpr bool kUseWsFp8 = true;
 
 hipError_t launch_decode_plan(const DecodeParams& p, hipStream_t stream) {
   if (p.batch == 0) return hipSuccess;
@@ -1910,17 +2046,22 @@ hipError_t launch_decode_stream(const DecodeParams& p, bool run_plan, hipEvent_t
   // times (recorded with the dispatch, no separate marker packets)
   void* args[] = {const_cast<DecodeParams*>(&p)};
   const void* fn;
-  if (p.kv_fp8) fn = p.rows_blk == 32 ? reinterpret_cast<const void*>(&attn_stream_kernel<4, true>)
-                                      : reinterpret_cast<const void*>(&attn_stream_kernel<2, true>);
-  else if (p.local_kv_indices != nullptr)
-    fn = p.rows_blk == 32 ? reinterpret_cast<const void*>(&attn_pipe_kernel<4, true>)
-         : kUseWs         ? reinterpret_cast<const void*>(&attn_ws_kernel<true>)
-                          : reinterpret_cast<const void*>(&attn_pipe_kernel<2, true>);
+  const bool local = p.local_kv_indices != nullptr;
+  const bool ws = kUseWs && p.rows_blk == kWsRows && (!p.kv_fp8 || kUseWsFp8);
+  if (p.kv_fp8 && !ws)
+    fn = p.rows_blk == 32 ? reinterpret_cast<const void*>(&attn_stream_kernel<4, true>)
+                          : reinterpret_cast<const void*>(&attn_stream_kernel<2, true>);
+  else if (p.kv_fp8)
+    fn = local ? reinterpret_cast<const void*>(&attn_ws_kernel<true, true>)
+               : reinterpret_cast<const void*>(&attn_ws_kernel<false, true>);
+  else if (ws)
+    fn = local ? reinterpret_cast<const void*>(&attn_ws_kernel<true, false>)
+               : reinterpret_cast<const void*>(&attn_ws_kernel<false, false>);
   else
-    fn = p.rows_blk == 32 ? reinterpret_cast<const void*>(&attn_pipe_kernel<4, false>)
-         : kUseWs         ? reinterpret_cast<const void*>(&attn_ws_kernel<false>)
-                          : reinterpret_cast<const void*>(&attn_pipe_kernel<2, false>);
-  const bool ws = kUseWs && !p.kv_fp8 && p.rows_blk == kWsRows;
+    fn = p.rows_blk == 32 ? (local ? reinterpret_cast<const void*>(&attn_pipe_kernel<4, true>)
+                                   : reinterpret_cast<const void*>(&attn_pipe_kernel<4, false>))
+                          : (local ? reinterpret_cast<const void*>(&attn_pipe_kernel<2, true>)
+                                   : reinterpret_cast<const void*>(&attn_pipe_kernel<2, false>));
   err = hipExtLaunchKernel(fn, dim3(p.grid), dim3(ws ? 512 : 256), args, 0, stream, ev_begin, ev_end, 0);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(stream_combine_kernel, dim3(p.batch, (p.rows + 3) / 4), dim3(256), 0, stream, p);
