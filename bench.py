@@ -278,7 +278,7 @@ def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True, spl
         eager_ms_per_step=eager_ms_step,
     )
     # the contraction runs on bf16 MFMAs for both KV types (fp8 pages are
-    # converted to bf16 in LDS), so its peak is the bf16 one
+    # converted to bf16 exactly, in registers), so its peak is the bf16 one
     peak_tf = BF16_PEAK_TFLOPS
     res["attn_kernel_hbm_frac"] = achieved_gbs / HBM_PEAK_GBS
     res["attn_kernel_mfma_frac"] = achieved_tflops / peak_tf
@@ -454,10 +454,10 @@ def main() -> int:
                     frac=res["attn_kernel_gbs"] / HBM_PEAK_GBS)
     roof["traffic"] = traffic_from_profile(wl.name)
     ds = 4 if wl.heads * wl.q_len <= 32 else 2
-    if wl.kv_dtype == "fp8":
-        kname = "attn_stream_kernel<%d, fp8> (mla_stream.hip)" % ds
-    elif ds == 2:
-        kname = "attn_ws_kernel<local indices> (mla_stream.hip)"
+    if ds == 2:
+        kname = "attn_ws_kernel<local indices, %s KV> (mla_stream.hip)" % wl.kv_dtype
+    elif wl.kv_dtype == "fp8":
+        kname = "attn_stream_kernel<4, fp8> (mla_stream.hip)"
     else:
         kname = "attn_pipe_kernel<4, local indices> (mla_stream.hip)"
     roof["kernel"] = kname + ", mean of %d launches" % (args.steps * wl.shards)
