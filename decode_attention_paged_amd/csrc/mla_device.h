@@ -62,8 +62,8 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)p);
 }
 
-// global_load_lds_dwordx4 / _dword: each active lane's 16 (4) bytes from
-// `src` go to LDS at lds_base + 16 (4) * lane. Issued as inline assembly so
+// global_load_lds_dwordx4: each active lane's 16 bytes from `src` go to LDS
+// at lds_base + 16 * lane. Issued as inline assembly so
 // that the compiler's wait-count bookkeeping does not make later LDS reads of
 // other buffers wait for them; every caller waits for completion explicitly
 // (s_waitcnt vmcnt + barrier) before any wave reads the destination. M0 holds
@@ -77,10 +77,6 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
 __device__ __forceinline__ void lds_dma16_sbase(const void* base, uint32_t offset, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(offset), "s"(base), "s"(lds_base));
-}
-__device__ __forceinline__ void lds_dma4(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :: "v"(src), "s"(lds_base));
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:

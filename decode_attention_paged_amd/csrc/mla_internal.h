@@ -49,19 +49,20 @@ struct DecodeParams {
   int32_t* wg_rec;
   uint16_t* spart_o;              // [slots][rows_blk][512] bf16, normalised, scaled
   float* spart_lse;               // [slots][rows_blk] base 2
-  int32_t rows_blk;               // query rows per workgroup (32 or 64)
+  int32_t rows_blk;               // query rows per workgroup (64)
   int32_t kv_fp8;                 // KV pages hold e4m3 (else bf16)
   int32_t grid;                   // persistent workgroups
 };
 
 constexpr int kMaxGrid = 1024;  // persistent workgroups of the streaming kernel
-constexpr int kRecInts = 80;    // start record: 8-int header, pad, 2 x 32 rows
+constexpr int kRecInts = 8;     // start record of a workgroup: 6 ints used
 
-// Query rows one streaming workgroup covers: its four waves are 2 row groups
-// of 32 rows x 2 halves of the dims (rows > 32), or 1 x 4 (rows <= 32); more
-// rows take several row blocks, whose workgroups read the same KV tiles at
-// about the same time (neighbours in the schedule), mostly from cache.
-inline int32_t stream_rows_per_block(int32_t rows) { return rows <= 32 ? 32 : 64; }
+// Query rows one workgroup covers: two row groups of 32 (a request with fewer
+// rows leaves the rest empty: they compute on zero queries and are never
+// stored); more rows take several row blocks, whose workgroups read the same
+// KV tiles at about the same time (neighbours in the schedule), mostly from
+// cache.
+inline int32_t stream_rows_per_block(int32_t) { return 64; }
 
 struct WorkspaceLayout {
   size_t plan, req_cnt, seg_off, seg_coff, seg_info, wg_start, wg_ustart, wg_rec, spart_lse, spart_o, total;

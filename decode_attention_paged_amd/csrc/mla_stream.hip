@@ -1,4 +1,4 @@
-// Rank-local paged MLA decode: persistent streaming kernels.
+// Rank-local paged MLA decode: a persistent, warp-specialised kernel.
 //
 // One shard r of S owns the tokens t = j S + r of every request (prhub.com.cn
 // digest of sgl-project/sglang PR 33926, sections 功能与动机 and 实现拆解
@@ -6,46 +6,33 @@
 // those tokens and emits the rank-local (out, lse), (0, -inf) where a row
 // sees no owned token.
 //
-// Schedule. The shard's work is a sequence of units (request b, block of
+// Schedule. The shard's work is a sequence of units (request b, block of 64
 // query rows rb, 32-token tile), ordered by segment s = b * row_blocks + rb
 // and tile. stream_plan_kernel lays the segments out on device (no host
-// synchronisation) and one workgroup per CU takes a contiguous share of the
-// units of about equal cost. A segment that a workgroup holds entirely is
-// finalised in place; a segment cut at workgroup boundaries leaves one bf16
-// partial per piece, combined by stream_combine_kernel.
+// synchronisation) and each persistent workgroup takes a contiguous share of
+// the units of about equal cost. A segment that a workgroup holds entirely
+// is finalised in place; a segment cut at workgroup boundaries leaves one
+// bf16 partial per piece, combined by stream_combine_kernel.
 //
-// Workgroup. Four waves: rows_blk / 32 row groups of 32 query rows times
-// 4 / (rows_blk / 32) slices of the 512 V dims. The waves of a row group
-// split the 576 QK dims and exchange their partial scores through LDS
-// (S^T = K Q^T, v_mfma_f32_32x32x16_bf16); each wave then accumulates the
-// output of its dims slice.
-//
-// bf16 KV (attn_pipe_kernel). Tiles move HBM -> LDS with
-// global_load_lds_dwordx4 (no register staging) through four 36 KB stages;
-// the row of every token comes from the block table by scalar loads, and
-// out-of-pool pages point the copy at a constant NaN row. The loop overlaps
-// two tiles: the scores of tile k + 1 run with tile k's softmax on the VALU
-// and then with tile k's accumulation (O^T += V^T P^T) on the MFMAs.
-//
-// fp8 KV (attn_stream_kernel<.., true>). Tiles are staged as stored (five
-// 18 KB stages), converted to a bf16 compute stage, and the row indices move
-// into an LDS ring 2 * 5 - 2 tiles ahead; every vector-memory operation in
-// the tile loop is an asynchronous copy and the loop waits on exactly the
-// tile it needs (s_waitcnt vmcnt(n) with n counted by the wave).
+// Workgroup (attn_ws_kernel). Eight waves, two per SIMD: four score waves
+// (S^T = K Q^T on v_mfma_f32_32x32x16_bf16, two per row group of 32 rows,
+// each over half the 576 QK dims, and the online softmax) and four output
+// waves (O^T += V^T P^T for all 64 rows, 128 dims each). Tiles move HBM ->
+// LDS with global_load_lds_dwordx4 (no register staging) through four
+// stages, as stored: bf16 (36 KB) or fp8 e4m3 (18 KB, converted to bf16 in
+// registers, exactly); the row of every token comes from the block table or
+// the local KV indices by scalar loads, and out-of-pool pages point the copy
+// at a constant NaN row.
 #include "mla_device.h"
 
 #include <hip/hip_ext.h>
 
-#include <limits.h>
-#include <type_traits>
 
 namespace mla {
 namespace {
 
-constexpr int kStageBytes = kTile * kDqk * 2;      // 36864: one tile
-constexpr int kRopeBase = kTile * 1024;             // rope part of a stage (dims 512..575)
-constexpr int kStageBytes8 = kTile * kDqk;          // 18432: one fp8 tile as stored
-constexpr int kRing = 16;                          // row-index ring, in tiles
+constexpr int kStageBytes = kTile * kDqk * 2;      // 36864: one bf16 tile
+constexpr int kRopeBase = kTile * 1024;             // rope part of a bf16 stage (dims 512..575)
 // A row's exponent reference moves up (rescaling its accumulator) only when a
 // tile's max exceeds it by more than this (log2 units), so rescaling is rare
 // and unnormalised probabilities stay below 2^kRescaleSlack.
@@ -53,8 +40,6 @@ constexpr float kRescaleSlack = 8.0f;
 
 constexpr int kPieceCost = 3;     // query load + epilogue of a piece, in tiles
 
-constexpr int kRowPastEnd = -2;   // token past the request's owned range
-constexpr int kRowBad = -1;       // page id or row outside the pool
 
 
 // ---------------------------------------------------------------------------
@@ -267,151 +252,14 @@ struct Cursor {
   }
 };
 
-// Row indices of the cursor's tile -> LDS ring slot (32 ints): wave w copies
-// the table entries of tokens 8w .. 8w + 7 (one instruction per wave). Past
-// the owned range it copies the tile's first entry instead; those tokens are
-// masked by the reader.
-__device__ __forceinline__ void fetch_rows(const DecodeParams& p, const Cursor& c, uint32_t slot_lds) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (lane < 8) {
-    int j = c.tile * kTile + 8 * wave + lane;
-    j = j < c.cnt ? j : c.tile * kTile;
-    const int32_t* src;
-    if (p.local_kv_indices != nullptr)
-      src = p.local_kv_indices + (long long)c.b * p.local_kv_stride + j;
-    else
-      src = p.block_table + (long long)c.b * p.max_pages + ((j * p.num_shards + p.shard) >> 6);
-    lds_dma4(src, __builtin_amdgcn_readfirstlane(slot_lds + 32 * wave));
-  }
-}
-
-// KV row of token `tok` of the cursor's tile from its table entry.
-__device__ __forceinline__ int resolve_row(const DecodeParams& p, int tile, int cnt, int tok, int raw) {
-  const int j = tile * kTile + tok;
-  if (j >= cnt) return kRowPastEnd;
-  long long row;
-  if (p.local_kv_indices != nullptr) {
-    row = raw;
-  } else {
-    const int t = j * p.num_shards + p.shard;
-    row = (raw < 0 || raw >= p.num_pages) ? -1 : (long long)raw * kPage + (t & 63);
-  }
-  return (row < 0 || row >= (long long)p.num_pages * kPage) ? kRowBad : (int)row;
-}
-
-// XOR swizzle of the 16-byte chunks inside each 128-byte group, by token:
-// eight consecutive tokens get eight different values, and four consecutive
-// tokens differ in the 32-byte pair they select.
-__host__ __device__ constexpr int chunk_swz(int t) { return 2 * (t & 3) + ((t >> 2) & 1); }
-
-// Copies of one tile into a stage (issue_tile, or its parts spread over a
-// tile loop iteration). Stage layout (token-major, swizzled):
+// bf16 stage layout (one 32-token tile, 36 KB, token-major, swizzled):
 //   chunk c < 64 (dims 8c .. 8c + 7) of token t at byte 1024 t + 16 (c ^ swz(t)),
-//   chunk c >= 64 (rope) at kRopeBase + 128 t + 16 ((c - 64) ^ swz(t)).
-// Wave w moves tokens 8w .. 8w + 7: one copy per token for its first 1 KB
-// (64 lanes over one row, so every copy reads whole 128-byte lines) and one
-// copy for the eight 128-byte rope tails. The row of each token comes from
-// the ring; the main copies take it as a scalar base address.
-// Row of token 8w + (lane >> 3) of the cursor's tile for wave w (0 if the
-// token is past the end or its page is outside the pool).
-__device__ __forceinline__ int tile_rows(const DecodeParams& p, const Cursor& c, const int32_t* ring_slot) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tk = 8 * wave + (lane >> 3);
-  const int row = resolve_row(p, c.tile, c.cnt, tk, ring_slot[tk]);
-  return row >= 0 ? row : 0;
-}
-__device__ __forceinline__ void copy_rope(const DecodeParams& p, int rowc, uint32_t stage_lds) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  lds_dma16(p.kv + (long long)rowc * (2 * kDqk) + 16 * (64 + ((lane & 7) ^ chunk_swz(lane >> 3))),
-            __builtin_amdgcn_readfirstlane(stage_lds + kRopeBase + 1024 * wave));
-}
-template <int kI0, int kI1>
-__device__ __forceinline__ void copy_main(const DecodeParams& p, int rowc, uint32_t stage_lds) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#pragma unroll
-  for (int i = kI0; i < kI1; ++i) {
-    const int r = __builtin_amdgcn_readlane(rowc, 8 * i);
-    const uint8_t* base = p.kv + (long long)r * (2 * kDqk);
-    lds_dma16_sbase(base, (uint32_t)(16 * (lane ^ chunk_swz(i))),
-                    __builtin_amdgcn_readfirstlane(stage_lds + 1024 * (8 * wave + i)));
-  }
-}
-__device__ __forceinline__ void issue_tile(const DecodeParams& p, const Cursor& c, uint32_t stage_lds,
-                                           const int32_t* ring_slot) {
-  const int rowc = tile_rows(p, c, ring_slot);
-  copy_rope(p, rowc, stage_lds);
-  copy_main<0, 8>(p, rowc, stage_lds);
-}
-
-// Wait until at most `after` vector-memory operations of this wave are
-// outstanding, i.e. everything issued before the last `after` ones landed.
-// `after` is wave-uniform; the ladder takes the largest immediate <= after
-// (kMax bounds it; waiting longer is always safe).
-template <int kMax>
-__device__ __forceinline__ void wait_vm_le(int after) {
-  if constexpr (kMax == 0) {
-    wait_vmcnt<0>();
-  } else {
-    if (after >= kMax) wait_vmcnt<kMax>();
-    else wait_vm_le<kMax - 1>(after);
-  }
-}
-
-// fp8 tiles: staged as stored (token t at byte 576 t). Wave w moves the 4608
-// bytes of tokens 8w .. 8w + 7; copy i covers bytes 1024 i .. + 1023 of them,
-// lane l the 16-byte chunk (64 i + l) % 36 of token (64 i + l) / 36, and the
-// fifth copy is a half one (32 lanes). rowc: row of token 8w + (lane & 7).
-__device__ __forceinline__ int tile_rows8(const DecodeParams& p, const Cursor& c, const int32_t* ring_slot) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tk = 8 * wave + (lane & 7);
-  const int row = resolve_row(p, c.tile, c.cnt, tk, ring_slot[tk]);
-  return row >= 0 ? row : 0;
-}
-template <int kI0, int kI1>
-__device__ __forceinline__ void copy8(const DecodeParams& p, int rowc, uint32_t stage_lds) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#pragma unroll
-  for (int i = kI0; i < kI1; ++i) {
-    const int g = 64 * i + lane;
-    const int tl = g / 36, ch = g - 36 * tl;
-    const int row = __shfl(rowc, tl);
-    const uint8_t* src = p.kv + (long long)row * kDqk + 16 * ch;
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(stage_lds + 4608 * wave + 1024 * i);
-    if (i < 4 || lane < 32) lds_dma16(src, dst);
-  }
-}
-__device__ __forceinline__ void issue_tile8(const DecodeParams& p, const Cursor& c, uint32_t stage_lds,
-                                            const int32_t* ring_slot) {
-  const int rowc = tile_rows8(p, c, ring_slot);
-  copy8<0, 5>(p, rowc, stage_lds);
-}
-
-// fp8 staging -> bf16 stage in the layout of the bf16 tiles (exact: every
-// e4m3 value is a bf16 value; the per-tensor scale is applied to the scores
-// and the output instead). Thread k converts the 8-dim chunks k + 256 j.
-__device__ __forceinline__ void convert_tile8(const uint8_t* stg, uint8_t* dst) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-#pragma unroll
-  for (int j = 0; j < kTile * (kDqk / 8) / 256; ++j) {
-    const int unit = threadIdx.x + 256 * j;
-    const int tkn = unit / (kDqk / 8), c = unit - (kDqk / 8) * tkn;
-    const u32x2_t x = *(const u32x2_t*)(stg + kDqk * tkn + 8 * c);
-    const bf16x2_t y0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, false);
-    const bf16x2_t y1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, true);
-    const bf16x2_t y2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, false);
-    const bf16x2_t y3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, true);
-    const bf16x8_t y = {y0[0], y0[1], y1[0], y1[1], y2[0], y2[1], y3[0], y3[1]};
-    const uint32_t a = c < 64 ? (uint32_t)(1024 * tkn + 16 * (c ^ chunk_swz(tkn)))
-                              : (uint32_t)(kRopeBase + 128 * tkn + 16 * ((c - 64) ^ chunk_swz(tkn)));
-    *(bf16x8_t*)(dst + a) = y;
-  }
-}
+//   chunk c >= 64 (rope) at kRopeBase + 128 t + 16 ((c - 64) ^ swz(t)),
+// with swz the XOR swizzle of the 16-byte chunks inside each 128-byte group,
+// by token: eight consecutive tokens get eight different values, and four
+// consecutive tokens differ in the 32-byte pair they select (the score
+// reads and the transposed V reads are bank-conflict free).
+__host__ __device__ constexpr int chunk_swz(int t) { return 2 * (t & 3) + ((t >> 2) & 1); }
 
 // QK A operand of this wave's i-th k-step (see the kernel for the layout).
 template <int kG>
@@ -431,16 +279,6 @@ __device__ __forceinline__ bf16x8_t pv_operand(const uint8_t* ks, uint32_t pv0, 
   return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// x * f for an accumulator element held in an AGPR, in place (VALU cannot
-// read AGPRs; keeping the operand constrained to an AGPR stops the compiler
-// from moving the whole accumulator to VGPRs around the rare rescale).
-__device__ __forceinline__ float acc_scale(float x, float f) {
-  float tmp;
-  asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-               : "+a"(x), "=&v"(tmp) : "v"(f));
-  return x;
-}
-
 // max over lanes l and l ^ 32 (the two halves of a wave hold the two token
 // halves of one query row)
 __device__ __forceinline__ float xor32_max(float x) {
@@ -452,425 +290,8 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Read an accumulator element held in an AGPR (keeps the compiler from
-// moving the whole accumulator to VGPRs for the epilogue).
-__device__ __forceinline__ float acc_read(float x) {
-  float r;
-  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
-  return r;
-}
-
-// Copy j of kCopies for a tile is issued after MFMA slot
-// floor(j * slots / kCopies) of the tile loop (slots: the QK MFMAs, then the
-// PV MFMAs); -1 for slots that issue none.
-__host__ __device__ constexpr int copy_at_slot(int slot, int slots, int copies) {
-  for (int j = 0; j < copies; ++j)
-    if (j * slots / copies == slot) return j;
-  return -1;
-}
-// Copy j of a tile: bf16 tiles move the rope tails (j = 0) and the 1 KB main
-// part of token 8 w + j - 1 (j >= 1); fp8 tiles move 1 KB slice j.
-template <bool kFp8>
-__device__ __forceinline__ void issue_copy(const DecodeParams& p, int j, int rows, uint32_t stage_lds) {
-  if constexpr (kFp8) {
-    switch (j) {
-      case 0: copy8<0, 1>(p, rows, stage_lds); break;
-      case 1: copy8<1, 2>(p, rows, stage_lds); break;
-      case 2: copy8<2, 3>(p, rows, stage_lds); break;
-      case 3: copy8<3, 4>(p, rows, stage_lds); break;
-      default: copy8<4, 5>(p, rows, stage_lds); break;
-    }
-  } else {
-    switch (j) {
-      case 0: copy_rope(p, rows, stage_lds); break;
-      case 1: copy_main<0, 1>(p, rows, stage_lds); break;
-      case 2: copy_main<1, 2>(p, rows, stage_lds); break;
-      case 3: copy_main<2, 3>(p, rows, stage_lds); break;
-      case 4: copy_main<3, 4>(p, rows, stage_lds); break;
-      case 5: copy_main<4, 5>(p, rows, stage_lds); break;
-      case 6: copy_main<5, 6>(p, rows, stage_lds); break;
-      case 7: copy_main<6, 7>(p, rows, stage_lds); break;
-      default: copy_main<7, 8>(p, rows, stage_lds); break;
-    }
-  }
-}
-
-template <int kDS, bool kFp8>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_stream_kernel(DecodeParams p) {
-  constexpr int kRG = 4 / kDS;                 // row groups of 32 rows
-  constexpr int kRowsBlk = 32 * kRG;
-  constexpr int kDb = (kDv / 32) / kDS;        // 32-dim blocks of this wave's V slice
-  // stages: copies in flight while one tile is computed, about the same bytes
-  // for both KV types (fp8 tiles are staged as stored and converted to one
-  // bf16 compute stage per tile)
-  constexpr int kNS = kFp8 ? 5 : 3;
-  constexpr int kStg = kFp8 ? kStageBytes8 : kStageBytes;   // bytes of a staged tile
-  constexpr int kCopies = kFp8 ? 5 : 9;                     // copies per wave per tile
-  constexpr int kWaitMax = (kNS - 2) * (kCopies + 1);       // ops after a tile's copies
-  constexpr int kAheadRows = 2 * kNS - 2;      // tiles whose row indices are fetched ahead
-  // QK: the kDS waves of a row group split the 36 k-steps; wave ds takes the
-  // k-steps kk with kk mod 4 in [kG ds, kG ds + kG) and sums the partial
-  // scores of all kDS waves in one fixed order (so they agree bit for bit)
-  constexpr int kG = 4 / kDS;
-  constexpr int kKS = 9 * kG;                  // k-steps per wave
-  // Q k-steps kept in LDS rather than VGPRs (with 32 rows x 512 dims of
-  // accumulators in AGPRs, this keeps the tile loop spill-free); read back
-  // once per tile
-  constexpr int kQInLds = kDS == 1 ? 12 : 0;
-  constexpr int kQRegSteps = kKS - kQInLds;
-  constexpr int kPvSteps = 2 * kDb;
-  constexpr int kAhead = 4;
-  static_assert(kAheadRows < kRing, "row ring too small");
-
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * kStg + (kFp8 ? kStageBytes : 0)];
-  __shared__ __attribute__((aligned(16))) int32_t ring[kRing * kTile];
-  __shared__ __attribute__((aligned(16))) uint8_t qlds[kQInLds > 0 ? 4 * kQInLds * 64 * 16 : 16];
-  __shared__ __attribute__((aligned(16))) f32x4_t xbuf[kDS > 1 ? 4 * 4 * 64 : 1];   // [wave][4][lane]
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rg = wave % kRG, ds = wave / kRG;
-  const int tok = lane & 31, hi = lane >> 5;
-
-  // consecutive workgroups of the unit order run on one XCD (blocks are
-  // dealt to the 8 XCDs round robin), so the L2 of that XCD serves the
-  // repeated reads of a request's Q and KV
-  int g = blockIdx.x;
-  if ((p.grid & 7) == 0) g = (blockIdx.x & 7) * (p.grid >> 3) + (blockIdx.x >> 3);
-  const int G = ld_const(p.plan + 1);   // workgroups in use
-  if (g >= G) return;
-  const int Uw = ld_const(p.wg_ustart + g + 1) - ld_const(p.wg_ustart + g);
-  if (Uw <= 0) return;
-
-  const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_address(smem));
-  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_address(ring));
-  Cursor cf, ci, cc;
-  {
-    const int2 st = ld_const(p.wg_start + g);
-    cf.start(p, st.x, st.y);
-    ci = cf;
-    cc = cf;
-  }
-
-  // QK operand of this wave's i-th k-step kk = 4 (i / kG) + kG ds + i % kG
-  // (lane: token tok, chunk 2 kk + hi): kk < 32 at
-  // (qk0 ^ 32 (i % kG)) + 128 (i / kG), kk >= 32 (rope) at rope0 ^ 32 (i % kG)
-  // (the XOR only touches the swizzled chunk bits 4..6)
-  const uint32_t qk0 = (uint32_t)(1024 * tok + 16 * ((2 * kG * ds) ^ hi ^ chunk_swz(tok)));
-  const uint32_t rope0 = (uint32_t)(kRopeBase + 128 * tok + 16 * ((2 * kG * ds) ^ hi ^ chunk_swz(tok)));
-  // PV transposing loads: in 16-lane group g, lane 4r + q supplies dims
-  // 32 db + 16 (g & 1) + 4 q .. + 3 of token 16 m + 8 h + 4 (g >> 1) + r
-  // (h = first or second load); pv0 is its address for db = 0, and db = 1
-  // differs in bit 6 only (chunk 4 + y instead of y under the swizzle)
-  uint32_t pv0;
-  {
-    const int g16 = lane >> 4, r = (lane >> 2) & 3, q = lane & 3;
-    const int tl = 4 * (g16 >> 1) + r;
-    const int y = 2 * (g16 & 1) + (q >> 1);
-    pv0 = (uint32_t)(1024 * tl + 16 * (y ^ chunk_swz(tl)) + 8 * (q & 1) + 64 * kDb * ds);
-  }
-
-  uint8_t* const qmine = qlds + 16 * (kQInLds * 64 * wave + lane);
-  bf16x8_t qreg[kQRegSteps];
-  // ops: vector-memory operations this wave has issued; pos[i]: ops right
-  // after issuing the copies of tile t + i
-  int ops = 0;
-  int pos[kNS - 1];
-#pragma unroll
-  for (int i = 0; i < kNS - 1; ++i) pos[i] = 0;
-  int t = 0, stage = 0;   // stage holds tile t
-  while (t < Uw) {
-    const int b = cc.b, rb = cc.rb, tile0 = cc.tile, ntiles = cc.ntiles, cnt = cc.cnt;
-    const int n = min(ntiles - tile0, Uw - t);
-
-    // the piece's queries, this wave's k-steps (rows past the last query row
-    // read as zero); the last kQInLds k-steps go to this wave's LDS slot
-    const int row = rb * kRowsBlk + rg * 32 + tok;
-    const bool row_ok = row < p.rows;
-    {
-      const uint16_t* qrow = p.q + ((long long)b * p.rows + (row_ok ? row : 0)) * kDqk + 8 * hi;
-#pragma unroll
-      for (int i = 0; i < kKS; ++i) {
-        const int kk = 4 * (i / kG) + kG * ds + i % kG;
-        bf16x8_t x = *(const bf16x8_t*)(qrow + 16 * kk);
-        x = row_ok ? x : bf16x8_t{};
-        if (i < kQRegSteps) qreg[i] = x;
-        else *(bf16x8_t*)(qmine + 16 * 64 * (i - kQRegSteps)) = x;
-      }
-    }
-    if (t == 0) {
-      // row indices of the first tiles, in flight with the queries
-#pragma unroll
-      for (int k = 0; k < kAheadRows; ++k) {
-        if (k < Uw) {
-          if (k > 0) cf.advance(p);
-          fetch_rows(p, cf, ring_lds + 4 * kTile * (k % kRing));
-        }
-      }
-    }
-    // the query loads are the only loads the compiler tracks: waiting for
-    // everything here keeps its own waits out of the tile loop (for later
-    // pieces the tile copies in flight land meanwhile)
-    wait_vmcnt<0>();
-    if (t == 0) {
-      __syncthreads();
-      // the first kNS - 1 tiles
-#pragma unroll
-      for (int k = 0; k < kNS - 1; ++k) {
-        if (k < Uw) {
-          if (k > 0) ci.advance(p);
-          if constexpr (kFp8) issue_tile8(p, ci, smem_lds + kStg * k, ring + kTile * k);
-          else issue_tile(p, ci, smem_lds + kStg * k, ring + kTile * k);
-          ops += kCopies;
-          pos[k] = ops;
-        }
-      }
-    }
-    // owned tokens row (draft i) may see: t = j S + r <= L - q_len + i; the
-    // count is computed per draft index with scalar arithmetic and selected
-    int jvis = 0;
-    {
-      int L = ld_const(p.seq_lens + b);
-      L = L < 0 ? 0 : min(L, p.max_pages * kPage);
-      const int i = (row >= p.heads) + (row >= 2 * p.heads) + (row >= 3 * p.heads);
-      for (int k = 0; k < p.q_len; ++k) {
-        const int lim = L - p.q_len + k - p.shard;
-        const int jl = lim >= 0 ? min(cnt, lim / p.num_shards + 1) : 0;
-        jvis = i == k ? jl : jvis;
-      }
-    }
-    // tiles that end at or before jvis_min need no visibility mask (rows
-    // past the last query row are never written and do not count)
-    int jvis_min = row_ok ? jvis : INT_MAX;
-    jvis_min = min(jvis_min, __shfl_xor(jvis_min, 1));
-    jvis_min = min(jvis_min, __shfl_xor(jvis_min, 2));
-    jvis_min = min(jvis_min, __shfl_xor(jvis_min, 4));
-    jvis_min = min(jvis_min, __shfl_xor(jvis_min, 8));
-    jvis_min = min(jvis_min, __shfl_xor(jvis_min, 16));
-    jvis_min = min(jvis_min, __shfl_xor(jvis_min, 32));
-    jvis_min = __builtin_amdgcn_readfirstlane(jvis_min);
-
-    f32x16_t o[kDb];
-#pragma unroll
-    for (int db = 0; db < kDb; ++db) o[db] = f32x16_t{};
-    float m_ref = kNegInf, l_sum = 0.f;
-
-    for (int k = 0; k < n; ++k, ++t) {
-      // tile t has landed for this wave, then for all waves; the stage of
-      // tile t - 1 is free
-      wait_vm_le<kWaitMax>(ops - pos[0]);
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i + 1 < kNS - 1; ++i) pos[i] = pos[i + 1];
-      // row indices kAheadRows tiles ahead: issued before this iteration's
-      // tile copies, so that waiting for those copies covers them too
-      if (t + kAheadRows < Uw) {
-        cf.advance(p);
-        fetch_rows(p, cf, ring_lds + 4 * kTile * ((t + kAheadRows) % kRing));
-        ops += 1;
-      }
-      // table entry of this tile's token `tok`, and the rows of tile
-      // t + kNS - 1, whose copies go into the stage of tile t - 1 spread over
-      // the MFMA sequences below (a burst would stall on the memory queue)
-      const int raw_c = ring[kTile * (t % kRing) + tok];
-      const bool more = t + kNS - 1 < Uw;
-      const uint32_t st_next = smem_lds + kStg * (stage == 0 ? kNS - 1 : stage - 1);   // tile t - 1's
-      int rows_next = 0;
-      if (more) {
-        ci.advance(p);
-        const int32_t* rs = ring + kTile * ((t + kNS - 1) % kRing);
-        rows_next = kFp8 ? tile_rows8(p, ci, rs) : tile_rows(p, ci, rs);
-      }
-
-      if constexpr (kFp8) {
-        // the compute stage was last read by tile t - 1 (done at the barrier)
-        convert_tile8(smem + kStg * stage, smem + kNS * kStg);
-        __syncthreads();
-      }
-      const uint8_t* ks = kFp8 ? smem + kNS * kStg : smem + kStageBytes * stage;
-      const int tile = tile0 + k;
-      const int jt = tile * kTile;
-      // tokens whose page is outside the pool poison their scores
-      const int rr = resolve_row(p, tile, cnt, tok, raw_c);
-      const uint64_t bad = __ballot(lane < kTile && rr == kRowBad);
-
-      // S^T[token][row] over this wave's k-steps; K operands are read kAhead
-      // steps ahead of their MFMA
-      bf16x8_t ka[kAhead];
-#pragma unroll
-      for (int u = 0; u < kAhead; ++u) ka[u] = qk_operand<kG>(ks, qk0, rope0, u);
-      f32x16_t s = f32x16_t{};
-#pragma unroll
-      for (int i = 0; i < kKS; ++i) {
-        const bf16x8_t a = ka[i % kAhead];
-        if (i + kAhead < kKS) {
-          const int u = i + kAhead;
-          ka[i % kAhead] = qk_operand<kG>(ks, qk0, rope0, u);
-        }
-        const bf16x8_t qb = i < kQRegSteps ? qreg[i < kQRegSteps ? i : 0]
-                                           : *(const bf16x8_t*)(qmine + 16 * 64 * (i - kQRegSteps));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb, s, 0, 0, 0);
-        constexpr int kSlots = kKS + kPvSteps;
-        if (copy_at_slot(i, kSlots, kCopies) >= 0 && more) {
-          issue_copy<kFp8>(p, copy_at_slot(i, kSlots, kCopies), rows_next, st_next);
-          ops += 1;
-        }
-      }
-      if constexpr (kDS == 2) {
-        // the partner wave's partial scores; both waves form s0 + s1
-        // (addition commutes exactly), so they agree bit for bit
-        f32x4_t* mine = xbuf + (wave * 4) * 64 + lane;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) mine[64 * q] = f32x4_t{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
-        __syncthreads();
-        const f32x4_t* src = xbuf + (((1 - ds) * kRG + rg) * 4) * 64 + lane;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4_t v = src[64 * q];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) s[4 * q + e] += v[e];
-        }
-      } else if constexpr (kDS > 2) {
-        // sum the row group's partial scores in wave order
-        f32x4_t* mine = xbuf + (wave * 4) * 64 + lane;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) mine[64 * q] = f32x4_t{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
-        __syncthreads();
-        f32x16_t tot = f32x16_t{};
-#pragma unroll
-        for (int d = 0; d < kDS; ++d) {
-          const f32x4_t* src = xbuf + ((d * kRG + rg) * 4) * 64 + lane;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x4_t v = src[64 * q];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) tot[4 * q + e] += v[e];
-          }
-        }
-        s = tot;
-      }
-
-      // online softmax in base 2 (this lane: one row, 16 tokens: value v is
-      // token 8 (v >> 2) + 4 hi + (v & 3)); the max is taken on the raw
-      // scores (scaling by a positive factor commutes with it exactly) and
-      // the scale is folded into the exponent's FMA
-      float tmax = kNegInf;
-      if (jt + kTile <= jvis_min && bad == 0) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[v]);
-      } else {
-        // masks shifted by 4 hi once so each test is against a constant
-        const int lim = jvis - jt - 4 * hi;
-        const uint32_t badl = (uint32_t)bad >> (4 * hi);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int c = 8 * (v >> 2) + (v & 3);
-          float x = c < lim ? s[v] : kNegInf;
-          x = ((badl >> c) & 1u) ? __builtin_nanf("") : x;
-          s[v] = x;
-          tmax = fmaxf(tmax, x);
-        }
-      }
-      tmax = xor32_max(tmax) * p.scale_log2;
-      const bool grow = m_ref != kNegInf && tmax > m_ref + kRescaleSlack;
-      if (__builtin_expect(__ballot(grow) != 0, 0)) {
-        const float f = grow ? exp2_fast(m_ref - tmax) : 1.f;
-        l_sum *= f;
-        // o[.][v] belongs to row 8 (v >> 2) + 4 hi + (v & 3), whose factor
-        // sits in that row's lane
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float fv = __shfl(f, 8 * (v >> 2) + 4 * hi + (v & 3));
-#pragma unroll
-          for (int db = 0; db < kDb; ++db) o[db][v] = acc_scale(o[db][v], fv);
-        }
-        m_ref = grow ? tmax : m_ref;
-      }
-      m_ref = m_ref == kNegInf ? tmax : m_ref;
-      const float neg_m = m_ref == kNegInf ? 0.f : -m_ref;
-      bf16x8_t pb[2];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float pv = exp2_fast(__builtin_fmaf(s[v], p.scale_log2, neg_m));
-        l_sum += pv;
-        pb[v >> 3][v & 7] = (__bf16)pv;
-      }
-
-      // O[row][dim] += P[row][token] V[token][dim] over this wave's dims: the
-      // P registers (lane = row) are the A operand and the transposed V reads
-      // (lane = dim) the B operand, both with the same token order in k; the
-      // accumulator then holds 32 consecutive dims across lanes, so the
-      // output stores write whole lines
-      bf16x8_t va[kAhead];
-#pragma unroll
-      for (int u = 0; u < kAhead; ++u) va[u] = pv_operand(ks, pv0, u);
-#pragma unroll
-      for (int st = 0; st < kPvSteps; ++st) {
-        const bf16x8_t a = va[st % kAhead];
-        if (st + kAhead < kPvSteps) va[st % kAhead] = pv_operand(ks, pv0, st + kAhead);
-        o[st >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb[st & 1], a, o[st >> 1], 0, 0, 0);
-        constexpr int kSlots = kKS + kPvSteps;
-        if (copy_at_slot(kKS + st, kSlots, kCopies) >= 0 && more) {
-          issue_copy<kFp8>(p, copy_at_slot(kKS + st, kSlots, kCopies), rows_next, st_next);
-          ops += 1;
-        }
-      }
-      if (more) pos[kNS - 2] = ops;
-      stage = stage + 1 == kNS ? 0 : stage + 1;
-    }
-
-    // piece epilogue: o[db][v] is row 8 (v >> 2) + 4 hi + (v & 3) of the
-    // row group, dim 32 (kDb ds + db) + (lane & 31)
-    const float l_tot = xor32_sum(l_sum);
-    const bool any = l_tot > 0.f || l_tot != l_tot;
-    const float inv = any ? p.out_scale / l_tot : 0.f;
-    const float lse2 = any ? m_ref + log2_fast(l_tot) : kNegInf;
-    const bool single = tile0 == 0 && n == ntiles;
-    const int row0 = rb * kRowsBlk + rg * 32;          // first row of the row group
-    const int dim = 32 * kDb * ds + (lane & 31);
-    long long base;                                    // element index of (row0, dim)
-    if (single) {
-      base = ((long long)b * p.rows + row0) * kDv + dim;
-    } else {
-      const int4 si = ld_const(p.seg_info + b * p.row_blocks + rb);
-      base = ((long long)(si.x + g - si.z) * kRowsBlk + rg * 32) * kDv + dim;
-    }
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = 8 * (v >> 2) + 4 * hi + (v & 3);
-      const float iv = __shfl(inv, r);
-      if (row0 + r < p.rows) {
-        const long long e0 = base + (long long)r * kDv;
-        if (single && !p.out_bf16) {
-          float* dst = (float*)p.out + e0;
-#pragma unroll
-          for (int db = 0; db < kDb; ++db) dst[32 * db] = acc_read(o[db][v]) * iv;
-        } else {
-          __bf16* dst = single ? (__bf16*)p.out + e0 : (__bf16*)p.spart_o + e0;
-#pragma unroll
-          for (int db = 0; db < kDb; ++db) dst[32 * db] = (__bf16)(acc_read(o[db][v]) * iv);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);   // one row at a time: short live ranges
-    }
-    if (row_ok && ds == 0 && hi == 0) {
-      if (single) {
-        p.lse[(long long)b * p.rows + row] = p.lse_base2 ? lse2 : lse2 * kLn2;
-      } else {
-        const int4 si = ld_const(p.seg_info + b * p.row_blocks + rb);
-        p.spart_lse[(long long)(si.x + g - si.z) * kRowsBlk + (row - rb * kRowsBlk)] = lse2;
-      }
-    }
-    if (t < Uw) {
-      cc.tile = ntiles - 1;
-      cc.advance(p);
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
-// software-pipelined attention over bf16 KV
+// tile rows and copies
 // ---------------------------------------------------------------------------
 // Rows that tokens read instead of the pool: zeros for tokens past a
 // request's owned range (finite, and masked by the visibility limit) and NaN
@@ -960,7 +381,7 @@ __device__ __forceinline__ const uint8_t* token_src(const DecodeParams& p, const
   }
 }
 
-// Copy j of a bf16 tile into a stage (layout as for the streaming kernel):
+// Copy j of a bf16 tile into a stage (the layout above):
 // j = 0 moves the eight rope tails of the wave's tokens, j = 1 + i the 1 KB
 // main part of token 8 w + i (one row per copy, as a scalar base).
 template <int kJ>
@@ -991,446 +412,6 @@ __device__ __forceinline__ void copy_tile_part_rt(int j, const uint8_t* src, uin
     case 7: copy_tile_part<7>(src, stage_lds, wave); break;
     default: copy_tile_part<8>(src, stage_lds, wave); break;
   }
-}
-
-// The tile loop overlaps two tiles: while the VALU computes tile k's softmax,
-// the MFMAs accumulate tile k - 1's P V. Four stages hold tile k - 1 (V),
-// tile k (K) and two tiles in flight. Every tile barrier issues exactly the
-// nine copies of the tile two ahead (from the zero row past the workgroup's
-// last unit), so the wait before it is a constant vmcnt(9): the only
-// vector-memory operations between two tile barriers are those copies (query
-// loads and output stores are drained at piece starts).
-template <int kDS, bool kLocal>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_pipe_kernel(DecodeParams p) {
-  constexpr int kRG = 4 / kDS;                 // row groups of 32 rows
-  constexpr int kRowsBlk = 32 * kRG;
-  constexpr int kDb = (kDv / 32) / kDS;        // 32-dim blocks of this wave's V slice
-  constexpr int kNS = 4;
-  constexpr int kCopies = 9;
-  constexpr int kG = 4 / kDS;
-  constexpr int kKS = 9 * kG;                  // QK k-steps per wave
-  constexpr int kPvSteps = 2 * kDb;
-  constexpr int kAhead = 4;
-
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNS * kStageBytes];
-  __shared__ __attribute__((aligned(16))) f32x4_t xbuf[4 * 4 * 64];   // [wave][4][lane]
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rg = wave % kRG, ds = wave / kRG;
-  const int tok = lane & 31, hi = lane >> 5;
-
-  // consecutive workgroups of the unit order run on one XCD (blocks are
-  // dealt to the 8 XCDs round robin), so the L2 of that XCD serves the
-  // repeated reads of a request's Q and KV
-  int g = blockIdx.x;
-  if ((p.grid & 7) == 0) g = (blockIdx.x & 7) * (p.grid >> 3) + (blockIdx.x >> 3);
-  // the start record: one round of scalar loads, then one for the table
-  // entries of the first two tiles, before the first copies
-  const int32_t* rec = p.wg_rec + (long long)g * kRecInts;
-  const int Uw = ld_const(rec);
-  const int rec_seg = ld_const(rec + 1), rec_tile = ld_const(rec + 2), rec_cnt = ld_const(rec + 3);
-  const int rec_seg1 = ld_const(rec + 4), rec_cnt1 = ld_const(rec + 5);
-  if (Uw <= 0) return;
-  const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_address(smem));
-  const uint32_t qk0 = (uint32_t)(1024 * tok + 16 * ((2 * kG * ds) ^ hi ^ chunk_swz(tok)));
-  const uint32_t rope0 = (uint32_t)(kRopeBase + 128 * tok + 16 * ((2 * kG * ds) ^ hi ^ chunk_swz(tok)));
-  uint32_t pv0;
-  {
-    const int g16 = lane >> 4, r = (lane >> 2) & 3, q = lane & 3;
-    const int tl = 4 * (g16 >> 1) + r;
-    const int y = 2 * (g16 & 1) + (q >> 1);
-    pv0 = (uint32_t)(1024 * tl + 16 * (y ^ chunk_swz(tl)) + 8 * (q & 1) + 64 * kDb * ds);
-  }
-
-  // cc: the piece being computed; cl: the next tile to copy
-  // cc: the piece being computed; cl: the next tile to copy, te its table
-  // entries. The first two tiles' cursors come from the record (the second
-  // one may start the next segment).
-  Cursor cc, cl;
-  cc.start_known(p, rec_seg, rec_tile, rec_cnt);
-  cl = cc;
-  if (1 < Uw) {
-    if (cl.tile + 1 < cl.ntiles) ++cl.tile;
-    else cl.start_known(p, rec_seg1, 0, rec_cnt1);
-  }
-  {
-    TileEntries te0, te1;
-    load_entries<kLocal>(p, cc, wave, te0);
-    if (1 < Uw) load_entries<kLocal>(p, cl, wave, te1);
-    const uint8_t* src0 = token_src<kLocal>(p, cc, true, te0, wave);
-#pragma unroll
-    for (int j = 0; j < kCopies; ++j) copy_tile_part_rt(j, src0, smem_lds, wave);
-    const uint8_t* src1 = token_src<kLocal>(p, cl, 1 < Uw, te1, wave);
-#pragma unroll
-    for (int j = 0; j < kCopies; ++j) copy_tile_part_rt(j, src1, smem_lds + kStageBytes, wave);
-  }
-  int ncopied = 2;
-  TileEntries te;   // entries of tile ncopied, loaded a barrier ahead
-  if (2 < Uw) {
-    cl.advance(p);
-    load_entries<kLocal>(p, cl, wave, te);
-  }
-
-  bf16x8_t qreg[kKS];
-  const uint8_t* csrc = nullptr;   // copies of this iteration: sources, stage
-  uint32_t cst = 0;
-  // tile barrier: the tile that the next QK reads has landed in every wave,
-  // and the stage of the tile two back is free for tile ncopied; the table
-  // entries of the tile after it are loaded here for the next barrier
-  auto tile_barrier = [&]() {
-    wait_vmcnt<kCopies>();
-    __syncthreads();
-    csrc = token_src<kLocal>(p, cl, ncopied < Uw, te, wave);
-    cst = __builtin_amdgcn_readfirstlane(smem_lds + kStageBytes * (ncopied & (kNS - 1)));
-    ++ncopied;
-    if (ncopied < Uw) {
-      cl.advance(p);
-      load_entries<kLocal>(p, cl, wave, te);
-    }
-  };
-  // The MFMAs of one iteration form a sequence of kSlots; copy j of the
-  // iteration's tile goes out after MFMA copy_slot(j).
-  constexpr int kSlots = kKS + kPvSteps;
-  auto after_mfma = [&](int m) {
-    if (copy_at_slot(m, kSlots, kCopies) >= 0) copy_tile_part_rt(copy_at_slot(m, kSlots, kCopies), csrc, cst, wave);
-  };
-  // scores: S^T of a tile over this wave's k-steps, one MFMA per step, K
-  // operands read kAhead steps ahead
-  bf16x8_t ka[kAhead];
-  f32x16_t acc;
-  auto qk_start = [&](const uint8_t* ks) {
-#pragma unroll
-    for (int u = 0; u < kAhead; ++u) ka[u] = qk_operand<kG>(ks, qk0, rope0, u);
-    acc = f32x16_t{};
-  };
-  auto qk_step = [&](const uint8_t* ks, int i) {
-    const bf16x8_t a = ka[i % kAhead];
-    if (i + kAhead < kKS) ka[i % kAhead] = qk_operand<kG>(ks, qk0, rope0, i + kAhead);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[i], acc, 0, 0, 0);
-  };
-  // this wave's partial scores to the exchange buffer
-  auto xchg_write = [&](const f32x16_t& a) {
-    f32x4_t* mine = xbuf + (wave * 4) * 64 + lane;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) mine[64 * q] = f32x4_t{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
-  };
-  // the row group's summed scores (after the exchange barrier): both waves
-  // of a pair form s0 + s1 (addition commutes exactly); four waves sum in
-  // wave order from the buffer
-  auto xchg_sum = [&](const f32x16_t& a) {
-    f32x16_t r;
-    if constexpr (kDS == 2) {
-      const f32x4_t* src = xbuf + (((1 - ds) * kRG + rg) * 4) * 64 + lane;
-      f32x4_t v[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = src[64 * q];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) r[4 * q + e] = a[4 * q + e] + v[q][e];
-    } else {
-      r = f32x16_t{};
-#pragma unroll
-      for (int d = 0; d < kDS; ++d) {
-        const f32x4_t* src = xbuf + ((d * kRG + rg) * 4) * 64 + lane;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4_t v = src[64 * q];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) r[4 * q + e] += v[e];
-        }
-      }
-    }
-    return r;
-  };
-  // accumulation O^T[dim][row] += V^T[dim][token] P^T[token][row] over
-  // this wave's dims (transposed V reads the A operand, the P registers the
-  // B operand, both with the same token order in k); step s2 covers dim
-  // block s2 % kDb and token half s2 / kDb, so consecutive MFMAs update
-  // different accumulators
-  auto pv_index = [](int s2) { return 2 * (s2 % kDb) + s2 / kDb; };
-  bf16x8_t va[kAhead];
-
-  int t = 0;   // unit index of the current piece's first tile
-  while (t < Uw) {
-    const int b = cc.b, rb = cc.rb, tile0 = cc.tile, ntiles = cc.ntiles, cnt = cc.cnt;
-    const int n = min(ntiles - tile0, Uw - t);
-    const int row = rb * kRowsBlk + rg * 32 + tok;
-    const bool row_ok = row < p.rows;
-    {
-      const uint16_t* qrow = p.q + ((long long)b * p.rows + (row_ok ? row : 0)) * kDqk + 8 * hi;
-#pragma unroll
-      for (int i = 0; i < kKS; ++i) {
-        const int kk = 4 * (i / kG) + kG * ds + i % kG;
-        const bf16x8_t x = *(const bf16x8_t*)(qrow + 16 * kk);
-        qreg[i] = row_ok ? x : bf16x8_t{};
-      }
-    }
-    // the query loads are the only loads the compiler tracks: waiting for
-    // everything here keeps its own waits out of the tile loop
-    wait_vmcnt<0>();
-    // owned tokens row (draft i) may see: t = j S + r <= L - q_len + i
-    int jvis = 0;
-    {
-      int L = ld_const(p.seq_lens + b);
-      L = L < 0 ? 0 : min(L, p.max_pages * kPage);
-      const int i = (row >= p.heads) + (row >= 2 * p.heads) + (row >= 3 * p.heads);
-      for (int k = 0; k < p.q_len; ++k) {
-        const int lim = L - p.q_len + k - p.shard;
-        const int jl = lim >= 0 ? min(cnt, lim / p.num_shards + 1) : 0;
-        jvis = i == k ? jl : jvis;
-      }
-    }
-
-    f32x16_t o[kDb];
-#pragma unroll
-    for (int db = 0; db < kDb; ++db) o[db] = f32x16_t{};
-    float m_ref = kNegInf, l_sum = 0.f;
-
-    auto pv_start = [&](const uint8_t* ks) {
-#pragma unroll
-      for (int u = 0; u < kAhead; ++u) va[u] = pv_operand(ks, pv0, pv_index(u));
-    };
-    auto pv_step = [&](const uint8_t* ks, const bf16x8_t (&pb)[2], int s2) {
-      const int st = pv_index(s2);
-      const bf16x8_t a = va[s2 % kAhead];
-      if (s2 + kAhead < kPvSteps) va[s2 % kAhead] = pv_operand(ks, pv0, pv_index(s2 + kAhead));
-      o[st >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st & 1], o[st >> 1], 0, 0, 0);
-    };
-    // online softmax of tile k in base 2 (lane: one row, 16 tokens; value v
-    // is token 8 (v >> 2) + 4 hi + (v & 3)); tokens at or past the row's
-    // visibility limit are masked; the max is taken on the raw scores
-    // (scaling by a positive factor commutes with it exactly) and the scale
-    // is folded into the exponent's FMA. Split into kQ1 chunks that run
-    // between the score MFMAs of the next tile: chunks 0 and 1 mask and take
-    // the max (and move the reference), the rest exponentiate.
-    constexpr int kQ1 = kKS / 2;            // score steps before the accumulation starts
-    constexpr int kP1 = kPvSteps / 2;       // accumulation steps before the exchange
-    static_assert(kQ1 >= 3, "softmax chunks");
-    float f = 1.f, tmax = kNegInf, neg_m = 0.f;
-    bool grow = false;
-    int lim = 0;
-    auto softmax_chunk = [&](int c, int k, f32x16_t& sc, bf16x8_t (&pb)[2]) {
-      if (c == 0) {
-        lim = jvis - (tile0 + k) * kTile - 4 * hi;
-        tmax = kNegInf;
-      }
-      if (c < 2) {
-#pragma unroll
-        for (int v = 8 * c; v < 8 * c + 8; ++v) {
-          const int cc_ = 8 * (v >> 2) + (v & 3);
-          sc[v] = cc_ < lim ? sc[v] : kNegInf;
-          tmax = fmaxf(tmax, sc[v]);
-        }
-      }
-      if (c == 1) {
-        const float tm = xor32_max(tmax) * p.scale_log2;
-        grow = m_ref != kNegInf && tm > m_ref + kRescaleSlack;
-        f = grow ? exp2_fast(m_ref - tm) : 1.f;
-        l_sum *= f;
-        m_ref = grow || m_ref == kNegInf ? tm : m_ref;
-        neg_m = m_ref == kNegInf ? 0.f : -m_ref;
-      }
-      if (c >= 2) {
-        constexpr int kE = kQ1 - 2;         // exponent chunks
-        const int v0 = (c - 2) * 16 / kE, v1 = (c - 1) * 16 / kE;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          if (v >= v0 && v < v1) {
-            const float pr = exp2_fast(__builtin_fmaf(sc[v], p.scale_log2, neg_m));
-            l_sum += pr;
-            pb[v >> 3][v & 7] = (__bf16)pr;
-          }
-        }
-      }
-      if (c == kQ1 - 1) {
-        // the results exist before the rescale branch (otherwise they are
-        // sunk below it, away from the MFMAs they overlap)
-        asm volatile("" :: "v"(l_sum), "v"(pb[0]), "v"(pb[1]));
-      }
-    };
-    // the rare rescale of the accumulators (every value a lane holds
-    // belongs to its own row)
-    auto rescale = [&]() {
-      if (__builtin_expect(__ballot(grow) != 0, 0)) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-#pragma unroll
-          for (int db = 0; db < kDb; ++db) o[db][v] = acc_scale(o[db][v], f);
-      }
-    };
-
-    // tile 0: its scores; the copies of its barrier all go out here
-    f32x16_t s_cur;
-    {
-      tile_barrier();
-      const uint8_t* ksq = smem + kStageBytes * (t & (kNS - 1));
-      qk_start(ksq);
-#pragma unroll
-      for (int i = 0; i < kKS; ++i) {
-        qk_step(ksq, i);
-        after_mfma(i);
-      }
-      xchg_write(acc);
-      __syncthreads();
-      s_cur = xchg_sum(acc);
-#pragma unroll
-      for (int m = kKS; m < kSlots; ++m) after_mfma(m);
-    }
-    // tiles k + 1 <= n - 1: the scores of tile k + 1 run with the softmax
-    // and then the accumulation of tile k
-    for (int k = 0; k + 1 < n; ++k) {
-      tile_barrier();
-      const uint8_t* ksq = smem + kStageBytes * ((t + k + 1) & (kNS - 1));
-      const uint8_t* ksv = smem + kStageBytes * ((t + k) & (kNS - 1));
-      bf16x8_t pb[2];
-      qk_start(ksq);
-#pragma unroll
-      for (int i = 0; i < kQ1; ++i) {
-        qk_step(ksq, i);
-        after_mfma(i);
-        softmax_chunk(i, k, s_cur, pb);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      rescale();
-      pv_start(ksv);
-      // the remaining score steps alternate with the first accumulation
-      // steps (independent MFMAs back to back)
-      constexpr int kMix = (kKS - kQ1) > kP1 ? (kKS - kQ1) : kP1;
-#pragma unroll
-      for (int j = 0; j < kMix; ++j) {
-        if (kQ1 + j < kKS) {
-          qk_step(ksq, kQ1 + j);
-          after_mfma(kQ1 + 2 * j);
-        }
-        if (j < kP1) {
-          pv_step(ksv, pb, j);
-          after_mfma(kQ1 + 2 * j + 1);
-        }
-      }
-      xchg_write(acc);
-      __syncthreads();
-      if constexpr (kDS == 2) {
-        // the partner's partial scores are read first and added after the
-        // accumulation steps, whose MFMAs cover the reads' latency
-        const f32x4_t* src = xbuf + (((1 - ds) * kRG + rg) * 4) * 64 + lane;
-        f32x4_t pv4[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) pv4[q] = src[64 * q];
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int s2 = kP1; s2 < kPvSteps; ++s2) {
-          pv_step(ksv, pb, s2);
-          after_mfma(kKS + s2);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) s_cur[4 * q + e] = acc[4 * q + e] + pv4[q][e];
-      } else {
-#pragma unroll
-        for (int s2 = kP1; s2 < kPvSteps; ++s2) {
-          pv_step(ksv, pb, s2);
-          after_mfma(kKS + s2);
-        }
-        s_cur = xchg_sum(acc);
-      }
-      // keep the accumulators in AGPRs across iterations (left to itself
-      // the register allocator moves them through VGPRs and spills)
-#pragma unroll
-      for (int db = 0; db < kDb; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) asm volatile("" : "+a"(o[db][v]));
-    }
-    // the last tile of the piece
-    {
-      bf16x8_t pb[2];
-#pragma unroll
-      for (int c = 0; c < kQ1; ++c) softmax_chunk(c, n - 1, s_cur, pb);
-      rescale();
-      const uint8_t* ksv = smem + kStageBytes * ((t + n - 1) & (kNS - 1));
-      pv_start(ksv);
-#pragma unroll
-      for (int s2 = 0; s2 < kPvSteps; ++s2) pv_step(ksv, pb, s2);
-    }
-
-    // piece epilogue: the accumulators hold O^T (V^T is the A operand): lane
-    // l has row rg * 32 + (l & 31) and o[db][v] is its dim
-    // 32 (kDb ds + db) + 8 (v >> 2) + 4 hi + (v & 3)
-    const float l_tot = xor32_sum(l_sum);
-    const bool any = l_tot > 0.f || l_tot != l_tot;
-    const float inv = any ? p.out_scale / l_tot : 0.f;
-    const float lse2 = any ? m_ref + log2_fast(l_tot) : kNegInf;
-    const bool single = tile0 == 0 && n == ntiles;
-    const int row0 = rb * kRowsBlk + rg * 32;          // first row of the row group
-    if (single && !p.out_bf16) {
-      // f32 output: four consecutive dims per lane and store
-      if (row_ok) {
-        float* dst = (float*)p.out + ((long long)b * p.rows + row) * kDv + 32 * kDb * ds + 4 * hi;
-#pragma unroll
-        for (int db = 0; db < kDb; ++db)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x4_t x = {acc_read(o[db][4 * q]) * inv, acc_read(o[db][4 * q + 1]) * inv,
-                               acc_read(o[db][4 * q + 2]) * inv, acc_read(o[db][4 * q + 3]) * inv};
-            *(f32x4_t*)(dst + 32 * db + 8 * q) = x;
-          }
-      }
-    } else {
-      // bf16 output through LDS: each wave writes its 32 rows x (kDb * 32)
-      // dims row-major (rows padded to 528 bytes) into the stages of the
-      // piece's last two tiles, free once every wave has passed this
-      // barrier, and stores whole rows (16 bytes a lane)
-      constexpr int kRowPitch = 528;
-      static_assert(2 * 32 * kRowPitch <= kStageBytes, "two waves' rows per stage");
-      __syncthreads();
-      uint8_t* tb = smem + kStageBytes * ((t + n - 1 - (wave >> 1)) & (kNS - 1)) + (wave & 1) * 32 * kRowPitch;
-      typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-#pragma unroll
-      for (int db = 0; db < kDb; ++db)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const bf16x4_t x = {(__bf16)(acc_read(o[db][4 * q]) * inv), (__bf16)(acc_read(o[db][4 * q + 1]) * inv),
-                              (__bf16)(acc_read(o[db][4 * q + 2]) * inv), (__bf16)(acc_read(o[db][4 * q + 3]) * inv)};
-          *(bf16x4_t*)(tb + kRowPitch * tok + 2 * (32 * db + 8 * q + 4 * hi)) = x;
-        }
-      __bf16* obase;
-      long long pitch_rows;
-      if (single) {
-        obase = (__bf16*)p.out + ((long long)b * p.rows + row0) * kDv;
-      } else {
-        const int4 si = ld_const(p.seg_info + b * p.row_blocks + rb);
-        obase = (__bf16*)p.spart_o + ((long long)(si.x + g - si.z) * kRowsBlk + rg * 32) * kDv;
-      }
-      (void)pitch_rows;
-      constexpr int kLanesPerRow = kDb * 32 / 8;        // 16-byte pieces of a row's slice
-      constexpr int kRowsPerStore = 64 / kLanesPerRow;
-      const int rr0 = lane / kLanesPerRow, cc = lane % kLanesPerRow;
-#pragma unroll
-      for (int i = 0; i < 32 / kRowsPerStore; ++i) {
-        const int rr = kRowsPerStore * i + rr0;
-        const bf16x8_t x = *(const bf16x8_t*)(tb + kRowPitch * rr + 16 * cc);
-        if (row0 + rr < p.rows) *(bf16x8_t*)(obase + (long long)rr * kDv + 32 * kDb * ds + 8 * cc) = x;
-      }
-    }
-    if (row_ok && ds == 0 && hi == 0) {
-      if (single) {
-        p.lse[(long long)b * p.rows + row] = p.lse_base2 ? lse2 : lse2 * kLn2;
-      } else {
-        const int4 si = ld_const(p.seg_info + b * p.row_blocks + rb);
-        p.spart_lse[(long long)(si.x + g - si.z) * kRowsBlk + (row - rb * kRowsBlk)] = lse2;
-      }
-    }
-    t += n;
-    if (t < Uw) {
-      cc.tile = ntiles - 1;
-      cc.advance(p);
-    }
-  }
-  // no copy may still be writing this workgroup's LDS when it exits
-  wait_vmcnt<0>();
 }
 
 // ---------------------------------------------------------------------------
@@ -2027,10 +1008,6 @@ __global__ __launch_bounds__(256) void stream_combine_kernel(DecodeParams p) {
 
 }  // namespace
 
-// 64-row blocks run the warp-specialised kernel (fp8 KV too)
-constexpr bool kUseWs = true;
-constexpr bool kUseWsFp8 = true;
-
 hipError_t launch_decode_plan(const DecodeParams& p, hipStream_t stream) {
   if (p.batch == 0) return hipSuccess;
   hipLaunchKernelGGL(stream_plan_kernel, dim3(1), dim3(1024), 0, stream, p);
@@ -2047,22 +1024,13 @@ hipError_t launch_decode_stream(const DecodeParams& p, bool run_plan, hipEvent_t
   void* args[] = {const_cast<DecodeParams*>(&p)};
   const void* fn;
   const bool local = p.local_kv_indices != nullptr;
-  const bool ws = kUseWs && p.rows_blk == kWsRows && (!p.kv_fp8 || kUseWsFp8);
-  if (p.kv_fp8 && !ws)
-    fn = p.rows_blk == 32 ? reinterpret_cast<const void*>(&attn_stream_kernel<4, true>)
-                          : reinterpret_cast<const void*>(&attn_stream_kernel<2, true>);
-  else if (p.kv_fp8)
+  if (p.kv_fp8)
     fn = local ? reinterpret_cast<const void*>(&attn_ws_kernel<true, true>)
                : reinterpret_cast<const void*>(&attn_ws_kernel<false, true>);
-  else if (ws)
+  else
     fn = local ? reinterpret_cast<const void*>(&attn_ws_kernel<true, false>)
                : reinterpret_cast<const void*>(&attn_ws_kernel<false, false>);
-  else
-    fn = p.rows_blk == 32 ? (local ? reinterpret_cast<const void*>(&attn_pipe_kernel<4, true>)
-                                   : reinterpret_cast<const void*>(&attn_pipe_kernel<4, false>))
-                          : (local ? reinterpret_cast<const void*>(&attn_pipe_kernel<2, true>)
-                                   : reinterpret_cast<const void*>(&attn_pipe_kernel<2, false>));
-  err = hipExtLaunchKernel(fn, dim3(p.grid), dim3(ws ? 512 : 256), args, 0, stream, ev_begin, ev_end, 0);
+  err = hipExtLaunchKernel(fn, dim3(p.grid), dim3(512), args, 0, stream, ev_begin, ev_end, 0);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(stream_combine_kernel, dim3(p.batch, (p.rows + 3) / 4), dim3(256), 0, stream, p);
   return hipGetLastError();
