@@ -453,13 +453,7 @@ def main() -> int:
         roof = dict(bound="hbm", achieved=res["attn_kernel_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=res["attn_kernel_gbs"] / HBM_PEAK_GBS)
     roof["traffic"] = traffic_from_profile(wl.name)
-    ds = 4 if wl.heads * wl.q_len <= 32 else 2
-    if ds == 2:
-        kname = "attn_ws_kernel<local indices, %s KV> (mla_stream.hip)" % wl.kv_dtype
-    elif wl.kv_dtype == "fp8":
-        kname = "attn_stream_kernel<4, fp8> (mla_stream.hip)"
-    else:
-        kname = "attn_pipe_kernel<4, local indices> (mla_stream.hip)"
+    kname = "attn_ws_kernel<local indices, %s KV> (mla_stream.hip)" % wl.kv_dtype
     roof["kernel"] = kname + ", mean of %d launches" % (args.steps * wl.shards)
     roof["mean_launch_us"] = res["attn_kernel_mean_us"]
     roof["algorithmic_bytes_per_launch"] = res["attn_kernel_bytes_per_launch"]

@@ -128,6 +128,27 @@ def test_partial_parity(name, use_metadata, split_target):
                                f"{name} shard {r}")
 
 
+@pytest.mark.parametrize("kv_dtype,heads,q_len,out_dtype", [
+    ("bf16", 48, 1, "f32"), ("fp8", 80, 1, "bf16"), ("bf16", 16, 3, "bf16"), ("fp8", 112, 2, "f32")])
+def test_partial_parity_partial_row_blocks(kv_dtype, heads, q_len, out_dtype):
+    """Row counts that leave part of a 64-row block empty (48, 80, 48, 224
+    rows): the empty rows are computed on zero queries and never stored."""
+    wl = make_workload("rows", batch=3, heads=heads, q_len=q_len, shards=3, kv_dtype=kv_dtype,
+                       lens=("uniform", 1, 900), seed=31 + heads, out_dtype=out_dtype)
+    dw = ST.DeviceWorkload.upload(wl)
+    bufs = ST.StepBuffers(dw)
+    bufs.fill_nan()
+    tol = U.TOL[wl.kv_dtype]
+    for r in range(wl.shards):
+        _flush(f"partial rows={heads * q_len} {kv_dtype} shard={r}")
+        ST.run_metadata(dw, bufs, r)
+        ST.run_partial(dw, bufs, r, split_target=7)
+        torch.cuda.synchronize()
+        ref_o, ref_l = O.decode_partial(wl, r, wl.shards, wl.lse_base)
+        U.assert_partial_close(bufs.outs[r], bufs.lses[r], ref_o, ref_l, wl.lse_base, tol,
+                               f"rows {heads * q_len} shard {r}")
+
+
 def test_partial_bf16_output():
     wl = _small("kimi_like")
     dw = ST.DeviceWorkload.upload(wl, out_dtype="bf16")
