@@ -254,28 +254,33 @@ struct Cursor {
 
 // bf16 stage layout (one 32-token tile, 36 KB, token-major, swizzled):
 //   chunk c < 64 (dims 8c .. 8c + 7) of token t at byte 1024 t + 16 (c ^ swz(t)),
-//   chunk c >= 64 (rope) at kRopeBase + 128 t + 16 ((c - 64) ^ swz(t)),
-// with swz the XOR swizzle of the 16-byte chunks inside each 128-byte group,
-// by token: eight consecutive tokens get eight different values, and four
-// consecutive tokens differ in the 32-byte pair they select (the score
-// reads and the transposed V reads are bank-conflict free).
-__host__ __device__ constexpr int chunk_swz(int t) { return 2 * (t & 3) + ((t >> 2) & 1); }
+//   chunk c >= 64 (rope) at kRopeBase + 128 t + 16 ((c - 64) ^ rswz(t)).
+// The LDS serves 64 banks of 4 bytes a cycle: 16 lanes of a 16-byte read,
+// 32 lanes of an 8-byte read. swz permutes the 16 chunks of each 256-byte
+// group so that 16 consecutive tokens put one chunk in 16 different places
+// (the score reads), and the four tokens of a transposed V read land in four
+// different 64-byte quarters; rswz does the same for the rope tails, two
+// tokens to 256 bytes.
+__host__ __device__ constexpr int chunk_swz(int t) { return 4 * (t & 3) + ((t >> 2) & 3); }
+__host__ __device__ constexpr int rope_swz(int t) { return (t >> 1) & 7; }
 
 // QK A operand of this wave's i-th k-step (see the kernel for the layout).
 template <int kG>
 __device__ __forceinline__ bf16x8_t qk_operand(const uint8_t* ks, uint32_t qk0, uint32_t rope0, int i) {
-  return i / kG < 8 ? *(const bf16x8_t*)(ks + (qk0 ^ (32u * (i % kG))) + 128 * (i / kG))
+  return i / kG < 8 ? *(const bf16x8_t*)(ks + (qk0 ^ (32u * (i % kG) + 128u * (i / kG))))
                     : *(const bf16x8_t*)(ks + (rope0 ^ (32u * (i % kG))));
 }
 
 // PV operand of step st = 2 db + m (db local to the wave's slice): dims
 // 32 db .. + 31 of tokens 16 m .. 16 m + 15 in the order of the P values,
-// from two transposing loads of four tokens each (the second 8 tokens on).
+// from two transposing loads of four tokens each (the second 8 tokens on,
+// whose swizzle differs from the first's by 2: swz(t + 8) = swz(t) ^ 2,
+// swz(t + 16) = swz(t)).
 __device__ __forceinline__ bf16x8_t pv_operand(const uint8_t* ks, uint32_t pv0, int st) {
   const int db = st >> 1, m = st & 1;
-  const uint8_t* a = ks + (pv0 ^ (64u * (db & 1))) + 128 * (db >> 1) + 16384 * m;
-  const i16x4_t lo = lds_read_tr16(a);
-  const i16x4_t hi = lds_read_tr16(a + 8192);
+  const uint32_t a = pv0 ^ (64u * db);
+  const i16x4_t lo = lds_read_tr16(ks + a + 16384 * m);
+  const i16x4_t hi = lds_read_tr16(ks + (a ^ 32u) + 8192 + 16384 * m);
   return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -388,7 +393,7 @@ template <int kJ>
 __device__ __forceinline__ void copy_tile_part(const uint8_t* src, uint32_t stage_lds, int wave) {
   const int lane = threadIdx.x & 63;
   if constexpr (kJ == 0) {
-    lds_dma16(src + 16 * (64 + ((lane & 7) ^ chunk_swz(lane >> 3))),
+    lds_dma16(src + 16 * (64 + ((lane & 7) ^ rope_swz(8 * wave + (lane >> 3)))),
               __builtin_amdgcn_readfirstlane(stage_lds + kRopeBase + 1024 * wave));
   } else {
     constexpr int i = kJ - 1;
@@ -396,7 +401,7 @@ __device__ __forceinline__ void copy_tile_part(const uint8_t* src, uint32_t stag
     const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)a, 8 * i);
     const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(a >> 32), 8 * i);
     const uint8_t* base = reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
-    lds_dma16_sbase(base, (uint32_t)(16 * (lane ^ chunk_swz(i))),
+    lds_dma16_sbase(base, (uint32_t)(16 * (lane ^ chunk_swz(8 * wave + i))),
                     __builtin_amdgcn_readfirstlane(stage_lds + 1024 * (8 * wave + i)));
   }
 }
@@ -545,8 +550,8 @@ void attn_ws_kernel(DecodeParams p) {
   if (wave < 4) {
     // ------------------------------------------------------------ scores
     const int rg = wave & 1, ds = wave >> 1;
-    const uint32_t qk0 = (uint32_t)(1024 * tok + 16 * ((2 * kG * ds) ^ hi ^ chunk_swz(tok)));
-    const uint32_t rope0 = (uint32_t)(kRopeBase + 128 * tok + 16 * ((2 * kG * ds) ^ hi ^ chunk_swz(tok)));
+    const uint32_t qk0 = (uint32_t)(1024 * tok + 16 * ((2 * kG * ds + hi) ^ chunk_swz(tok)));
+    const uint32_t rope0 = (uint32_t)(kRopeBase + 128 * tok + 16 * ((2 * kG * ds + hi) ^ rope_swz(tok)));
     // fp8: score step i = 2 j + u uses 16-dim chunk 2 m + hi of the lane's
     // token, m = 2 j + ds (m = 16, 17: rope), its 8-byte half u; the query
     // registers follow the same order of the dims
