@@ -112,9 +112,14 @@ def workload_work(wl):
     return kv_bytes, flops, per_shard
 
 
+# the attention kernel's translation unit and the headers it includes: the
+# committed counter summary applies while these are unchanged
+KERNEL_SOURCES = ("mla_device.h", "mla_internal.h", "mla_stream.hip")
+
+
 def kernel_sha() -> str:
     h = hashlib.sha256()
-    for name in sorted(os.listdir(KERNEL_SRC_DIR)):
+    for name in KERNEL_SOURCES:
         with open(os.path.join(KERNEL_SRC_DIR, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -345,6 +350,54 @@ def bench_merge_sweep(replays: int = 20, warmup: int = 5):
     return out
 
 
+def bench_append(calls: int = 16, replays: int = 10):
+    """KV append of one decode step's newest tokens (one token per request)
+    into the owning shard's pool, at the bf16 default workload's shape (B 64,
+    S 4) and the fp8 one's (B 32, S 8): µs per shard call, from graph replays
+    of `calls` rounds of every shard's call (back-to-back dispatches without
+    host overhead; the median replay / calls). A few hundred bytes per
+    request: the call is latency bound, reported in µs only."""
+    import numpy as np
+    import torch
+
+    from decode_attention_paged_amd import _lib as L
+    from workloads import make_append_inputs
+
+    out = {}
+    for tag, B, S, kv_dtype in (("bf16 B64 S4", 64, 4, "bf16"), ("fp8 B32 S8", 32, 8, "fp8")):
+        inp = make_append_inputs(batch=B, n_new=1, max_pages=64, num_pages=B * 64, kv_dtype=kv_dtype,
+                                 kv_scale=0.05, seed=6000 + B)
+        if kv_dtype == "bf16":
+            pool = torch.from_numpy(inp.kv_pages.view(np.int16)).cuda().view(torch.bfloat16)
+        else:
+            pool = torch.from_numpy(inp.kv_pages).cuda()
+        k_nope = torch.from_numpy(inp.k_nope.view(np.int16)).cuda().view(torch.bfloat16)
+        k_rope = torch.from_numpy(inp.k_rope.view(np.int16)).cuda().view(torch.bfloat16)
+        lens = torch.from_numpy(inp.seq_lens).cuda()
+        bt = torch.from_numpy(inp.block_table).cuda()
+        for r in range(S):
+            L.mla_append_kv(k_nope, k_rope, lens, bt, pool, r, S, kv_scale=inp.kv_scale)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(calls):
+                for r in range(S):
+                    L.mla_append_kv(k_nope, k_rope, lens, bt, pool, r, S, kv_scale=inp.kv_scale)
+        graph.replay()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(replays)]
+        for a, b in evs:
+            a.record()
+            graph.replay()
+            b.record()
+        torch.cuda.synchronize()
+        per = [1e3 * a.elapsed_time(b) / (calls * S) for a, b in evs]
+        out[tag] = round(statistics.median(per), 2)
+        del pool, graph
+    torch.cuda.empty_cache()
+    return out
+
+
 # --------------------------------------------------------------------------
 # CPU oracle baseline
 # --------------------------------------------------------------------------
@@ -385,7 +438,7 @@ def main() -> int:
     ap.add_argument("--all", action="store_true", help="also measure every workload")
     ap.add_argument("--details", default=None, help="write per-workload results (JSON) here")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-merge-sweep", action="store_true")
+    ap.add_argument("--no-merge-sweep", action="store_true", help="skip the merge-only sweep and the append timing")
     ap.add_argument("--no-graph", action="store_true", help="time the step as eager launches")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--split-target", type=int, default=0,
@@ -431,6 +484,9 @@ def main() -> int:
     merge = None if args.no_merge_sweep else bench_merge_sweep()
     if merge:
         details["merge_only"] = merge
+    append = None if args.no_merge_sweep else bench_append()
+    if append:
+        details["append_us_per_shard_call"] = append
     if args.all:
         for idx in (1, 2, 3, 4, 5):
             if idx == args.config:
@@ -484,6 +540,7 @@ def main() -> int:
                                 unit="GB/s", frac=round(merge["128"]["kernel_gbs"] / HBM_PEAK_GBS, 4),
                                 kernel_us=round(merge["128"]["kernel_us_mean"], 2))
                            if merge and "128" in merge else None),
+        "append_us": append,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

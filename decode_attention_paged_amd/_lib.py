@@ -79,9 +79,27 @@ class MergeArgs(ctypes.Structure):
     ]
 
 
+class AppendArgs(ctypes.Structure):
+    _fields_ = [
+        ("k_nope", ctypes.c_void_p),
+        ("k_rope", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("kv_pages", ctypes.c_void_p),
+        ("batch", ctypes.c_int32),
+        ("n_new", ctypes.c_int32),
+        ("max_pages", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("shard_id", ctypes.c_int32),
+        ("num_shards", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int),
+        ("kv_scale", ctypes.c_float),
+    ]
+
+
 EXPORTS = ("mla_build_shard_metadata", "mla_decode_workspace_bytes", "mla_decode_partial", "mla_decode_plan",
-           "mla_merge_partials", "mla_status_string", "mla_last_error", "mla_abi_version",
-           "mla_sizeof_decode_args", "mla_sizeof_merge_args")
+           "mla_merge_partials", "mla_append_kv", "mla_status_string", "mla_last_error", "mla_abi_version",
+           "mla_sizeof_decode_args", "mla_sizeof_merge_args", "mla_sizeof_append_args")
 
 _lib = None
 
@@ -109,6 +127,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_decode_plan.restype = ctypes.c_int
     lib.mla_merge_partials.argtypes = [ctypes.POINTER(MergeArgs), vp]
     lib.mla_merge_partials.restype = ctypes.c_int
+    lib.mla_append_kv.argtypes = [ctypes.POINTER(AppendArgs), vp]
+    lib.mla_append_kv.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_last_error.argtypes = []
@@ -116,10 +136,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_abi_version.restype = i32
     lib.mla_sizeof_decode_args.restype = sz
     lib.mla_sizeof_merge_args.restype = sz
+    lib.mla_sizeof_append_args.restype = sz
     if lib.mla_sizeof_decode_args() != ctypes.sizeof(DecodeArgs):
         raise RuntimeError("mla_decode_args_t layout mismatch between library and binding")
     if lib.mla_sizeof_merge_args() != ctypes.sizeof(MergeArgs):
         raise RuntimeError("mla_merge_args_t layout mismatch between library and binding")
+    if lib.mla_sizeof_append_args() != ctypes.sizeof(AppendArgs):
+        raise RuntimeError("mla_append_args_t layout mismatch between library and binding")
     _lib = lib
     return lib
 
@@ -259,3 +282,31 @@ def mla_merge_partials(outs: Sequence, lses: Sequence, bases: Sequence[int], out
     if events is not None:
         a.event_begin, a.event_end = int(events[0].cuda_event), int(events[1].cuda_event)
     _check(lib.mla_merge_partials(ctypes.byref(a), _stream_ptr(stream)))
+
+
+def mla_append_kv(k_nope, k_rope, seq_lens, block_table, kv_pages, shard_id: int, num_shards: int, *,
+                  kv_scale: float = 1.0, stream=None) -> None:
+    """Write the newest n_new tokens of each request into the pool, on the
+    shard that owns each token (token L - n_new + i belongs to shard
+    (L - n_new + i) mod S); fp8 pools get the row quantised with kv_scale.
+
+    k_nope [B, n_new, 512] bf16; k_rope [B, n_new, 64] bf16; seq_lens [B] i32
+    (new global lengths); block_table [B, max_pages] i32; kv_pages
+    [P, 64, 576] bf16 or uint8 (e4m3), written in place.
+    """
+    lib = load()
+    if k_nope.dim() != 3 or k_nope.shape[2] != 512 or k_rope.dim() != 3 or k_rope.shape[2] != 64:
+        raise ValueError("k_nope must be [B, n_new, 512] and k_rope [B, n_new, 64]")
+    if tuple(k_nope.shape[:2]) != tuple(k_rope.shape[:2]):
+        raise ValueError("k_nope and k_rope must agree in [B, n_new]")
+    if not (k_nope.is_contiguous() and k_rope.is_contiguous()):
+        raise ValueError("k_nope and k_rope must be contiguous")
+    a = AppendArgs()
+    a.k_nope, a.k_rope = _ptr(k_nope), _ptr(k_rope)
+    a.seq_lens, a.block_table, a.kv_pages = _ptr(seq_lens), _ptr(block_table), _ptr(kv_pages)
+    a.batch, a.n_new = int(k_nope.shape[0]), int(k_nope.shape[1])
+    a.max_pages, a.num_pages = int(block_table.shape[1]), int(kv_pages.shape[0])
+    a.shard_id, a.num_shards = int(shard_id), int(num_shards)
+    a.kv_dtype = _dtype_code(kv_pages)
+    a.kv_scale = float(kv_scale)
+    _check(lib.mla_append_kv(ctypes.byref(a), _stream_ptr(stream)))

@@ -101,6 +101,7 @@ const char* mla_last_error(void) { return g_last_error.c_str(); }
 int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
 size_t mla_sizeof_decode_args(void) { return sizeof(mla_decode_args_t); }
 size_t mla_sizeof_merge_args(void) { return sizeof(mla_merge_args_t); }
+size_t mla_sizeof_append_args(void) { return sizeof(mla_append_args_t); }
 
 mla_status_t mla_build_shard_metadata(const int32_t* seq_lens, const int32_t* block_table,
                                       int32_t batch, int32_t max_pages, int32_t page_size,
@@ -132,6 +133,43 @@ mla_status_t mla_build_shard_metadata(const int32_t* seq_lens, const int32_t* bl
                                         local_seq_lens, local_kv_indices, local_kv_stride,
                                         (hipStream_t)stream);
   if (err != hipSuccess) return device_fail(err, "metadata launch");
+  return ok();
+}
+
+mla_status_t mla_append_kv(const mla_append_args_t* a, void* stream) {
+  if (a == nullptr) return fail(MLA_STATUS_INVALID_ARGUMENT, "args is NULL");
+  if (a->batch < 0) return fail(MLA_STATUS_INVALID_ARGUMENT, "batch must be >= 0 (got %d)", a->batch);
+  if (a->n_new < 1 || a->n_new > MLA_MAX_Q_LEN)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "n_new must be in [1, %d] (got %d)", MLA_MAX_Q_LEN, a->n_new);
+  if (a->num_shards < 1 || a->num_shards > MLA_MAX_SHARDS)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "num_shards must be in [1, %d] (got %d)", MLA_MAX_SHARDS, a->num_shards);
+  if (a->shard_id < 0 || a->shard_id >= a->num_shards)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "shard_id %d outside [0, %d)", a->shard_id, a->num_shards);
+  if (a->max_pages < 1) return fail(MLA_STATUS_INVALID_ARGUMENT, "max_pages must be >= 1 (got %d)", a->max_pages);
+  if (a->num_pages < 1) return fail(MLA_STATUS_INVALID_ARGUMENT, "num_pages must be >= 1 (got %d)", a->num_pages);
+  if (a->kv_dtype != MLA_DTYPE_BF16 && a->kv_dtype != MLA_DTYPE_FP8_E4M3)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "kv_dtype must be BF16 or FP8_E4M3");
+  if (a->kv_dtype == MLA_DTYPE_FP8_E4M3 && !(a->kv_scale > 0.f && a->kv_scale <= 3.4028235e38f))
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "kv_scale must be finite and > 0 for an fp8 pool");
+  if (a->batch > 0 && (a->k_nope == nullptr || a->k_rope == nullptr || a->seq_lens == nullptr ||
+                       a->block_table == nullptr || a->kv_pages == nullptr))
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "k_nope, k_rope, seq_lens, block_table and kv_pages are required");
+  mla::AppendParams p;
+  p.k_nope = a->k_nope;
+  p.k_rope = a->k_rope;
+  p.seq_lens = a->seq_lens;
+  p.block_table = a->block_table;
+  p.kv = a->kv_pages;
+  p.batch = a->batch;
+  p.n_new = a->n_new;
+  p.max_pages = a->max_pages;
+  p.num_pages = a->num_pages;
+  p.shard = a->shard_id;
+  p.num_shards = a->num_shards;
+  p.fp8 = a->kv_dtype == MLA_DTYPE_FP8_E4M3;
+  p.kv_scale = a->kv_scale;
+  hipError_t err = mla::launch_append(p, (hipStream_t)stream);
+  if (err != hipSuccess) return device_fail(err, "append launch");
   return ok();
 }
 

@@ -83,6 +83,17 @@ struct MergeParams {
   float lse_out_from_log2;        // multiplier from base 2 to the output base
 };
 
+struct AppendParams {
+  const uint16_t* k_nope;         // [batch * n_new][512] bf16
+  const uint16_t* k_rope;         // [batch * n_new][64] bf16
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  void* kv;                       // [num_pages][64][576] bf16 | e4m3
+  int32_t batch, n_new, max_pages, num_pages, shard, num_shards;
+  int32_t fp8;
+  float kv_scale;
+};
+
 hipError_t launch_metadata(const int32_t* seq_lens, const int32_t* block_table, int32_t batch,
                            int32_t max_pages, int32_t shard, int32_t num_shards,
                            int32_t* local_seq_lens, int32_t* local_kv_indices,
@@ -91,5 +102,6 @@ hipError_t launch_decode_plan(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_stream(const DecodeParams& p, bool run_plan, hipEvent_t ev_begin, hipEvent_t ev_end,
                                 hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream);
+hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 
 }  // namespace mla

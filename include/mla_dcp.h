@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 3
+#define MLA_ABI_VERSION 4
 #define MLA_PAGE_SIZE 64
 #define MLA_D_QK 576
 #define MLA_D_V 512
@@ -228,6 +228,54 @@ typedef struct mla_merge_args {
 mla_status_t mla_merge_partials(const mla_merge_args_t* args, void* stream);
 
 /* ------------------------------------------------------------------------
+ * KV append into the owning shard.
+ *
+ * Follows [DCP decode] key code (the layout test: a decode step appends one
+ * token per request, and exactly one rank's local length grows, the rank
+ * (L - 1) mod S) and implementation steps 3-4 (under DCP the KV row is
+ * written through the pool's plain row write, not the fused bf16 write; fp8
+ * pools store the row quantised). For request b with new global length
+ * L = seq_lens[b] and i in [0, n_new), token t = L - n_new + i is written
+ * by shard t mod S only, into pool row
+ *   block_table[b][t / 64] * 64 + t % 64
+ * as the 576 values [k_nope[b][i][0:512] | k_rope[b][i][0:64]]:
+ *   - kv_dtype BF16: the bf16 values as given;
+ *   - kv_dtype FP8_E4M3: code = e4m3(x / kv_scale), the division in IEEE
+ *     fp32 (x is the bf16 value widened exactly), then rounded to the
+ *     nearest e4m3 value, ties to even; magnitudes above 448 (and
+ *     infinities) saturate to +-448; NaN gives 0x7F with the input's sign.
+ * Tokens with t < 0, t / 64 >= max_pages, or a page id outside
+ * [0, num_pages) are skipped (nothing is written for them). Rows of other
+ * shards' tokens are never written.
+ * Layout: k_nope [batch][n_new][512] bf16, k_rope [batch][n_new][64] bf16
+ * (device, contiguous); seq_lens [batch] i32 and block_table
+ * [batch][max_pages] i32 (device); kv_pages [num_pages][64][576] of
+ * kv_dtype (device, written in place).
+ * Errors: INVALID_ARGUMENT for null pointers (batch > 0), batch < 0,
+ * n_new outside [1, MLA_MAX_Q_LEN], num_shards outside [1, MLA_MAX_SHARDS],
+ * shard_id outside [0, num_shards), max_pages < 1, num_pages < 1, a kv_dtype
+ * other than BF16 / FP8_E4M3, kv_scale not finite and > 0 (fp8);
+ * DEVICE_ERROR if the launch fails.
+ * ---------------------------------------------------------------------- */
+typedef struct mla_append_args {
+  const uint16_t* k_nope;        /* [batch][n_new][512] bf16 bits */
+  const uint16_t* k_rope;        /* [batch][n_new][64]  bf16 bits */
+  const int32_t* seq_lens;       /* [batch] new global lengths    */
+  const int32_t* block_table;    /* [batch][max_pages]            */
+  void* kv_pages;                /* [num_pages][64][576]          */
+  int32_t batch;
+  int32_t n_new;
+  int32_t max_pages;
+  int32_t num_pages;
+  int32_t shard_id;
+  int32_t num_shards;
+  mla_dtype_t kv_dtype;
+  float kv_scale;
+} mla_append_args_t;
+
+mla_status_t mla_append_kv(const mla_append_args_t* args, void* stream);
+
+/* ------------------------------------------------------------------------
  * Introspection.
  * ---------------------------------------------------------------------- */
 const char* mla_status_string(mla_status_t status);
@@ -236,6 +284,7 @@ int32_t mla_abi_version(void);
 /* sizeof the argument structs as compiled, for binding layout checks */
 size_t mla_sizeof_decode_args(void);
 size_t mla_sizeof_merge_args(void);
+size_t mla_sizeof_append_args(void);
 
 #ifdef __cplusplus
 }

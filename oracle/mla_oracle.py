@@ -37,6 +37,14 @@ What it computes, and the passage each step follows:
 * ``merge`` -- [symm_a2a] Modifications, the fourth kernel (and the ag_rs /
   a2a combines under Motivation): the LSE-weighted softmax reduction of all
   ranks' partial outputs into the full-context result.
+* ``append_kv`` / ``encode_e4m3`` -- [DCP decode] key code (the layout test:
+  each appended token grows exactly one rank's local length, rank
+  (L - 1) mod S) and implementation steps 3-4 (the KV row is written with
+  the pool's plain row write; fp8 pools hold it quantised): the owner of each
+  new token writes its [k_nope | k_rope] row into its page slot. fp8 codes
+  are the nearest e4m3 value to the fp32 quotient x / kv_scale, ties to the
+  even code, saturating at 448; the oracle finds that value by searching the
+  table of all codes it decodes itself.
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes): owner indexing is 0-based; for q_len > 1 the sequence length
@@ -264,3 +272,65 @@ def decode_step(wl, requests: Optional[Sequence[int]] = None, out_base: str = "e
     parts = [decode_partial(wl, r, wl.shards, wl.lse_base, requests) for r in range(wl.shards)]
     out, lse = merge([p[0] for p in parts], [p[1] for p in parts], [wl.lse_base] * wl.shards)
     return out, to_base(lse, out_base), parts
+
+
+# --------------------------------------------------------------------------
+# KV append into the owning shard ([DCP decode] key code: the layout test;
+# implementation steps 3-4: the plain row write, fp8 pools quantised)
+# --------------------------------------------------------------------------
+def _e4m3_table() -> np.ndarray:
+    """Values of the non-negative finite codes 0x00 .. 0x7E, increasing."""
+    return decode_e4m3(np.arange(0x7F, dtype=np.uint8))
+
+
+def encode_e4m3(x) -> np.ndarray:
+    """float32 values -> OCP e4m3 ("fn") codes by the definition: the nearest
+    representable value, ties to the code with an even mantissa; magnitudes
+    above 448 (and infinities) give +-448; NaN gives 0x7F with x's sign."""
+    x = np.asarray(x, dtype=np.float32)
+    table = _e4m3_table()
+    a = np.abs(x.astype(np.float64))
+    sign = np.signbit(x).astype(np.uint8) << np.uint8(7)
+    finite = np.isfinite(a)
+    a_c = np.where(finite, np.minimum(a, table[-1]), table[-1])
+    hi = np.searchsorted(table, a_c, side="left")          # first value >= a
+    hi = np.minimum(hi, len(table) - 1)
+    lo = np.where(table[hi] == a_c, hi, hi - 1)
+    lo = np.maximum(lo, 0)
+    d_lo = a_c - table[lo]
+    d_hi = table[hi] - a_c
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0) & (hi != lo))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(np.isnan(x), np.uint8(0x7F), code)
+    return code | sign
+
+
+def append_kv(kv_pages: np.ndarray, k_nope: np.ndarray, k_rope: np.ndarray, seq_lens: Sequence[int],
+              block_table: np.ndarray, shard_id: int, num_shards: int, kv_dtype: str,
+              kv_scale: float = 1.0, page_size: int = 64) -> np.ndarray:
+    """The pool after shard ``shard_id`` appends the newest n_new tokens of
+    every request: token t = L - n_new + i (i < n_new) is written only if
+    t >= 0 and t mod S == shard_id, into row block_table[b][t // 64] * 64 +
+    t % 64, and only when that page id lies in the pool. ``k_nope`` [B, n, 512]
+    and ``k_rope`` [B, n, 64] are bf16 bit patterns (uint16)."""
+    out = np.array(kv_pages, copy=True)
+    B, n = k_nope.shape[0], k_nope.shape[1]
+    max_pages = block_table.shape[1]
+    for b in range(B):
+        L = int(seq_lens[b])
+        for i in range(n):
+            t = L - n + i
+            if t < 0 or t % num_shards != shard_id or t // page_size >= max_pages:
+                continue
+            page = int(block_table[b][t // page_size])
+            if page < 0 or page >= out.shape[0]:
+                continue
+            row_bits = np.concatenate([k_nope[b, i], k_rope[b, i]]).astype(np.uint16)
+            if kv_dtype == "bf16":
+                out[page, t % page_size, :] = row_bits
+            elif kv_dtype == "fp8":
+                x = decode_bf16(row_bits).astype(np.float32)      # exact
+                out[page, t % page_size, :] = encode_e4m3(x / np.float32(kv_scale))
+            else:
+                raise ValueError(kv_dtype)
+    return out

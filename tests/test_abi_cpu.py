@@ -29,7 +29,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert "mla_decode_partial" in names and "mla_merge_partials" in names
-    assert "mla_build_shard_metadata" in names
+    assert "mla_build_shard_metadata" in names and "mla_append_kv" in names
     for n in names:
         assert hasattr(lib, n), n
     assert set(L.EXPORTS) <= set(names)
@@ -38,7 +38,8 @@ def test_exports_every_declared_symbol(lib):
 def test_struct_layouts_and_version(lib):
     assert lib.mla_sizeof_decode_args() == ctypes.sizeof(L.DecodeArgs)
     assert lib.mla_sizeof_merge_args() == ctypes.sizeof(L.MergeArgs)
-    assert lib.mla_abi_version() == 3
+    assert lib.mla_sizeof_append_args() == ctypes.sizeof(L.AppendArgs)
+    assert lib.mla_abi_version() == 4
     assert lib.mla_status_string(L.STATUS_INVALID_ARGUMENT) == b"invalid argument"
 
 
@@ -129,3 +130,33 @@ def test_merge_argument_errors(lib):
     assert lib.mla_merge_partials(ctypes.byref(a), None) == L.STATUS_INVALID_ARGUMENT   # null shard out
     a.dv = 500
     assert lib.mla_merge_partials(ctypes.byref(a), None) == L.STATUS_INVALID_ARGUMENT
+
+
+def _valid_append():
+    a = L.AppendArgs()
+    a.k_nope = a.k_rope = a.seq_lens = a.block_table = a.kv_pages = 0x1000
+    a.batch, a.n_new, a.max_pages, a.num_pages = 2, 1, 4, 8
+    a.shard_id, a.num_shards = 1, 4
+    a.kv_dtype, a.kv_scale = L.DTYPE_FP8_E4M3, 0.5
+    return a
+
+
+@pytest.mark.parametrize("field,value", [
+    ("batch", -1), ("n_new", 0), ("n_new", 5), ("num_shards", 0), ("num_shards", 17),
+    ("shard_id", 4), ("shard_id", -1), ("max_pages", 0), ("num_pages", 0),
+    ("kv_dtype", L.DTYPE_F32), ("kv_scale", 0.0), ("kv_scale", -1.0), ("kv_scale", float("inf")),
+    ("kv_scale", float("nan")), ("k_rope", None), ("kv_pages", None),
+])
+def test_append_argument_errors(lib, field, value):
+    a = _valid_append()
+    setattr(a, field, value)
+    assert lib.mla_append_kv(ctypes.byref(a), None) == L.STATUS_INVALID_ARGUMENT
+    assert lib.mla_last_error()
+
+
+def test_append_empty_batch_and_bf16_scale_are_ok_without_device(lib):
+    a = _valid_append()
+    a.batch = 0
+    assert lib.mla_append_kv(ctypes.byref(a), None) == L.STATUS_OK
+    a.kv_dtype, a.kv_scale = L.DTYPE_BF16, 0.0          # the scale is not used for a bf16 pool
+    assert lib.mla_append_kv(ctypes.byref(a), None) == L.STATUS_OK

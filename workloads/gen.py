@@ -303,3 +303,55 @@ def make_merge_inputs(tokens: int, *, shards: int = 4, heads: int = 64, dv: int 
     bases = list(bases) if bases is not None else ["e"] * shards
     outs = f32_to_bf16_bits(o) if dtype == "bf16" else o
     return MergeInputs(outs=outs, lses=lse, bases=bases)
+
+
+@dataclasses.dataclass
+class AppendInputs:
+    k_nope: np.ndarray        # [B, n_new, 512] uint16 (bf16 bits)
+    k_rope: np.ndarray        # [B, n_new, 64] uint16 (bf16 bits)
+    seq_lens: np.ndarray      # [B] int32, new global lengths
+    block_table: np.ndarray   # [B, max_pages] int32 (some entries -1 or past the pool)
+    kv_pages: np.ndarray      # [num_pages, 64, 576] uint16 (bf16) | uint8 (e4m3), the pool before
+    kv_dtype: str
+    kv_scale: float
+
+
+def make_append_inputs(*, batch: int = 40, n_new: int = 1, max_pages: int = 6, num_pages: int = 256,
+                       kv_dtype: str = "bf16", kv_scale: float = 0.75, seed: int = 3003,
+                       special: Sequence[float] = ()) -> AppendInputs:
+    """New-token KV rows and a paged pool for the append step.
+
+    Lengths cover the edge cases of the owner and page arithmetic: 1 .. n_new
+    (tokens before the request start), page boundaries (63, 64, 65, 128),
+    the last slot of the table (max_pages * 64) and one past it, then uniform
+    draws. Block tables hold distinct pages of the pool (no two requests
+    share one), with a few entries
+    set to -1 and to num_pages (outside the pool). Row values are N(0, 4)
+    bf16; ``special`` values (bf16-representable, e.g. NaN, +-inf, format
+    midpoints) are planted at seeded positions. The pool starts as random
+    bytes so that every write and every untouched row is visible.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    fixed = [1, 2, 3, n_new, 63, 64, 65, 128, max_pages * 64, max_pages * 64 + 1]
+    lens = list(fixed) + list(rng.integers(1, max_pages * 64 + 1, size=max(batch - len(fixed), 0)))
+    lens = np.asarray(lens[:batch], dtype=np.int32)
+    if num_pages < batch * max_pages:
+        raise ValueError("the pool must hold batch * max_pages distinct pages")
+    bt = rng.permutation(num_pages)[:batch * max_pages].reshape(batch, max_pages).astype(np.int32)
+    holes = rng.uniform(size=bt.shape)
+    bt[holes < 0.04] = -1
+    bt[(holes >= 0.04) & (holes < 0.08)] = num_pages
+    x = (2.0 * rng.standard_normal((batch, n_new, D_QK))).astype(np.float32)
+    if len(special):
+        flat = x.reshape(-1)
+        pos = rng.choice(flat.size, size=min(len(special) * 8, flat.size), replace=False)
+        flat[pos] = np.resize(np.asarray(special, dtype=np.float32), pos.size)
+    bits = f32_to_bf16_bits(x)
+    if kv_dtype == "bf16":
+        pool = rng.integers(0, 1 << 16, size=(num_pages, PAGE_SIZE, D_QK), dtype=np.uint16)
+    elif kv_dtype == "fp8":
+        pool = rng.integers(0, 1 << 8, size=(num_pages, PAGE_SIZE, D_QK), dtype=np.uint8)
+    else:
+        raise ValueError(kv_dtype)
+    return AppendInputs(k_nope=np.ascontiguousarray(bits[..., :512]), k_rope=np.ascontiguousarray(bits[..., 512:]),
+                        seq_lens=lens, block_table=bt, kv_pages=pool, kv_dtype=kv_dtype, kv_scale=float(kv_scale))
