@@ -958,7 +958,23 @@ void attn_ws_kernel(DecodeParams p) {
 // combine the pieces of segments cut at workgroup boundaries; neutral rows
 // for requests with no owned token
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// One wave per query row of a segment cut into np pieces: the LSE of piece c
+// sits in lane c (64 pieces at a time), and the bf16 partials of kPieces
+// pieces (8 dims per lane) are loaded together, the first group in the same
+// round trip as the LSEs; pieces are then accumulated in order.
 __global__ __launch_bounds__(256) void stream_combine_kernel(DecodeParams p) {
+  constexpr int kPieces = 8;
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.y * 4 + (threadIdx.x >> 6);
@@ -972,18 +988,41 @@ __global__ __launch_bounds__(256) void stream_combine_kernel(DecodeParams p) {
   float mx = kNegInf, wsum = 0.f;
   if (np > 1) {
     const long long prow0 = (long long)si.x * p.rows_blk + (row - rb * p.rows_blk);
-    for (int c = 0; c < np; ++c) mx = fmaxf(mx, p.spart_lse[prow0 + (long long)c * p.rows_blk]);
-    if (mx != kNegInf) {
-      for (int c = 0; c < np; ++c) {
-        const long long prow = prow0 + (long long)c * p.rows_blk;
-        const float w = exp2_fast(p.spart_lse[prow] - mx);
-        const u32x4_t x = *(const u32x4_t*)(p.spart_o + prow * kDv + 8 * lane);
+    auto piece_lse = [&](int c) { return c < np ? p.spart_lse[prow0 + (long long)c * p.rows_blk] : kNegInf; };
+    auto piece_o = [&](int c) {
+      return *(const u32x4_t*)(p.spart_o + (prow0 + (long long)c * p.rows_blk) * kDv + 8 * lane);
+    };
+    const float lse_lo = piece_lse(lane);
+    u32x4_t xs[kPieces];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc0[e] += w * __uint_as_float(x[e >> 1] << (16 * ((e & 1) ^ 1)) & 0xFFFF0000u);
-          acc1[e] += w * __uint_as_float(x[2 + (e >> 1)] << (16 * ((e & 1) ^ 1)) & 0xFFFF0000u);
+    for (int u = 0; u < kPieces; ++u)
+      if (u < np) xs[u] = piece_o(u);
+    mx = wave_max(lse_lo);
+    for (int c0 = 64; c0 < np; c0 += 64) mx = fmaxf(mx, wave_max(piece_lse(c0 + lane)));
+    if (mx != kNegInf) {
+      for (int c0 = 0; c0 < np; c0 += 64) {
+        const float l = c0 == 0 ? lse_lo : piece_lse(c0 + lane);
+        const float w = exp2_fast(l - mx);            // 0 for pieces past np (lse -inf)
+        wsum += wave_sum(w);
+        const int n = min(64, np - c0);
+        for (int u0 = 0; u0 < n; u0 += kPieces) {
+          if (c0 + u0 > 0) {
+#pragma unroll
+            for (int u = 0; u < kPieces; ++u)
+              if (u0 + u < n) xs[u] = piece_o(c0 + u0 + u);
+          }
+#pragma unroll
+          for (int u = 0; u < kPieces; ++u) {
+            if (u0 + u < n) {
+              const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u0 + u));
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                acc0[e] += wu * __uint_as_float(xs[u][e >> 1] << (16 * ((e & 1) ^ 1)) & 0xFFFF0000u);
+                acc1[e] += wu * __uint_as_float(xs[u][2 + (e >> 1)] << (16 * ((e & 1) ^ 1)) & 0xFFFF0000u);
+              }
+            }
+          }
         }
-        wsum += w;
       }
     }
   }
