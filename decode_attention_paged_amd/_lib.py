@@ -57,6 +57,7 @@ class DecodeArgs(ctypes.Structure):
         ("event_begin", ctypes.c_void_p),
         ("event_end", ctypes.c_void_p),
         ("reuse_plan", ctypes.c_int32),
+        ("q_lens", ctypes.c_void_p),
     ]
 
 
@@ -203,7 +204,7 @@ def mla_decode_workspace_bytes(batch: int, num_heads: int, q_len: int) -> int:
 
 def _decode_args(q, kv_pages, block_table, seq_lens, shard_id, num_shards, q_len, out, lse, workspace,
                  kv_scale, softmax_scale, lse_base, local_seq_lens, local_kv_indices, split_target, events,
-                 reuse_plan):
+                 reuse_plan, q_lens=None):
     a = DecodeArgs()
     B, ql, H = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
     if ql != q_len:
@@ -223,13 +224,15 @@ def _decode_args(q, kv_pages, block_table, seq_lens, shard_id, num_shards, q_len
     if events is not None:
         a.event_begin, a.event_end = int(events[0].cuda_event), int(events[1].cuda_event)
     a.reuse_plan = 1 if reuse_plan else 0
+    a.q_lens = _ptr(q_lens)
     return a
 
 
 def mla_decode_partial(q, kv_pages, block_table, seq_lens, shard_id: int, num_shards: int, q_len: int,
                        out, lse, workspace, *, kv_scale: float = 1.0, softmax_scale: float,
                        lse_base: int = LSE_BASE_E, local_seq_lens=None, local_kv_indices=None,
-                       split_target: int = 0, events=None, reuse_plan: bool = False, stream=None) -> int:
+                       split_target: int = 0, events=None, reuse_plan: bool = False, q_lens=None,
+                       stream=None) -> int:
     """Rank-local (out, lse) of one shard; returns the LSE base written.
 
     q [B, q_len, H, 576] bf16; kv_pages [P, 64, 576] bf16 or uint8 (e4m3);
@@ -238,11 +241,13 @@ def mla_decode_partial(q, kv_pages, block_table, seq_lens, shard_id: int, num_sh
     mla_decode_workspace_bytes(B, H, q_len). ``events`` = optional pair of
     timing events recorded around the attention kernel. ``reuse_plan``: the
     workspace holds the schedule mla_decode_plan built for the same inputs.
+    ``q_lens``: optional [B] i32 decode depth per request (rows past it are
+    padding, written (0, -inf)).
     """
     lib = load()
     a = _decode_args(q, kv_pages, block_table, seq_lens, shard_id, num_shards, q_len, out, lse, workspace,
                      kv_scale, softmax_scale, lse_base, local_seq_lens, local_kv_indices, split_target, events,
-                     reuse_plan)
+                     reuse_plan, q_lens)
     written = ctypes.c_int(-1)
     _check(lib.mla_decode_partial(ctypes.byref(a), ctypes.byref(written), _stream_ptr(stream)))
     return int(written.value)

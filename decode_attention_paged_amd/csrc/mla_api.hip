@@ -238,6 +238,7 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
   p.local_seq_lens = a->local_seq_lens;
   p.local_kv_indices = a->local_kv_indices;
   p.local_kv_stride = a->local_kv_stride;
+  p.q_lens = a->q_lens;
   p.batch = a->batch;
   p.heads = a->num_heads;
   p.q_len = a->q_len;

@@ -22,6 +22,7 @@ struct DecodeParams {
   const int32_t* seq_lens;        // [B] global lengths
   const int32_t* local_seq_lens;  // optional [B]
   const int32_t* local_kv_indices;// optional [B][stride]
+  const int32_t* q_lens;          // optional [B] decode depth per request (<= q_len)
   int32_t local_kv_stride;
   int32_t batch, heads, q_len, rows, row_blocks;
   int32_t max_pages, num_pages, shard, num_shards;

@@ -609,16 +609,22 @@ void attn_ws_kernel(DecodeParams p) {
         }
       }
       wait_vmcnt<0>();
-      // owned tokens row (draft i) may see: t = j S + r <= L - q_len + i
+      // owned tokens row (draft i) may see: t = j S + r <= L - q_b + i, with
+      // q_b the request's decode depth (rows i >= q_b are padding: none)
       int jvis = 0;
       {
         int L = ld_const(p.seq_lens + b);
         L = L < 0 ? 0 : min(L, p.max_pages * kPage);
+        int qb = p.q_len;
+        if (p.q_lens != nullptr) {
+          qb = ld_const(p.q_lens + b);
+          qb = qb < 0 ? 0 : (qb > p.q_len ? p.q_len : qb);
+        }
         const int i = (row >= p.heads) + (row >= 2 * p.heads) + (row >= 3 * p.heads);
         for (int k = 0; k < p.q_len; ++k) {
-          const int lim = L - p.q_len + k - p.shard;
+          const int lim = L - qb + k - p.shard;
           const int jl = lim >= 0 ? min(cnt, lim / p.num_shards + 1) : 0;
-          jvis = i == k ? jl : jvis;
+          jvis = i == k && k < qb ? jl : jvis;
         }
       }
       float m_ref = kNegInf, l_sum = 0.f;

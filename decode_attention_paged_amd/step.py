@@ -34,6 +34,7 @@ class DeviceWorkload:
     kv_pages: torch.Tensor     # [P, 64, 576] bf16 | uint8
     block_table: torch.Tensor  # [B, max_pages] i32
     seq_lens: torch.Tensor     # [B] i32
+    q_lens: Optional[torch.Tensor] = None   # [B] i32 decode depth per request, or None
 
     @staticmethod
     def upload(wl, device="cuda", out_dtype: Optional[str] = None) -> "DeviceWorkload":
@@ -49,7 +50,9 @@ class DeviceWorkload:
             out_bf16=(out_dtype or wl.out_dtype) == "bf16", max_seq_len=wl.max_seq_len,
             q=q, kv_pages=kv,
             block_table=torch.from_numpy(np.ascontiguousarray(wl.block_table)).to(device),
-            seq_lens=torch.from_numpy(np.ascontiguousarray(wl.seq_lens)).to(device))
+            seq_lens=torch.from_numpy(np.ascontiguousarray(wl.seq_lens)).to(device),
+            q_lens=(torch.from_numpy(np.ascontiguousarray(wl.q_lens)).to(device)
+                    if getattr(wl, "q_lens", None) is not None else None))
 
     def local_max(self, shard: int) -> int:
         M, S = self.max_seq_len, self.shards
@@ -117,7 +120,7 @@ def run_partial(dw: DeviceWorkload, bufs: StepBuffers, shard: int, use_metadata:
         softmax_scale=dw.softmax_scale, lse_base=dw.lse_base,
         local_seq_lens=bufs.local_seq_lens[shard] if use_metadata else None,
         local_kv_indices=bufs.local_kv_indices[shard] if use_metadata else None,
-        split_target=split_target, events=events, reuse_plan=reuse_plan, stream=stream)
+        split_target=split_target, events=events, reuse_plan=reuse_plan, q_lens=dw.q_lens, stream=stream)
 
 
 def run_merge(dw: DeviceWorkload, bufs: StepBuffers, out_base: int = L.LSE_BASE_E, stream=None) -> None:

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 4
+#define MLA_ABI_VERSION 5
 #define MLA_PAGE_SIZE 64
 #define MLA_D_QK 576
 #define MLA_D_V 512
@@ -161,6 +161,14 @@ typedef struct mla_decode_args {
    * contents of seq_lens / local_seq_lens (the schedule depends on nothing
    * else), so one schedule serves every layer of a decode step. */
   int32_t reuse_plan;
+  /* optional [batch] i32 (device) or NULL: the decode depth q_b of each
+   * request when requests of one step differ ([next_n] implementation
+   * step 3: the kernel receives the step's largest depth of query rows).
+   * Rows i < q_b are real and see owned tokens t <= L - q_b + i; rows
+   * q_b <= i < q_len are padding and are written as (0, -inf). Values are
+   * clamped to [0, q_len]. NULL: every request is q_len deep. The work
+   * schedule does not depend on it. */
+  const int32_t* q_lens;
 } mla_decode_args_t;
 
 /* Bytes of workspace mla_decode_partial needs for these sizes (host only,

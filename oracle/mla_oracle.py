@@ -185,21 +185,25 @@ def decode_partial(wl, shard_id: int, num_shards: int, base: str = "e",
     """Rank-local (out, lse) of one shard for a decode step.
 
     ``wl`` is a ``workloads.gen.Workload`` (bytes). For request b with
-    global length L and query row (i, h), the shard attends over
-    {t < L : t mod S == r and t <= L - q_len + i}. Returns out
-    [B', q_len, H, 512] and lse [B', q_len, H] (in ``base``) for the chosen
-    requests (all by default).
+    global length L, decode depth q_b (``wl.q_lens[b]``, else q_len) and
+    query row (i, h), the shard attends over
+    {t < L : t mod S == r and t <= L - q_b + i} for i < q_b; rows i >= q_b
+    are padding and see nothing. Returns out [B', q_len, H, 512] and lse
+    [B', q_len, H] (in ``base``) for the chosen requests (all by default).
     """
     reqs = list(range(wl.batch)) if requests is None else list(requests)
     q, H = wl.q_len, wl.heads
+    q_lens = getattr(wl, "q_lens", None)
     out = np.zeros((len(reqs), q, H, D_V), dtype=np.float64)
     lse = np.full((len(reqs), q, H), -np.inf, dtype=np.float64)
     for n, b in enumerate(reqs):
         L = int(wl.seq_lens[b])
+        qb = q if q_lens is None else int(q_lens[b])
         toks = owned_tokens(L, shard_id, num_shards)
         K = gather_kv_rows(wl.kv_pages, wl.block_table[b], toks, wl.kv_dtype, wl.kv_scale)
         t = np.asarray(toks, dtype=np.int64)
-        rows_vis = np.stack([t <= L - q + i for i in range(q)]) if t.size else np.zeros((q, 0), bool)
+        rows_vis = (np.stack([(t <= L - qb + i) & (i < qb) for i in range(q)]) if t.size
+                    else np.zeros((q, 0), bool))
         visible = np.repeat(rows_vis, H, axis=0)     # row index = i * H + h
         o, l = attend(_q_rows(wl, b), K, wl.softmax_scale, visible)
         out[n] = o.reshape(q, H, D_V)

@@ -39,7 +39,7 @@ def test_struct_layouts_and_version(lib):
     assert lib.mla_sizeof_decode_args() == ctypes.sizeof(L.DecodeArgs)
     assert lib.mla_sizeof_merge_args() == ctypes.sizeof(L.MergeArgs)
     assert lib.mla_sizeof_append_args() == ctypes.sizeof(L.AppendArgs)
-    assert lib.mla_abi_version() == 4
+    assert lib.mla_abi_version() == 5
     assert lib.mla_status_string(L.STATUS_INVALID_ARGUMENT) == b"invalid argument"
 
 

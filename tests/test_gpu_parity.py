@@ -128,6 +128,33 @@ def test_partial_parity(name, use_metadata, split_target):
                                f"{name} shard {r}")
 
 
+@pytest.mark.parametrize("kv_dtype,heads,q_len,shards,out_dtype", [
+    ("bf16", 16, 4, 1, "f32"), ("bf16", 64, 4, 4, "bf16"), ("fp8", 128, 3, 2, "bf16"), ("bf16", 32, 2, 3, "f32")])
+def test_partial_parity_per_request_depth(kv_dtype, heads, q_len, shards, out_dtype):
+    """A decode depth per request (0 .. q_len, drawn): real rows against the
+    oracle, padding rows exactly (+0, -inf); then the merged step."""
+    wl = make_workload("var_q", batch=6, heads=heads, q_len=q_len, shards=shards, kv_dtype=kv_dtype,
+                       lens=("uniform", 1, 700), seed=61 + heads + q_len, out_dtype=out_dtype, var_q=True)
+    assert wl.q_lens is not None and (wl.q_lens < q_len).any()
+    dw = ST.DeviceWorkload.upload(wl)
+    bufs = ST.StepBuffers(dw)
+    bufs.fill_nan()
+    tol = U.TOL[kv_dtype]
+    parts = []
+    for r in range(wl.shards):
+        _flush(f"per-request depth {kv_dtype} H={heads} q={q_len} q_lens={wl.q_lens.tolist()} shard={r}/{shards}")
+        ST.run_metadata(dw, bufs, r)
+        ST.run_partial(dw, bufs, r)
+        torch.cuda.synchronize()
+        ref_o, ref_l = O.decode_partial(wl, r, wl.shards, wl.lse_base)
+        parts.append((ref_o, ref_l))
+        U.assert_partial_close(bufs.outs[r], bufs.lses[r], ref_o, ref_l, wl.lse_base, tol, f"var_q shard {r}")
+    ST.run_merge(dw, bufs)
+    torch.cuda.synchronize()
+    mo, ml = O.merge([p_[0] for p_ in parts], [p_[1] for p_ in parts], [wl.lse_base] * wl.shards)
+    U.assert_partial_close(bufs.out, bufs.lse, mo, ml, "e", tol, "var_q merged")
+
+
 @pytest.mark.parametrize("kv_dtype,heads,q_len,out_dtype", [
     ("bf16", 48, 1, "f32"), ("fp8", 80, 1, "bf16"), ("bf16", 16, 3, "bf16"), ("fp8", 112, 2, "f32")])
 def test_partial_parity_partial_row_blocks(kv_dtype, heads, q_len, out_dtype):

@@ -206,6 +206,36 @@ def test_draft_rows_equal_single_row_decode_at_shorter_length():
                 np.testing.assert_array_equal(l4[:, i], l1[:, 0])
 
 
+def test_per_request_depth_rows_equal_single_row_decodes_and_padding_is_neutral():
+    """With a decode depth q_b per request (the step's q_len = the largest),
+    real row i < q_b of request b sees what a q_len=1 step of length
+    L - q_b + 1 + i sees; rows i >= q_b are padding, exactly (0, -inf); all
+    depths equal to q_len reproduce the fixed-depth result."""
+    wl4 = _tiny(q_len=4, lens=(70, 9, 4, 33, 12), heads=2, seed=13)
+    q_lens = np.array([4, 1, 0, 2, 3], dtype=np.int32)
+    var = dataclasses.replace(wl4, q_lens=q_lens)
+    full = dataclasses.replace(wl4, q_lens=np.full(5, 4, dtype=np.int32))
+    for S in (1, 3):
+        for r in range(S):
+            o4, l4 = O.decode_partial(wl4, r, S, "e")
+            of, lf = O.decode_partial(full, r, S, "e")
+            np.testing.assert_array_equal(o4, of)
+            np.testing.assert_array_equal(l4, lf)
+            ov, lv = O.decode_partial(var, r, S, "e")
+            for b in range(5):
+                qb = int(q_lens[b])
+                for i in range(4):
+                    if i >= qb:
+                        assert np.all(ov[b, i] == 0.0) and np.all(np.isneginf(lv[b, i]))
+                        continue
+                    wl1 = dataclasses.replace(wl4, batch=1, q_len=1, q=np.ascontiguousarray(wl4.q[b:b + 1, i:i + 1]),
+                                              seq_lens=np.array([wl4.seq_lens[b] - qb + 1 + i], dtype=np.int32),
+                                              block_table=wl4.block_table[b:b + 1])
+                    o1, l1 = O.decode_partial(wl1, r, S, "e")
+                    np.testing.assert_array_equal(ov[b, i], o1[0, 0])
+                    np.testing.assert_array_equal(lv[b, i], l1[0, 0])
+
+
 # --------------------------------------------------------------------------
 # merge
 # --------------------------------------------------------------------------

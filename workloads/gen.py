@@ -150,6 +150,9 @@ class Workload:
     kv_pages: np.ndarray          # [num_pages, 64, 576] uint16 (bf16) | uint8 (e4m3)
     kv_scale: float               # per-tensor dequant scale (1.0 for bf16)
     q: np.ndarray                 # [B, q_len, H, 576] uint16 (bf16)
+    # per-request decode depth (rows i < q_lens[b] are real, the rest padding
+    # up to the step's q_len); None = every request q_len deep
+    q_lens: Optional[np.ndarray] = None
 
     @property
     def max_pages(self) -> int:
@@ -209,11 +212,14 @@ def _draw_lengths(rng: np.random.Generator, batch: int, lens) -> np.ndarray:
 def make_workload(name: str, *, batch: int, heads: int, q_len: int, shards: int,
                   kv_dtype: str, lens, seed: int, lse_base: str = "e",
                   out_dtype: str = "f32", softmax_scale: float = SOFTMAX_SCALE,
-                  extra_pages: int = 0) -> Workload:
+                  extra_pages: int = 0, var_q: bool = False) -> Workload:
     """Draw one workload. ``lens`` is ("fixed", seq) | ("uniform", a, b) | ("skewed", 1, hi).
 
     ``extra_pages`` appends NaN-poisoned pages to the pool that no request
-    references (a guard against stray page indices).
+    references (a guard against stray page indices). ``var_q`` draws a
+    decode depth per request, uniform in [0, q_len] (0: a request with no
+    real query row this step), after every other draw, so the rest of the
+    workload is the same as without it.
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     seq_lens = _draw_lengths(rng, batch, lens)
@@ -258,11 +264,13 @@ def make_workload(name: str, *, batch: int, heads: int, q_len: int, shards: int,
     if extra_pages:
         kv[num_used:] = nan_code
 
+    q_lens = rng.integers(0, q_len + 1, size=batch).astype(np.int32) if var_q else None
+
     return Workload(name=name, batch=batch, heads=heads, q_len=q_len, shards=shards,
                     kv_dtype=kv_dtype, lse_base=lse_base, out_dtype=out_dtype,
                     softmax_scale=softmax_scale, seq_lens=seq_lens,
                     block_table=block_table, kv_pages=kv, kv_scale=float(kv_scale),
-                    q=q_bits)
+                    q=q_bits, q_lens=q_lens)
 
 
 def make_config(index: int, seed: Optional[int] = None, **overrides) -> Workload:
