@@ -108,7 +108,9 @@ mla_status_t mla_build_shard_metadata(const int32_t* seq_lens, const int32_t* bl
  *
  * For request b (global KV length L = seq_lens[b], which includes the q_len
  * draft rows), query row i in [0, q_len) and head h:
- *   visible owned tokens O = { t < L : t mod S == r, t <= L - q_len + i }
+ *   visible owned tokens O = { t < L : t mod S == r, t <= L - q_b + i }
+ *   with q_b = q_len, or the request's own depth q_lens[b] when given (rows
+ *   i >= q_b are padding: O is empty)
  *   s_t = softmax_scale * sum_{d<576} Q[b,i,h,d] * K_t[d]
  *   out[b,i,h,:] = sum_{t in O} exp(s_t) K_t[0:512] / sum_{t in O} exp(s_t)
  *   lse[b,i,h]   = log sum_{t in O} exp(s_t)   in `lse_base`

@@ -48,7 +48,8 @@ What it computes, and the passage each step follows:
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes): owner indexing is 0-based; for q_len > 1 the sequence length
-includes the draft rows and draft row i sees tokens t <= L - q_len + i; the
+includes the draft rows and draft row i sees tokens t <= L - q_len + i (with a
+per-request depth q_b in place of q_len when given; rows past it see none); the
 softmax scale is 1/sqrt(192) unless given; fp8 is OCP e4m3 with a per-tensor
 scale; an all-empty merge gives (0, -inf).
 """
