@@ -109,3 +109,43 @@ def test_append_then_decode_matches_the_original_workload():
     for r in range(wl.shards):
         ref_o, ref_l = O.decode_partial(wl, r, wl.shards, wl.lse_base)
         U.assert_partial_close(bufs.outs[r], bufs.lses[r], ref_o, ref_l, wl.lse_base, U.TOL["bf16"], f"shard {r}")
+
+
+def test_append_in_a_graph_matches_eager_on_every_replay():
+    """The append captured in a HIP graph (all shards' calls), replayed three
+    times on fresh pool contents with eager work and synchronisation in
+    between, writes the same pool as the eager calls each time."""
+    print("append graph replays", flush=True)
+    S = 4
+    inp = make_append_inputs(batch=32, n_new=2, kv_dtype="fp8", kv_scale=0.29, seed=91,
+                             special=[np.nan, np.inf, 1e4])
+    dev = torch.device("cuda")
+    pool0 = torch.from_numpy(inp.kv_pages.copy()).to(dev)
+    pool = pool0.clone()
+    k_nope = torch.from_numpy(inp.k_nope.view(np.int16)).to(dev).view(torch.bfloat16)
+    k_rope = torch.from_numpy(inp.k_rope.view(np.int16)).to(dev).view(torch.bfloat16)
+    lens = torch.from_numpy(inp.seq_lens).to(dev)
+    bt = torch.from_numpy(inp.block_table).to(dev)
+    for r in range(S):
+        L.mla_append_kv(k_nope, k_rope, lens, bt, pool, r, S, kv_scale=inp.kv_scale)
+    torch.cuda.synchronize()
+    eager = pool.cpu().numpy()
+    ref = inp.kv_pages
+    for r in range(S):
+        ref = O.append_kv(ref, inp.k_nope, inp.k_rope, inp.seq_lens, inp.block_table, r, S, "fp8", inp.kv_scale)
+    assert np.array_equal(eager, ref)
+    pool.copy_(pool0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for r in range(S):
+            L.mla_append_kv(k_nope, k_rope, lens, bt, pool, r, S, kv_scale=inp.kv_scale)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        pool.copy_(pool0)
+        scratch = torch.randn(1 << 16, device=dev).sum()     # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(pool.cpu().numpy(), eager), f"replay {rep}"
+        del scratch
