@@ -155,6 +155,41 @@ def test_partial_parity_per_request_depth(kv_dtype, heads, q_len, shards, out_dt
     U.assert_partial_close(bufs.out, bufs.lse, mo, ml, "e", tol, "var_q merged")
 
 
+@pytest.mark.parametrize("kv_dtype,q_len", [("bf16", 1), ("fp8", 1), ("bf16", 2)])
+def test_max_shard_count(kv_dtype, q_len):
+    """S = 16 (the largest supported): a wave's eight owned tokens span 128
+    positions and up to three pages on the block-table path. Every shard
+    through both gather paths, the metadata bit-exact, then the 16-way
+    merge against the unsharded oracle."""
+    S = 16
+    wl = make_workload("s16", batch=3, heads=16, q_len=q_len, shards=S, kv_dtype=kv_dtype,
+                       lens=("uniform", 1, 2600), seed=160 + q_len, out_dtype="bf16")
+    dw = ST.DeviceWorkload.upload(wl)
+    bufs = ST.StepBuffers(dw)
+    tol = U.TOL[kv_dtype]
+    for use_metadata in (False, True):
+        bufs.fill_nan()
+        for r in range(S):
+            _flush(f"max shards {kv_dtype} q={q_len} meta={use_metadata} shard={r}/{S}")
+            if use_metadata:
+                lmax = ST.run_metadata(dw, bufs, r)
+                ref_len, ref_max, ref_idx = O.shard_metadata(wl.seq_lens, wl.block_table, 64, wl.max_seq_len, r, S)
+                torch.cuda.synchronize()
+                assert lmax == ref_max
+                assert np.array_equal(bufs.local_seq_lens[r].cpu().numpy(), ref_len)
+                got_idx = bufs.local_kv_indices[r].cpu().numpy()
+                assert np.array_equal(got_idx[:, :ref_idx.shape[1]], ref_idx)
+            ST.run_partial(dw, bufs, r, use_metadata=use_metadata)
+            torch.cuda.synchronize()
+            ref_o, ref_l = O.decode_partial(wl, r, S, wl.lse_base)
+            U.assert_partial_close(bufs.outs[r], bufs.lses[r], ref_o, ref_l, wl.lse_base, tol,
+                                   f"S16 shard {r} meta={use_metadata}")
+    ST.run_merge(dw, bufs)
+    torch.cuda.synchronize()
+    full_o, full_l = O.decode_full(wl)
+    U.assert_partial_close(bufs.out, bufs.lse, full_o, full_l, "e", tol, "S16 merged")
+
+
 @pytest.mark.parametrize("kv_dtype,heads,q_len,out_dtype", [
     ("bf16", 48, 1, "f32"), ("fp8", 80, 1, "bf16"), ("bf16", 16, 3, "bf16"), ("fp8", 112, 2, "f32")])
 def test_partial_parity_partial_row_blocks(kv_dtype, heads, q_len, out_dtype):
