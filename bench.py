@@ -165,7 +165,7 @@ def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True, spl
     bufs = ST.StepBuffers(dws[0])
     S = wl.shards
     ev = [[(HipEvent(), HipEvent()) for _ in range(S)] for _ in range(steps)]
-    mev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    mev = [(HipEvent(), HipEvent()) for _ in range(steps)]      # the merge kernel's own dispatch
 
     # shard-local metadata is built once per decode step, not per layer: it
     # is timed on its own and not part of the step below
@@ -197,11 +197,7 @@ def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True, spl
         for r in range(S):
             ST.run_partial(dw, bufs, r, split_target=split_target, events=ev[k][r] if timed else None,
                            reuse_plan=True)
-        if timed:
-            mev[k][0].record()
-        ST.run_merge(dw, bufs)
-        if timed:
-            mev[k][1].record()
+        ST.run_merge(dw, bufs, events=mev[k] if timed else None)
 
     # kernel timing: eager steps, the attention kernel bracketed by events
     # that take its own dispatch start and end
@@ -264,7 +260,12 @@ def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True, spl
         ms_step = eager_ms_step
         step_timing = "eager launches"
     attn_ms = [[ev[k][r][0].elapsed_ms(ev[k][r][1]) for r in range(S)] for k in range(steps)]
-    merge_ms = [mev[k][0].elapsed_time(mev[k][1]) for k in range(steps)]
+    merge_ms = [mev[k][0].elapsed_ms(mev[k][1]) for k in range(steps)]
+    # merge bytes: every shard's partial (out + f32 LSE) read, the merged out
+    # and its LSE written
+    n_vec = wl.batch * wl.q_len * wl.heads
+    part_b = 2 if wl.out_dtype == "bf16" else 4
+    merge_bytes = S * n_vec * (512 * part_b + 4) + n_vec * (512 * part_b + 4)
     tot_bytes = sum(b for b, _ in per_shard)
     tot_flops = sum(f for _, f in per_shard)
     attn_total_ms = statistics.mean(sum(row) for row in attn_ms)
@@ -278,7 +279,10 @@ def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True, spl
         tflops=flops / (ms_step * 1e-3) / 1e12,
         attn_kernel_mean_us=1e3 * mean_launch_ms, attn_kernel_bytes_per_launch=tot_bytes / S,
         attn_kernel_gbs=achieved_gbs, attn_kernel_tflops=achieved_tflops,
-        merge_us=1e3 * statistics.median(merge_ms), steps=steps, warmup=warmup, rotated=len(dws),
+        merge_us=1e3 * statistics.median(merge_ms), merge_bytes=merge_bytes,
+        merge_gbs=merge_bytes / (statistics.median(merge_ms) * 1e-3) / 1e9,
+        merge_hbm_frac=merge_bytes / (statistics.median(merge_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        steps=steps, warmup=warmup, rotated=len(dws),
         metadata_us_per_shard=metadata_us, plan_us_per_shard=plan_us, step_timing=step_timing,
         eager_ms_per_step=eager_ms_step,
     )
@@ -497,7 +501,8 @@ def main() -> int:
             log(f"[bench] config {idx} {r['name']}: {r['ms_per_step']:.3f} ms/step, "
                 f"{r['kv_gbs']:.0f} KV-GB/s, {r['tflops']:.1f} TFLOP/s, attn kernel "
                 f"{r['attn_kernel_gbs']:.0f} GB/s ({100 * r['attn_kernel_hbm_frac']:.1f}% HBM, "
-                f"{100 * r['attn_kernel_mfma_frac']:.1f}% MFMA)")
+                f"{100 * r['attn_kernel_mfma_frac']:.1f}% MFMA), merge {r['merge_us']:.1f} us "
+                f"({r['merge_gbs']:.0f} GB/s, {100 * r['merge_hbm_frac']:.1f}% HBM)")
 
     cpu = None if args.no_cpu else cpu_baseline(wl, args.cpu_seconds)
     mfma_bound = res["attn_kernel_mfma_frac"] > res["attn_kernel_hbm_frac"]

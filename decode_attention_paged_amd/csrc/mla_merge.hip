@@ -41,25 +41,37 @@ __device__ __forceinline__ void store_stream(T* p, const T& v) {
   else *p = v;
 }
 
-// Eight consecutive elements of shard r's partials at element index e, as fp32.
-__device__ __forceinline__ void load8(const MergeParams& p, int r, long long e, f32x4_t& lo, f32x4_t& hi) {
-  if (p.in_bf16) {
-    const bf16x8_t x = load_stream((const bf16x8_t*)((const __bf16*)p.outs[r] + e));
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      lo[k] = (float)x[k];
-      hi[k] = (float)x[4 + k];
-    }
+// Eight consecutive elements of shard r's partials at element index e, as
+// stored: one 16-byte word group for bf16 (kept packed until they are
+// accumulated, which halves the registers that hold every shard's chunk),
+// two for f32.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+template <bool kBf16>
+struct Raw8 {
+  u32x4_t w[kBf16 ? 1 : 2];
+};
+template <bool kBf16>
+__device__ __forceinline__ Raw8<kBf16> load8(const MergeParams& p, int r, long long e) {
+  Raw8<kBf16> x;
+  if constexpr (kBf16) {
+    x.w[0] = load_stream((const u32x4_t*)((const __bf16*)p.outs[r] + e));
   } else {
-    const f32x4_t* x = (const f32x4_t*)((const float*)p.outs[r] + e);
-    lo = load_stream(x);
-    hi = load_stream(x + 1);
+    const u32x4_t* q = (const u32x4_t*)((const float*)p.outs[r] + e);
+    x.w[0] = load_stream(q);
+    x.w[1] = load_stream(q + 1);
   }
+  return x;
+}
+// element k (0..7) of a chunk as fp32 (bf16: the upper half of a binary32)
+template <bool kBf16>
+__device__ __forceinline__ float elem(const Raw8<kBf16>& x, int k) {
+  if constexpr (kBf16) return __uint_as_float((x.w[0][k >> 1] << (16 * ((k & 1) ^ 1))) & 0xFFFF0000u);
+  else return __uint_as_float(x.w[k >> 2][k & 3]);
 }
 
 // kS: shard count rounded up to a power of two (registers for kS vectors);
-// kV: vectors per wave.
-template <int kS, int kV>
+// kV: vectors per wave; kBf16: partials stored as bf16 (else f32).
+template <int kS, int kV, bool kBf16>
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeParams p) {
   const long long vec0 =
       (long long)__builtin_amdgcn_readfirstlane((int)(blockIdx.x * kMergeWaves + (threadIdx.x >> 6))) * kV;
@@ -72,7 +84,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeParams p) 
   // 512-element chunk of every shard's vector (one 16- or 32-byte load per
   // lane); a shard with weight 0 holds zeros, so loading it is harmless
   float lse2[kV][kS];
-  f32x4_t x0[kV][kS], x1[kV][kS];
+  Raw8<kBf16> x[kV][kS];
   const int e_first = 8 * lane;
   const bool have = e_first < p.dv;
 #pragma unroll
@@ -82,7 +94,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeParams p) 
     for (int r = 0; r < kS; ++r) {
       if (r < S) {
         lse2[u][r] = *(const __attribute__((address_space(4))) float*)(p.lses[r] + vec) * p.lse_to_log2[r];
-        if (have) load8(p, r, vec * p.dv + e_first, x0[u][r], x1[u][r]);
+        if (have) x[u][r] = load8<kBf16>(p, r, vec * p.dv + e_first);
       }
     }
   }
@@ -110,14 +122,17 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeParams p) 
       if (e0 != e_first) {
 #pragma unroll
         for (int r = 0; r < kS; ++r)
-          if (r < S) load8(p, r, vec * p.dv + e0, x0[u][r], x1[u][r]);
+          if (r < S) x[u][r] = load8<kBf16>(p, r, vec * p.dv + e0);
       }
       f32x4_t a0 = f32x4_t{}, a1 = f32x4_t{};
 #pragma unroll
       for (int r = 0; r < kS; ++r) {
         if (r < S && w[r] != 0.f) {
-          a0 += w[r] * x0[u][r];
-          a1 += w[r] * x1[u][r];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            a0[k] += w[r] * elem<kBf16>(x[u][r], k);
+            a1[k] += w[r] * elem<kBf16>(x[u][r], 4 + k);
+          }
         }
       }
       a0 *= inv;
@@ -179,11 +194,19 @@ hipError_t launch_merge(const MergeParams& p, hipEvent_t ev_begin, hipEvent_t ev
   const int vpw = p.num_shards <= 8 ? kMergeVecsPerWave : 1;
   const long long blocks = (p.vectors + kMergeWaves * vpw - 1) / (kMergeWaves * vpw);
   const void* fn;
-  if (p.num_shards <= 1) fn = reinterpret_cast<const void*>(&merge_kernel<1, kMergeVecsPerWave>);
-  else if (p.num_shards <= 2) fn = reinterpret_cast<const void*>(&merge_kernel<2, kMergeVecsPerWave>);
-  else if (p.num_shards <= 4) fn = reinterpret_cast<const void*>(&merge_kernel<4, kMergeVecsPerWave>);
-  else if (p.num_shards <= 8) fn = reinterpret_cast<const void*>(&merge_kernel<8, kMergeVecsPerWave>);
-  else fn = reinterpret_cast<const void*>(&merge_kernel<16, 1>);
+  if (p.in_bf16) {
+    if (p.num_shards <= 1) fn = reinterpret_cast<const void*>(&merge_kernel<1, kMergeVecsPerWave, true>);
+    else if (p.num_shards <= 2) fn = reinterpret_cast<const void*>(&merge_kernel<2, kMergeVecsPerWave, true>);
+    else if (p.num_shards <= 4) fn = reinterpret_cast<const void*>(&merge_kernel<4, kMergeVecsPerWave, true>);
+    else if (p.num_shards <= 8) fn = reinterpret_cast<const void*>(&merge_kernel<8, kMergeVecsPerWave, true>);
+    else fn = reinterpret_cast<const void*>(&merge_kernel<16, 1, true>);
+  } else {
+    if (p.num_shards <= 1) fn = reinterpret_cast<const void*>(&merge_kernel<1, kMergeVecsPerWave, false>);
+    else if (p.num_shards <= 2) fn = reinterpret_cast<const void*>(&merge_kernel<2, kMergeVecsPerWave, false>);
+    else if (p.num_shards <= 4) fn = reinterpret_cast<const void*>(&merge_kernel<4, kMergeVecsPerWave, false>);
+    else if (p.num_shards <= 8) fn = reinterpret_cast<const void*>(&merge_kernel<8, kMergeVecsPerWave, false>);
+    else fn = reinterpret_cast<const void*>(&merge_kernel<16, 1, false>);
+  }
   // the events, when given, take the kernel's own dispatch start and end
   void* args[] = {const_cast<MergeParams*>(&p)};
   return hipExtLaunchKernel(fn, dim3((unsigned)blocks), dim3(64 * kMergeWaves), args, 0, stream, ev_begin, ev_end, 0);

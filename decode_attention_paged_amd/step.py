@@ -123,12 +123,13 @@ def run_partial(dw: DeviceWorkload, bufs: StepBuffers, shard: int, use_metadata:
         split_target=split_target, events=events, reuse_plan=reuse_plan, q_lens=dw.q_lens, stream=stream)
 
 
-def run_merge(dw: DeviceWorkload, bufs: StepBuffers, out_base: int = L.LSE_BASE_E, stream=None) -> None:
+def run_merge(dw: DeviceWorkload, bufs: StepBuffers, out_base: int = L.LSE_BASE_E, stream=None,
+              events=None) -> None:
     N = dw.batch * dw.q_len
     outs = [o.view(N, dw.heads, L.D_V) for o in bufs.outs]
     lses = [l.view(N, dw.heads) for l in bufs.lses]
     L.mla_merge_partials(outs, lses, [dw.lse_base] * dw.shards, bufs.out.view(N, dw.heads, L.D_V),
-                         bufs.lse.view(N, dw.heads), lse_out_base=out_base, stream=stream)
+                         bufs.lse.view(N, dw.heads), lse_out_base=out_base, stream=stream, events=events)
 
 
 def run_step(dw: DeviceWorkload, bufs: StepBuffers, use_metadata: bool = True, split_target: int = 0,
