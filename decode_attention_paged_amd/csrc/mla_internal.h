@@ -102,6 +102,7 @@ hipError_t launch_metadata(const int32_t* seq_lens, const int32_t* block_table, 
 hipError_t launch_decode_plan(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_stream(const DecodeParams& p, bool run_plan, hipEvent_t ev_begin, hipEvent_t ev_end,
                                 hipStream_t stream);
+hipError_t launch_combine(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 

@@ -12,7 +12,7 @@
 // synchronisation) and each persistent workgroup takes a contiguous share of
 // the units of about equal cost. A segment that a workgroup holds entirely
 // is finalised in place; a segment cut at workgroup boundaries leaves one
-// bf16 partial per piece, combined by stream_combine_kernel.
+// bf16 partial per piece, combined by stream_combine_kernel (mla_combine.hip).
 //
 // Workgroup (attn_ws_kernel). Eight waves, two per SIMD: four score waves
 // (S^T = K Q^T on v_mfma_f32_32x32x16_bf16, two per row group of 32 rows,
@@ -960,102 +960,6 @@ void attn_ws_kernel(DecodeParams p) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// combine the pieces of segments cut at workgroup boundaries; neutral rows
-// for requests with no owned token
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-  return x;
-}
-
-// One wave per query row of a segment cut into np pieces: the LSE of piece c
-// sits in lane c (64 pieces at a time), and the bf16 partials of kPieces
-// pieces (8 dims per lane) are loaded together, the first group in the same
-// round trip as the LSEs; pieces are then accumulated in order.
-__global__ __launch_bounds__(256) void stream_combine_kernel(DecodeParams p) {
-  constexpr int kPieces = 8;
-  const int b = blockIdx.x;
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.y * 4 + (threadIdx.x >> 6);
-  if (row >= p.rows) return;
-  const int rb = row / p.rows_blk;
-  const int4 si = p.seg_info[b * p.row_blocks + rb];
-  const int np = si.y;
-  if (np == 1) return;
-  const long long orow = (long long)b * p.rows + row;
-  f32x4_t acc0 = f32x4_t{}, acc1 = f32x4_t{};
-  float mx = kNegInf, wsum = 0.f;
-  if (np > 1) {
-    const long long prow0 = (long long)si.x * p.rows_blk + (row - rb * p.rows_blk);
-    auto piece_lse = [&](int c) { return c < np ? p.spart_lse[prow0 + (long long)c * p.rows_blk] : kNegInf; };
-    auto piece_o = [&](int c) {
-      return *(const u32x4_t*)(p.spart_o + (prow0 + (long long)c * p.rows_blk) * kDv + 8 * lane);
-    };
-    const float lse_lo = piece_lse(lane);
-    u32x4_t xs[kPieces];
-#pragma unroll
-    for (int u = 0; u < kPieces; ++u)
-      if (u < np) xs[u] = piece_o(u);
-    mx = wave_max(lse_lo);
-    for (int c0 = 64; c0 < np; c0 += 64) mx = fmaxf(mx, wave_max(piece_lse(c0 + lane)));
-    if (mx != kNegInf) {
-      for (int c0 = 0; c0 < np; c0 += 64) {
-        const float l = c0 == 0 ? lse_lo : piece_lse(c0 + lane);
-        const float w = exp2_fast(l - mx);            // 0 for pieces past np (lse -inf)
-        wsum += wave_sum(w);
-        const int n = min(64, np - c0);
-        for (int u0 = 0; u0 < n; u0 += kPieces) {
-          if (c0 + u0 > 0) {
-#pragma unroll
-            for (int u = 0; u < kPieces; ++u)
-              if (u0 + u < n) xs[u] = piece_o(c0 + u0 + u);
-          }
-#pragma unroll
-          for (int u = 0; u < kPieces; ++u) {
-            if (u0 + u < n) {
-              const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u0 + u));
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                acc0[e] += wu * __uint_as_float(xs[u][e >> 1] << (16 * ((e & 1) ^ 1)) & 0xFFFF0000u);
-                acc1[e] += wu * __uint_as_float(xs[u][2 + (e >> 1)] << (16 * ((e & 1) ^ 1)) & 0xFFFF0000u);
-              }
-            }
-          }
-        }
-      }
-    }
-  }
-  const bool any = wsum > 0.f;
-  const float inv = any ? 1.f / wsum : 0.f;
-  acc0 *= inv;
-  acc1 *= inv;
-  if (p.out_bf16) {
-    __bf16* dst = (__bf16*)p.out + orow * kDv + 8 * lane;
-    bf16x8_t v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[e] = (__bf16)acc0[e];
-      v[4 + e] = (__bf16)acc1[e];
-    }
-    *(bf16x8_t*)dst = v;
-  } else {
-    f32x4_t* dst = (f32x4_t*)((float*)p.out + orow * kDv + 8 * lane);
-    dst[0] = acc0;
-    dst[1] = acc1;
-  }
-  if (lane == 0) {
-    const float lse2 = any ? mx + log2_fast(wsum) : kNegInf;
-    p.lse[orow] = p.lse_base2 ? lse2 : lse2 * kLn2;
-  }
-}
-
 }  // namespace
 
 hipError_t launch_decode_plan(const DecodeParams& p, hipStream_t stream) {
@@ -1082,8 +986,7 @@ hipError_t launch_decode_stream(const DecodeParams& p, bool run_plan, hipEvent_t
                : reinterpret_cast<const void*>(&attn_ws_kernel<false, false>);
   err = hipExtLaunchKernel(fn, dim3(p.grid), dim3(512), args, 0, stream, ev_begin, ev_end, 0);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(stream_combine_kernel, dim3(p.batch, (p.rows + 3) / 4), dim3(256), 0, stream, p);
-  return hipGetLastError();
+  return launch_combine(p, stream);
 }
 
 }  // namespace mla
