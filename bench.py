@@ -545,6 +545,9 @@ def main() -> int:
                                 unit="GB/s", frac=round(merge["128"]["kernel_gbs"] / HBM_PEAK_GBS, 4),
                                 kernel_us=round(merge["128"]["kernel_us_mean"], 2))
                            if merge and "128" in merge else None),
+        "merge_step": dict(us=round(res["merge_us"], 2), bytes=int(res["merge_bytes"]),
+                           gbs=round(res["merge_gbs"], 1), frac=round(res["merge_hbm_frac"], 4),
+                           shards=wl.shards, timing="the step's merge kernel, its own dispatch (eager)"),
         "append_us": append,
         "roofline": roof,
         "cpu_baseline": cpu,
