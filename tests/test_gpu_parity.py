@@ -388,3 +388,33 @@ def test_many_segments_plan_in_workspace():
         ST.run_partial(dw, bufs, r, reuse_plan=True)
         torch.cuda.synchronize()
         assert torch.equal(bufs.outs[r].view(torch.int16), first.view(torch.int16))
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_zero_length_and_tiny_requests(kv_dtype):
+    """Requests of length 0 (no token on any shard), 1 and 2 next to a
+    longer one, q_len 2 (the first draft row of a length-1 request sees
+    nothing): every such row is exactly (+0, -inf) per shard and after the
+    merge, on both gather paths."""
+    S = 3
+    wl = make_workload("zero", batch=6, heads=16, q_len=2, shards=S, kv_dtype=kv_dtype,
+                       lens=("fixed", [0, 1, 0, 65, 2, 0]), seed=3, out_dtype="bf16")
+    dw = ST.DeviceWorkload.upload(wl)
+    bufs = ST.StepBuffers(dw)
+    tol = U.TOL[kv_dtype]
+    for use_metadata in (True, False):
+        bufs.fill_nan()
+        parts = []
+        for r in range(S):
+            _flush(f"zero-length {kv_dtype} meta={use_metadata} shard {r}/{S}")
+            if use_metadata:
+                ST.run_metadata(dw, bufs, r)
+            ST.run_partial(dw, bufs, r, use_metadata=use_metadata)
+            torch.cuda.synchronize()
+            ref_o, ref_l = O.decode_partial(wl, r, S, wl.lse_base)
+            parts.append((ref_o, ref_l))
+            U.assert_partial_close(bufs.outs[r], bufs.lses[r], ref_o, ref_l, wl.lse_base, tol, f"zero shard {r}")
+        ST.run_merge(dw, bufs)
+        torch.cuda.synchronize()
+        full_o, full_l = O.decode_full(wl)
+        U.assert_partial_close(bufs.out, bufs.lse, full_o, full_l, "e", tol, "zero merged")
