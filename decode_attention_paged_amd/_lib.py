@@ -99,7 +99,7 @@ class AppendArgs(ctypes.Structure):
 
 
 EXPORTS = ("mla_build_shard_metadata", "mla_decode_workspace_bytes", "mla_decode_partial", "mla_decode_plan",
-           "mla_merge_partials", "mla_append_kv", "mla_status_string", "mla_last_error", "mla_abi_version",
+           "mla_decode_all_shards", "mla_decode_all_shards_workspace_bytes", "mla_merge_partials", "mla_append_kv", "mla_status_string", "mla_last_error", "mla_abi_version",
            "mla_sizeof_decode_args", "mla_sizeof_merge_args", "mla_sizeof_append_args")
 
 _lib = None
@@ -126,6 +126,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_decode_partial.restype = ctypes.c_int
     lib.mla_decode_plan.argtypes = [ctypes.POINTER(DecodeArgs), vp]
     lib.mla_decode_plan.restype = ctypes.c_int
+    lib.mla_decode_all_shards.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_int), vp]
+    lib.mla_decode_all_shards.restype = ctypes.c_int
+    lib.mla_decode_all_shards_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.mla_decode_all_shards_workspace_bytes.restype = sz
     lib.mla_merge_partials.argtypes = [ctypes.POINTER(MergeArgs), vp]
     lib.mla_merge_partials.restype = ctypes.c_int
     lib.mla_append_kv.argtypes = [ctypes.POINTER(AppendArgs), vp]
@@ -202,6 +206,11 @@ def mla_decode_workspace_bytes(batch: int, num_heads: int, q_len: int) -> int:
     return int(load().mla_decode_workspace_bytes(int(batch), int(num_heads), int(q_len)))
 
 
+def mla_decode_all_shards_workspace_bytes(batch: int, num_heads: int, q_len: int, num_shards: int) -> int:
+    return int(load().mla_decode_all_shards_workspace_bytes(int(batch), int(num_heads), int(q_len),
+                                                            int(num_shards)))
+
+
 def _decode_args(q, kv_pages, block_table, seq_lens, shard_id, num_shards, q_len, out, lse, workspace,
                  kv_scale, softmax_scale, lse_base, local_seq_lens, local_kv_indices, split_target, events,
                  reuse_plan, q_lens=None):
@@ -250,6 +259,23 @@ def mla_decode_partial(q, kv_pages, block_table, seq_lens, shard_id: int, num_sh
                      reuse_plan, q_lens)
     written = ctypes.c_int(-1)
     _check(lib.mla_decode_partial(ctypes.byref(a), ctypes.byref(written), _stream_ptr(stream)))
+    return int(written.value)
+
+
+def mla_decode_all_shards(q, kv_pages, block_table, seq_lens, num_shards: int, q_len: int, out, lse, workspace,
+                          *, kv_scale: float = 1.0, softmax_scale: float, lse_base: int = LSE_BASE_E,
+                          split_target: int = 0, events=None, reuse_plan: bool = False, q_lens=None,
+                          stream=None) -> int:
+    """Every shard of the cyclic split in one launch, merged: out / lse get
+    the full-context result. Shapes as mla_decode_partial; workspace of at
+    least mla_decode_all_shards_workspace_bytes(B, H, q_len, num_shards).
+    ``reuse_plan``: the workspace holds the schedule an earlier call built
+    for the same inputs. Returns the LSE base written."""
+    lib = load()
+    a = _decode_args(q, kv_pages, block_table, seq_lens, 0, num_shards, q_len, out, lse, workspace,
+                     kv_scale, softmax_scale, lse_base, None, None, split_target, events, reuse_plan, q_lens)
+    written = ctypes.c_int(-1)
+    _check(lib.mla_decode_all_shards(ctypes.byref(a), ctypes.byref(written), _stream_ptr(stream)))
     return int(written.value)
 
 

@@ -178,11 +178,19 @@ size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t q_le
   return mla::decode_workspace_layout(batch, num_heads * q_len).total;
 }
 
+size_t mla_decode_all_shards_workspace_bytes(int32_t batch, int32_t num_heads, int32_t q_len, int32_t num_shards) {
+  if (num_shards < 1 || num_shards > MLA_MAX_SHARDS) return 0;
+  if ((int64_t)batch * num_shards > 0x7FFFFFFFLL) return 0;
+  return mla_decode_workspace_bytes(batch * num_shards, num_heads, q_len);
+}
+
 }  // extern "C"
 
 // Validates the arguments and fills the kernels' parameters; `launch` is
-// false when there is nothing to run (batch 0).
-static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams& p, bool& launch) {
+// false when there is nothing to run (batch 0). `all_shards`: one launch for
+// every shard (shard_id ignored, no shard metadata, merged output).
+static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams& p, bool& launch,
+                                   bool all_shards = false) {
   launch = false;
   if (a == nullptr) return fail(MLA_STATUS_INVALID_ARGUMENT, "args is NULL");
   if (a->batch < 0) return fail(MLA_STATUS_INVALID_ARGUMENT, "batch must be >= 0 (got %d)", a->batch);
@@ -194,7 +202,7 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
     return fail(MLA_STATUS_INVALID_ARGUMENT, "page_size must be %d (got %d)", MLA_PAGE_SIZE, a->page_size);
   if (a->num_shards < 1 || a->num_shards > MLA_MAX_SHARDS)
     return fail(MLA_STATUS_INVALID_ARGUMENT, "num_shards must be in [1, %d] (got %d)", MLA_MAX_SHARDS, a->num_shards);
-  if (a->shard_id < 0 || a->shard_id >= a->num_shards)
+  if (!all_shards && (a->shard_id < 0 || a->shard_id >= a->num_shards))
     return fail(MLA_STATUS_INVALID_ARGUMENT, "shard_id %d outside [0, %d)", a->shard_id, a->num_shards);
   if (a->max_pages < 1) return fail(MLA_STATUS_INVALID_ARGUMENT, "max_pages must be >= 1 (got %d)", a->max_pages);
   if (a->num_pages < 1) return fail(MLA_STATUS_INVALID_ARGUMENT, "num_pages must be >= 1 (got %d)", a->num_pages);
@@ -212,6 +220,8 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
     return fail(MLA_STATUS_INVALID_ARGUMENT, "kv_scale must be positive and finite");
   if ((a->local_seq_lens == nullptr) != (a->local_kv_indices == nullptr))
     return fail(MLA_STATUS_INVALID_ARGUMENT, "local_seq_lens and local_kv_indices go together");
+  if (all_shards && a->local_seq_lens != nullptr)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "the all-shards decode reads the global block table: no shard metadata");
   if (a->local_kv_indices != nullptr && a->local_kv_stride < 1)
     return fail(MLA_STATUS_INVALID_ARGUMENT, "local_kv_stride must be >= 1 (got %d)", a->local_kv_stride);
   if (a->reuse_plan != 0 && a->reuse_plan != 1)
@@ -223,7 +233,10 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
       return fail(MLA_STATUS_INVALID_ARGUMENT, "q, kv_pages, block_table, seq_lens, out, lse and workspace are required");
   }
   const int32_t rows = a->num_heads * a->q_len;
-  const mla::WorkspaceLayout w = mla::decode_workspace_layout(a->batch, rows);
+  const int32_t fold = all_shards ? a->num_shards : 1;
+  if ((int64_t)a->batch * fold > 0x7FFFFFFFLL)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "batch %d x %d shards is too large", a->batch, fold);
+  const mla::WorkspaceLayout w = mla::decode_workspace_layout(a->batch * fold, rows);
   if (a->batch > 0 && a->workspace_bytes < w.total)
     return fail(MLA_STATUS_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", w.total, a->workspace_bytes);
   if (a->batch == 0) return ok();
@@ -245,8 +258,9 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
   p.rows = rows;
   p.max_pages = a->max_pages;
   p.num_pages = a->num_pages;
-  p.shard = a->shard_id;
+  p.shard = all_shards ? 0 : a->shard_id;
   p.num_shards = a->num_shards;
+  p.fold = fold;
   const float kv_scale = a->kv_dtype == MLA_DTYPE_FP8_E4M3 ? a->kv_scale : 1.f;
   p.scale_log2 = (float)((double)a->softmax_scale * (double)kv_scale * 1.4426950408889634);
   p.out_scale = kv_scale;
@@ -288,6 +302,19 @@ mla_status_t mla_decode_partial(const mla_decode_args_t* a, mla_lse_base_t* lse_
   mla::DecodeParams p;
   bool launch = false;
   const mla_status_t st = prepare_decode(a, p, launch);
+  if (st != MLA_STATUS_OK) return st;
+  if (lse_base_written) *lse_base_written = a->lse_base;
+  if (!launch) return ok();
+  hipError_t err = mla::launch_decode_stream(p, a->reuse_plan == 0, (hipEvent_t)a->event_begin,
+                                             (hipEvent_t)a->event_end, (hipStream_t)stream);
+  if (err != hipSuccess) return device_fail(err, "decode launch");
+  return ok();
+}
+
+mla_status_t mla_decode_all_shards(const mla_decode_args_t* a, mla_lse_base_t* lse_base_written, void* stream) {
+  mla::DecodeParams p;
+  bool launch = false;
+  const mla_status_t st = prepare_decode(a, p, launch, true);
   if (st != MLA_STATUS_OK) return st;
   if (lse_base_written) *lse_base_written = a->lse_base;
   if (!launch) return ok();

@@ -5,7 +5,9 @@
 // sgl-project/sglang PR 33364, Modifications, the fourth kernel) into the
 // shard's (out, lse), and writes the neutral (0, -inf) for requests whose
 // shard owns no token (prhub.com.cn digest of sgl-project/sglang PR 33926,
-// 实现拆解 step 3).
+// 实现拆解 step 3). When one launch runs every shard, the pieces of all
+// shards' segments of a row block are merged here in one pass, which is the
+// cross-shard merge of the same paragraph fused with the piece combine.
 #include "mla_device.h"
 
 namespace mla {
@@ -36,13 +38,22 @@ __global__ __launch_bounds__(256) void stream_combine_kernel(DecodeParams p) {
   const int row = blockIdx.y * 4 + (threadIdx.x >> 6);
   if (row >= p.rows) return;
   const int rb = row / p.rows_blk;
-  const int4 si = p.seg_info[b * p.row_blocks + rb];
-  const int np = si.y;
-  if (np == 1) return;
+  // pieces of the row block: those of its one segment (a segment held by one
+  // workgroup was finalised in place), or, when the launch runs several
+  // shards, those of its shards' neighbouring segments, whose partial slots
+  // are consecutive
+  const int s0 = (b * p.row_blocks + rb) * p.fold;
+  const int4 si = p.seg_info[s0];
+  int np = si.y;
+  if (p.fold == 1 && np == 1) return;
+  if (p.fold > 1) {
+    const int4 sl = p.seg_info[s0 + p.fold - 1];
+    np = sl.x + sl.y - si.x;
+  }
   const long long orow = (long long)b * p.rows + row;
   f32x4_t acc0 = f32x4_t{}, acc1 = f32x4_t{};
   float mx = kNegInf, wsum = 0.f;
-  if (np > 1) {
+  if (np > 0) {
     const long long prow0 = (long long)si.x * p.rows_blk + (row - rb * p.rows_blk);
     auto piece_lse = [&](int c) { return c < np ? p.spart_lse[prow0 + (long long)c * p.rows_blk] : kNegInf; };
     auto piece_o = [&](int c) {

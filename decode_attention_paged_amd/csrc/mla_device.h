@@ -26,15 +26,29 @@ __device__ __forceinline__ int req_len(const DecodeParams& p, int b) {
   return L > cap ? cap : L;
 }
 
-// Number of tokens of request b the shard owns (before any causal limit).
-__device__ __forceinline__ int local_count(const DecodeParams& p, int b) {
+// Number of tokens of request b shard r owns (before any causal limit).
+__device__ __forceinline__ int owned_count(const DecodeParams& p, int b, int r) {
   if (p.local_seq_lens != nullptr) {
     int n = p.local_seq_lens[b];
     n = n < 0 ? 0 : n;
     return n > p.local_kv_stride ? p.local_kv_stride : n;
   }
   const int L = req_len(p, b);
-  return L / p.num_shards + (p.shard < L % p.num_shards ? 1 : 0);
+  return L / p.num_shards + (r < L % p.num_shards ? 1 : 0);
+}
+
+// Request, row block and shard of segment s of the schedule.
+struct SegId {
+  int b, rb, r, ri;   // ri: index of the shard among those of the launch
+};
+__device__ __forceinline__ SegId seg_id(const DecodeParams& p, int s) {
+  SegId id;
+  const int q = s / p.fold;
+  id.ri = s - q * p.fold;
+  id.b = q / p.row_blocks;
+  id.rb = q - id.b * p.row_blocks;
+  id.r = p.fold > 1 ? id.ri : p.shard;
+  return id;
 }
 
 // Load through the constant address space: a wave-uniform address becomes a

@@ -26,6 +26,12 @@ struct DecodeParams {
   int32_t local_kv_stride;
   int32_t batch, heads, q_len, rows, row_blocks;
   int32_t max_pages, num_pages, shard, num_shards;
+  // shards this launch computes: 1 (shard `shard` alone), or num_shards when
+  // every shard of the batch runs in one launch; then a segment is (request,
+  // row block, shard), the shards of one row block are neighbours in the
+  // schedule, every piece leaves a partial and the combine merges all pieces
+  // of all shards into the full-context result
+  int32_t fold;
   float scale_log2;               // softmax_scale * kv_scale * log2(e)
   float out_scale;                // kv_scale (fp8) or 1
   int32_t lse_base2;              // write lse in base 2 (else natural)
@@ -35,14 +41,15 @@ struct DecodeParams {
   // workspace
   int32_t* plan;                  // [0] units, [1] workgroups in use
   // persistent schedule of the streaming kernel: the shard's work is the
-  // sequence of units (request b, row block rb, 32-token tile), ordered by
-  // segment s = b * row_blocks + rb and tile; workgroup g takes a contiguous
-  // range of units of about equal cost (tiles plus a charge per segment)
-  int32_t* req_cnt;               // [B] owned tokens per request
-  int32_t* seg_off;               // [B * row_blocks + 1] first unit of each segment
-  int32_t* seg_coff;              // [B * row_blocks + 1] cost offset of each segment
+  // sequence of units (request b, row block rb, shard, 32-token tile),
+  // ordered by segment s = (b * row_blocks + rb) * fold + (shard index) and
+  // tile; workgroup g takes a contiguous range of units of about equal cost
+  // (tiles plus a charge per segment)
+  int32_t* req_cnt;               // [B * fold] owned tokens per request and shard
+  int32_t* seg_off;               // [B * row_blocks * fold + 1] first unit of each segment
+  int32_t* seg_coff;              // [B * row_blocks * fold + 1] cost offset of each segment
   int32_t* wg_ustart;             // [grid + 1] first unit of each workgroup
-  int4* seg_info;                 // [B * row_blocks] (slot base, pieces, first workgroup, -)
+  int4* seg_info;                 // [B * row_blocks * fold] (slot base, pieces, first workgroup, -)
   int2* wg_start;                 // [grid] (segment, tile) of each workgroup's first unit
   // [grid][kRecInts] start record of each workgroup: units, first segment and
   // tile, owned-token count of that request, then the KV rows of the tokens

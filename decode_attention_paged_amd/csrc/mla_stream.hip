@@ -8,7 +8,12 @@
 //
 // Schedule. The shard's work is a sequence of units (request b, block of 64
 // query rows rb, 32-token tile), ordered by segment s = b * row_blocks + rb
-// and tile. stream_plan_kernel lays the segments out on device (no host
+// and tile. A launch may also run every shard at once (the single-launch
+// decode of all shards): a segment is then (b, rb, shard r), the S segments
+// of (b, rb) are neighbours, and the pieces of all of them are merged by
+// the combine with the same LSE-weighted reduction as the cross-shard merge
+// (github.com sgl-project/sglang PR 33364, Modifications, the fourth
+// kernel), so the shards' partials never leave the workspace. stream_plan_kernel lays the segments out on device (no host
 // synchronisation) and each persistent workgroup takes a contiguous share of
 // the units of about equal cost. A segment that a workgroup holds entirely
 // is finalised in place; a segment cut at workgroup boundaries leaves one
@@ -87,9 +92,12 @@ __device__ __forceinline__ int last_le(const int32_t* a, int n, long long x) {
   return lo;
 }
 
+__device__ __forceinline__ int seg_count(const DecodeParams& p, int s) {
+  const SegId id = seg_id(p, s);
+  return owned_count(p, id.b, id.r);
+}
 __device__ __forceinline__ int seg_tiles(const DecodeParams& p, int s) {
-  const int b = s / p.row_blocks;
-  return (local_count(p, b) + kTile - 1) / kTile;
+  return (seg_count(p, s) + kTile - 1) / kTile;
 }
 
 // One workgroup of 1024 threads; thread i handles a contiguous block of
@@ -104,7 +112,7 @@ __global__ __launch_bounds__(1024) void stream_plan_kernel(DecodeParams p) {
   __shared__ int2 s_wave[16];
   const int tid = threadIdx.x;
   const int RB = p.row_blocks;
-  const int nseg = p.batch * RB;
+  const int nseg = p.batch * RB * p.fold;
   const bool in_lds = nseg <= kPlanLdsSegs;
   int32_t* const off = in_lds ? s_arr : p.seg_off;              // unit offset of each segment
   int32_t* const coff = in_lds ? s_arr + kPlanLdsSegs + 1 : p.seg_coff;   // cost offset
@@ -115,9 +123,9 @@ __global__ __launch_bounds__(1024) void stream_plan_kernel(DecodeParams p) {
   // its queries) of this thread's segments, scanned over the block
   int su = 0, sc = 0;
   for (int s = s0; s < s1; ++s) {
-    const int b = s / RB;
-    const int cnt = local_count(p, b);
-    if (s - b * RB == 0) p.req_cnt[b] = cnt;
+    const SegId id = seg_id(p, s);
+    const int cnt = owned_count(p, id.b, id.r);
+    if (id.rb == 0) p.req_cnt[id.b * p.fold + id.ri] = cnt;
     if (in_lds) s_cnt[s] = cnt;
     const int n = (cnt + kTile - 1) / kTile;
     su += n;
@@ -175,11 +183,11 @@ __global__ __launch_bounds__(1024) void stream_plan_kernel(DecodeParams p) {
     if (u1 > u0) {
       seg = last_le(off, nseg + 1, u0);
       tile = u0 - off[seg];
-      cnt = in_lds ? s_cnt[seg] : local_count(p, seg / RB);
+      cnt = in_lds ? s_cnt[seg] : seg_count(p, seg);
       const int un = off[seg + 1];          // first unit past the first segment
       if (un < u1) {
         seg1 = last_le(off, nseg + 1, un);
-        cnt1 = in_lds ? s_cnt[seg1] : local_count(p, seg1 / RB);
+        cnt1 = in_lds ? s_cnt[seg1] : seg_count(p, seg1);
       }
     }
     rec[0] = u1 - u0;
@@ -191,13 +199,15 @@ __global__ __launch_bounds__(1024) void stream_plan_kernel(DecodeParams p) {
   }
 
   // pieces of each segment (one per non-empty workgroup it meets) and
-  // partial slots (only for segments cut into several pieces)
+  // partial slots (only for segments cut into several pieces, unless the
+  // launch runs several shards: then every piece leaves a partial)
+  const int np_slot = p.fold > 1 ? 1 : 2;
   int ms = 0;
   for (int s = s0; s < s1; ++s) {
     const int o = off[s], n = off[s + 1] - o;
     if (n > 0) {
       const int np = last_le(s_wgu, G, o + n - 1) - last_le(s_wgu, G, o) + 1;
-      ms += np > 1 ? np : 0;
+      ms += np >= np_slot ? np : 0;
     }
   }
   const int2 ex2 = block_excl_scan2(ms, 0, s_wave, tot);
@@ -210,28 +220,24 @@ __global__ __launch_bounds__(1024) void stream_plan_kernel(DecodeParams p) {
       np = last_le(s_wgu, G, o + n - 1) - first + 1;
     }
     p.seg_info[s] = make_int4(slot, np, first, 0);
-    slot += np > 1 ? np : 0;
+    slot += np >= np_slot ? np : 0;
   }
 }
 
 // ---------------------------------------------------------------------------
 // streaming attention
 // ---------------------------------------------------------------------------
-// Position in the unit sequence: request, row block, tile, and the request's
-// tile count and owned-token count. Wave-uniform.
+// Position in the unit sequence: segment, its request, row block and shard,
+// tile, and the segment's tile count and owned-token count. Wave-uniform.
 struct Cursor {
-  int b, rb, tile, ntiles, cnt;
+  int seg, b, rb, r, tile, ntiles, cnt;
 
-  __device__ __forceinline__ void start(const DecodeParams& p, int seg, int t) {
-    b = seg / p.row_blocks;
-    rb = seg - b * p.row_blocks;
-    tile = t;
-    cnt = ld_const(p.req_cnt + b);
-    ntiles = (cnt + kTile - 1) / kTile;
-  }
-  __device__ __forceinline__ void start_known(const DecodeParams& p, int seg, int t, int count) {
-    b = seg / p.row_blocks;
-    rb = seg - b * p.row_blocks;
+  __device__ __forceinline__ void start_known(const DecodeParams& p, int s, int t, int count) {
+    const SegId id = seg_id(p, s);
+    seg = s;
+    b = id.b;
+    rb = id.rb;
+    r = id.r;
     tile = t;
     cnt = count;
     ntiles = (cnt + kTile - 1) / kTile;
@@ -241,12 +247,23 @@ struct Cursor {
     if (++tile < ntiles) return;
     tile = 0;
     for (;;) {
-      if (++rb == p.row_blocks) {
-        rb = 0;
-        ++b;
-        cnt = ld_const(p.req_cnt + b);
-        ntiles = (cnt + kTile - 1) / kTile;
+      ++seg;
+      if (p.fold > 1 && ++r < p.fold) {
+        cnt = ld_const(p.req_cnt + b * p.fold + r);
+      } else {
+        const bool next_b = ++rb == p.row_blocks;
+        if (next_b) {
+          rb = 0;
+          ++b;
+        }
+        if (p.fold > 1) {
+          r = 0;
+          cnt = ld_const(p.req_cnt + b * p.fold);
+        } else if (next_b) {
+          cnt = ld_const(p.req_cnt + b);
+        }
       }
+      ntiles = (cnt + kTile - 1) / kTile;
       if (ntiles > 0) break;
     }
   }
@@ -337,7 +354,7 @@ __device__ __forceinline__ void load_entries(const DecodeParams& p, const Cursor
     te.e7 = ld_const(base + min(j0 + 7, last));
     te.p0 = 0;
   } else {
-    te.p0 = (j0 * p.num_shards + p.shard) >> 6;
+    te.p0 = (j0 * p.num_shards + c.r) >> 6;
     const int32_t* base = p.block_table + (long long)c.b * p.max_pages;
     const int last = p.max_pages - 1;
     te.e0 = ld_const(base + min(te.p0 + 0, last));
@@ -375,7 +392,7 @@ __device__ __forceinline__ const uint8_t* token_src(const DecodeParams& p, const
     const bool ok = ei >= 0 && (long long)ei < (long long)p.num_pages * kPage;
     return ok ? p.kv + (long long)ei * kRowBytes : nan;
   } else {
-    const int t = j * p.num_shards + p.shard;
+    const int t = j * p.num_shards + c.r;
     const int d = (t >> 6) - te.p0;
     unsigned eu = (unsigned)te.e0;
     eu += d >= 1 ? (unsigned)te.e1 - (unsigned)te.e0 : 0u;
@@ -593,7 +610,7 @@ void attn_ws_kernel(DecodeParams p) {
 
     int t = 0;
     while (t < Uw) {
-      const int b = cc.b, rb = cc.rb, tile0 = cc.tile, ntiles = cc.ntiles, cnt = cc.cnt;
+      const int b = cc.b, rb = cc.rb, tile0 = cc.tile, ntiles = cc.ntiles, cnt = cc.cnt, sh = cc.r, seg = cc.seg;
       const int n = min(ntiles - tile0, Uw - t);
       const int row = rb * kWsRows + rg * 32 + tok;
       const bool row_ok = row < p.rows;
@@ -622,7 +639,7 @@ void attn_ws_kernel(DecodeParams p) {
         }
         const int i = (row >= p.heads) + (row >= 2 * p.heads) + (row >= 3 * p.heads);
         for (int k = 0; k < p.q_len; ++k) {
-          const int lim = L - qb + k - p.shard;
+          const int lim = L - qb + k - sh;
           const int jl = lim >= 0 ? min(cnt, lim / p.num_shards + 1) : 0;
           jvis = i == k && k < qb ? jl : jvis;
         }
@@ -724,8 +741,9 @@ void attn_ws_kernel(DecodeParams p) {
         __syncthreads();   // P of tile t + k and the partials exchanged
         if (ds == 0) s_cur = partner_sum();
       }
-      // the last tile's softmax; row sums and LSE of the piece
-      const bool single = tile0 == 0 && n == ntiles;
+      // the last tile's softmax; row sums and LSE of the piece (finalised in
+      // place when this workgroup holds the whole segment of a one-shard launch)
+      const bool single = p.fold == 1 && tile0 == 0 && n == ntiles;
       if (ds == 0) {
         bf16x8_t pb[2];
 #pragma unroll
@@ -739,7 +757,7 @@ void attn_ws_kernel(DecodeParams p) {
           if (single) {
             p.lse[(long long)b * p.rows + row] = p.lse_base2 ? lse2 : lse2 * kLn2;
           } else {
-            const int4 si = ld_const(p.seg_info + b * p.row_blocks + rb);
+            const int4 si = ld_const(p.seg_info + seg);
             p.spart_lse[(long long)(si.x + g - si.z) * kWsRows + (row - rb * kWsRows)] = lse2;
           }
         }
@@ -867,7 +885,7 @@ void attn_ws_kernel(DecodeParams p) {
 
     int t = 0;
     while (t < Uw) {
-      const int b = cc.b, rb = cc.rb, tile0 = cc.tile, ntiles = cc.ntiles;
+      const int b = cc.b, rb = cc.rb, tile0 = cc.tile, ntiles = cc.ntiles, seg = cc.seg;
       const int n = min(ntiles - tile0, Uw - t);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
@@ -898,7 +916,7 @@ void attn_ws_kernel(DecodeParams p) {
         inv[0] = a0 ? p.out_scale / l0 : 0.f;
         inv[1] = a1 ? p.out_scale / l1 : 0.f;
       }
-      const bool single = tile0 == 0 && n == ntiles;
+      const bool single = p.fold == 1 && tile0 == 0 && n == ntiles;
       const int row0 = rb * kWsRows;
       if (single && !p.out_bf16) {
 #pragma unroll
@@ -938,7 +956,7 @@ void attn_ws_kernel(DecodeParams p) {
         if (single) {
           obase = (__bf16*)p.out + ((long long)b * p.rows + row0) * kDv;
         } else {
-          const int4 si = ld_const(p.seg_info + b * p.row_blocks + rb);
+          const int4 si = ld_const(p.seg_info + seg);
           obase = (__bf16*)p.spart_o + ((long long)(si.x + g - si.z) * kWsRows) * kDv;
         }
         const int rr0 = lane >> 4, c16 = lane & 15;

@@ -158,3 +158,22 @@ def run_step_concurrent(dw: DeviceWorkload, bufs: StepBuffers, streams, use_meta
     for r in range(dw.shards):
         cur.wait_stream(streams[r])
     run_merge(dw, bufs, out_base=out_base, stream=cur)
+
+
+def all_shards_workspace(dw: DeviceWorkload, bufs: StepBuffers):
+    """Workspace of the single-launch decode of every shard (allocated once)."""
+    import torch
+    if getattr(bufs, "all_workspace", None) is None:
+        n = L.mla_decode_all_shards_workspace_bytes(dw.batch, dw.heads, dw.q_len, dw.shards)
+        bufs.all_workspace = torch.empty((max(n, 1),), dtype=torch.uint8, device=dw.q.device)
+    return bufs.all_workspace
+
+
+def run_all_shards(dw: DeviceWorkload, bufs: StepBuffers, out_base: int = L.LSE_BASE_E, split_target: int = 0,
+                   events=None, reuse_plan: bool = False, stream=None) -> int:
+    """Every shard in one launch with the merge fused, into bufs.out / bufs.lse."""
+    ws = all_shards_workspace(dw, bufs)
+    return L.mla_decode_all_shards(dw.q, dw.kv_pages, dw.block_table, dw.seq_lens, dw.shards, dw.q_len,
+                                   bufs.out, bufs.lse, ws, kv_scale=dw.kv_scale, softmax_scale=dw.softmax_scale,
+                                   lse_base=out_base, split_target=split_target, events=events,
+                                   reuse_plan=reuse_plan, q_lens=dw.q_lens, stream=stream)

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 5
+#define MLA_ABI_VERSION 6
 #define MLA_PAGE_SIZE 64
 #define MLA_D_QK 576
 #define MLA_D_V 512
@@ -197,6 +197,37 @@ mla_status_t mla_decode_partial(const mla_decode_args_t* args, mla_lse_base_t* l
  * workgroups' shares of (request, row block, 32-token tile) units, balanced
  * by cost, with the pieces of requests cut at workgroup boundaries. */
 mla_status_t mla_decode_plan(const mla_decode_args_t* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Single-launch decode of every shard, merge fused.
+ *
+ * Runs all num_shards shards of the cyclic split in one schedule ([DCP
+ * decode] 功能与动机 and 实现拆解 step 3: shard r attends over the tokens
+ * t = j S + r it owns) and merges their partials with the LSE-weighted
+ * reduction of [symm_a2a] Modifications (fourth kernel) inside the same
+ * call: the pieces of every shard's share of a request are combined in one
+ * pass, so no per-shard (out, lse) is written or re-read. `out` / `lse`
+ * receive the merged result, which is the full-context attention of every
+ * query row (the per-shard formula above with O the union over r):
+ *   out[b,i,h,:] = merge_r (out_r, lse_r),  lse[b,i,h] = log sum_r exp(lse_r)
+ * and (0, -inf) for a row that sees no token (L = 0, or a padding row).
+ * Arguments as mla_decode_partial, except: shard_id is ignored; shard
+ * metadata (local_seq_lens / local_kv_indices) must be NULL (KV rows come
+ * from block_table); the workspace size comes from
+ * mla_decode_all_shards_workspace_bytes; reuse_plan = 1 reuses the schedule
+ * a previous mla_decode_all_shards call (reuse_plan = 0) built in the same
+ * workspace for the same batch, num_heads, q_len, num_shards, max_pages,
+ * split_target and seq_lens contents; event_begin / event_end time the
+ * attention kernel. Errors: those of mla_decode_partial, and
+ * INVALID_ARGUMENT for shard metadata or batch x num_shards >= 2^31.
+ * Nothing is allocated; every kernel of the call is safe to capture in a
+ * HIP graph (no memset nodes). */
+mla_status_t mla_decode_all_shards(const mla_decode_args_t* args, mla_lse_base_t* lse_base_written,
+                                   void* stream);
+
+/* Workspace bytes of mla_decode_all_shards (host only; 0 for invalid sizes). */
+size_t mla_decode_all_shards_workspace_bytes(int32_t batch, int32_t num_heads, int32_t q_len,
+                                             int32_t num_shards);
 
 /* ------------------------------------------------------------------------
  * Cross-shard merge.

@@ -39,7 +39,7 @@ def test_struct_layouts_and_version(lib):
     assert lib.mla_sizeof_decode_args() == ctypes.sizeof(L.DecodeArgs)
     assert lib.mla_sizeof_merge_args() == ctypes.sizeof(L.MergeArgs)
     assert lib.mla_sizeof_append_args() == ctypes.sizeof(L.AppendArgs)
-    assert lib.mla_abi_version() == 5
+    assert lib.mla_abi_version() == 6
     assert lib.mla_status_string(L.STATUS_INVALID_ARGUMENT) == b"invalid argument"
 
 
@@ -98,6 +98,35 @@ def test_empty_batch_is_ok_without_device(lib):
     a.batch = 0
     written = ctypes.c_int(-1)
     assert lib.mla_decode_partial(ctypes.byref(a), ctypes.byref(written), None) == L.STATUS_OK
+    assert written.value == L.LSE_BASE_E
+
+
+def test_all_shards_workspace_and_argument_errors(lib):
+    # the single launch of every shard schedules B x S segments
+    assert lib.mla_decode_all_shards_workspace_bytes(8, 64, 1, 4) == lib.mla_decode_workspace_bytes(32, 64, 1)
+    assert lib.mla_decode_all_shards_workspace_bytes(8, 64, 1, 1) == lib.mla_decode_workspace_bytes(8, 64, 1)
+    assert lib.mla_decode_all_shards_workspace_bytes(8, 64, 1, 17) == 0
+    assert lib.mla_decode_all_shards_workspace_bytes(8, 64, 1, 0) == 0
+    assert lib.mla_decode_all_shards_workspace_bytes(8, 17, 1, 2) == 0
+    for field, value, status in [("local_seq_lens", 0x2000, L.STATUS_INVALID_ARGUMENT),
+                                 ("num_shards", 17, L.STATUS_INVALID_ARGUMENT),
+                                 ("q_len", 5, L.STATUS_INVALID_ARGUMENT),
+                                 ("workspace_bytes", 0, L.STATUS_WORKSPACE_TOO_SMALL)]:
+        a = _valid_args()
+        setattr(a, field, value)
+        if field == "local_seq_lens":
+            a.local_kv_indices, a.local_kv_stride = 0x3000, 8
+        assert lib.mla_decode_all_shards(ctypes.byref(a), None, None) == status, field
+        assert lib.mla_last_error()
+    # the workspace of one shard's decode is too small for all of them
+    a = _valid_args()
+    a.workspace_bytes = lib.mla_decode_workspace_bytes(a.batch, a.num_heads, a.q_len)
+    assert lib.mla_decode_all_shards(ctypes.byref(a), None, None) == L.STATUS_WORKSPACE_TOO_SMALL
+    # shard_id is ignored; an empty batch runs nothing
+    a = _valid_args()
+    a.batch, a.shard_id = 0, 9
+    written = ctypes.c_int(-1)
+    assert lib.mla_decode_all_shards(ctypes.byref(a), ctypes.byref(written), None) == L.STATUS_OK
     assert written.value == L.LSE_BASE_E
 
 
