@@ -286,6 +286,8 @@ def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True, spl
         metadata_us_per_shard=metadata_us, plan_us_per_shard=plan_us, step_timing=step_timing,
         eager_ms_per_step=eager_ms_step,
     )
+    if use_graph and split_target == 0:
+        res["all_shards"] = bench_all_shards(wl, dws, bufs, steps, warmup, kv_bytes, flops)
     # the contraction runs on bf16 MFMAs for both KV types (fp8 pages are
     # converted to bf16 exactly, in registers), so its peak is the bf16 one
     peak_tf = BF16_PEAK_TFLOPS
@@ -294,6 +296,73 @@ def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True, spl
     del dws, bufs
     torch.cuda.empty_cache()
     return wl, res
+
+
+def bench_all_shards(wl, dws, bufs, steps: int, warmup: int, kv_bytes: int, flops: float):
+    """The same step as one call: every shard in one launch, the merge fused
+    into the piece combine (mla_decode_all_shards). Its schedule is built
+    once per decode step and reused; the call is captured as a HIP graph per
+    input set, checked bit for bit against the eager call and against the
+    separate step's merged output (within the KV type's tolerance), then
+    replayed for the step time. The attention kernel is timed on its own
+    dispatch in eager calls."""
+    import torch
+
+    from decode_attention_paged_amd import step as ST
+
+    tol = 6e-2 if wl.kv_dtype == "fp8" else 2e-2
+    sep_out, sep_lse = bufs.out.clone(), bufs.lse.clone()     # the separate step's last result
+    log(f"[bench] {wl.name}: single-launch step of all shards")
+    ST.run_all_shards(dws[0], bufs)                              # builds the schedule
+    torch.cuda.synchronize()
+    d_out = (bufs.out.float() - sep_out.float()).abs().max().item()
+    fin = torch.isfinite(sep_lse)
+    d_lse = (bufs.lse[fin] - sep_lse[fin]).abs().max().item() if bool(fin.any()) else 0.0
+    if not (d_out <= tol and d_lse <= tol and torch.equal(torch.isfinite(bufs.lse), fin)):
+        raise RuntimeError(f"single-launch step differs from the separate step ({d_out}, {d_lse})")
+    aev = [(HipEvent(), HipEvent()) for _ in range(steps)]
+    for k in range(warmup):
+        ST.run_all_shards(dws[k % len(dws)], bufs, reuse_plan=True)
+    for k in range(steps):
+        ST.run_all_shards(dws[k % len(dws)], bufs, reuse_plan=True, events=aev[k])
+    torch.cuda.synchronize()
+    attn_ms = statistics.mean(a.elapsed_ms(b) for a, b in aev)
+    graphs = []
+    for dw in dws:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            ST.run_all_shards(dw, bufs, reuse_plan=True)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i, dw in enumerate(dws):
+        ST.run_all_shards(dw, bufs, reuse_plan=True)
+        torch.cuda.synchronize()
+        ref_out, ref_lse = bufs.out.clone(), bufs.lse.clone()
+        bufs.fill_nan()
+        graphs[i].replay()
+        torch.cuda.synchronize()
+        if not (torch.equal(bufs.out.view(torch.uint8), ref_out.view(torch.uint8))
+                and torch.equal(bufs.lse.view(torch.uint8), ref_lse.view(torch.uint8))):
+            raise RuntimeError("graph replay of the single-launch step differs from the eager call")
+    for k in range(warmup):
+        graphs[k % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        graphs[k % len(graphs)].replay()
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / steps
+    del graphs
+    # algorithmic bytes of the call: every owned row once, the queries once
+    # per shard (each shard's segments load them), the merged out and LSE
+    rows = wl.batch * wl.q_len * wl.heads
+    out_elt = 2 if wl.out_dtype == "bf16" else 4
+    call_bytes = kv_bytes + wl.shards * rows * 576 * 2 + rows * (512 * out_elt + 4)
+    return dict(ms_per_step=ms, kv_gbs=kv_bytes / (ms * 1e-3) / 1e9, tflops=flops / (ms * 1e-3) / 1e12,
+                attn_kernel_us=1e3 * attn_ms, call_bytes=call_bytes,
+                attn_kernel_gbs=call_bytes / (attn_ms * 1e-3) / 1e9,
+                attn_kernel_hbm_frac=call_bytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                max_abs_diff_vs_separate=dict(out=d_out, lse=d_lse))
 
 
 def bench_merge_sweep(replays: int = 20, warmup: int = 5):
@@ -503,6 +572,11 @@ def main() -> int:
                 f"{r['attn_kernel_gbs']:.0f} GB/s ({100 * r['attn_kernel_hbm_frac']:.1f}% HBM, "
                 f"{100 * r['attn_kernel_mfma_frac']:.1f}% MFMA), merge {r['merge_us']:.1f} us "
                 f"({r['merge_gbs']:.0f} GB/s, {100 * r['merge_hbm_frac']:.1f}% HBM)")
+            if "all_shards" in r:
+                a = r["all_shards"]
+                log(f"[bench] config {idx} {r['name']} single launch: {a['ms_per_step']:.3f} ms/step, "
+                    f"{a['kv_gbs']:.0f} KV-GB/s, attn kernel {a['attn_kernel_us']:.1f} us "
+                    f"({100 * a['attn_kernel_hbm_frac']:.1f}% HBM)")
 
     cpu = None if args.no_cpu else cpu_baseline(wl, args.cpu_seconds)
     mfma_bound = res["attn_kernel_mfma_frac"] > res["attn_kernel_hbm_frac"]
@@ -549,6 +623,13 @@ def main() -> int:
                            gbs=round(res["merge_gbs"], 1), frac=round(res["merge_hbm_frac"], 4),
                            shards=wl.shards, timing="the step's merge kernel, its own dispatch (eager)"),
         "append_us": append,
+        "all_shards_step": (dict(ms_per_step=round(res["all_shards"]["ms_per_step"], 5),
+                                 kv_gbs=round(res["all_shards"]["kv_gbs"], 1),
+                                 attn_kernel_us=round(res["all_shards"]["attn_kernel_us"], 2),
+                                 attn_kernel_hbm_frac=round(res["all_shards"]["attn_kernel_hbm_frac"], 4),
+                                 timing="mla_decode_all_shards: every shard in one launch, merge fused, "
+                                        "graph replay; schedule built once per step")
+                            if "all_shards" in res else None),
         "roofline": roof,
         "cpu_baseline": cpu,
     }
