@@ -242,13 +242,15 @@ struct Cursor {
     cnt = count;
     ntiles = (cnt + kTile - 1) / kTile;
   }
-  // move to the next unit; only called when one exists
+  // move to the next unit; only called when one exists (kFold: the launch
+  // runs every shard, p.fold > 1)
+  template <bool kFold>
   __device__ __forceinline__ void advance(const DecodeParams& p) {
     if (++tile < ntiles) return;
     tile = 0;
     for (;;) {
       ++seg;
-      if (p.fold > 1 && ++r < p.fold) {
+      if (kFold && ++r < p.fold) {
         cnt = ld_const(p.req_cnt + b * p.fold + r);
       } else {
         const bool next_b = ++rb == p.row_blocks;
@@ -256,7 +258,7 @@ struct Cursor {
           rb = 0;
           ++b;
         }
-        if (p.fold > 1) {
+        if (kFold) {
           r = 0;
           cnt = ld_const(p.req_cnt + b * p.fold);
         } else if (next_b) {
@@ -523,7 +525,7 @@ __device__ __forceinline__ void copy8_tile_part_rt(int j, const uint8_t* srcw, u
 constexpr int kWsRows = 64;
 constexpr int kWsStagePitch = 272;     // output staging row: 128 bf16 + 16 bytes
 
-template <bool kLocal, bool kFp8>
+template <bool kLocal, bool kFp8, bool kFold>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_ws_kernel(DecodeParams p) {
   constexpr int kNS = 4;
@@ -743,7 +745,7 @@ void attn_ws_kernel(DecodeParams p) {
       }
       // the last tile's softmax; row sums and LSE of the piece (finalised in
       // place when this workgroup holds the whole segment of a one-shard launch)
-      const bool single = p.fold == 1 && tile0 == 0 && n == ntiles;
+      const bool single = !kFold && tile0 == 0 && n == ntiles;
       if (ds == 0) {
         bf16x8_t pb[2];
 #pragma unroll
@@ -767,7 +769,7 @@ void attn_ws_kernel(DecodeParams p) {
       t += n;
       if (t < Uw) {
         cc.tile = ntiles - 1;
-        cc.advance(p);
+        cc.template advance<kFold>(p);
       }
     }
     wait_vmcnt<0>();
@@ -821,7 +823,7 @@ void attn_ws_kernel(DecodeParams p) {
     int ncopied = 2;
     TileEntries te;
     if (2 < Uw) {
-      cl.advance(p);
+      cl.template advance<kFold>(p);
       load_entries<kLocal>(p, cl, wq, te);
     }
     // tile barrier: the next scores' tile has landed in every wave and the
@@ -835,7 +837,7 @@ void attn_ws_kernel(DecodeParams p) {
       for (int j = 0; j < kCopies; ++j) copy_part(j, csrc, cst);
       ++ncopied;
       if (ncopied < Uw) {
-        cl.advance(p);
+        cl.template advance<kFold>(p);
         load_entries<kLocal>(p, cl, wq, te);
       }
     };
@@ -916,7 +918,7 @@ void attn_ws_kernel(DecodeParams p) {
         inv[0] = a0 ? p.out_scale / l0 : 0.f;
         inv[1] = a1 ? p.out_scale / l1 : 0.f;
       }
-      const bool single = p.fold == 1 && tile0 == 0 && n == ntiles;
+      const bool single = !kFold && tile0 == 0 && n == ntiles;
       const int row0 = rb * kWsRows;
       if (single && !p.out_bf16) {
 #pragma unroll
@@ -970,7 +972,7 @@ void attn_ws_kernel(DecodeParams p) {
       t += n;
       if (t < Uw) {
         cc.tile = ntiles - 1;
-        cc.advance(p);
+        cc.template advance<kFold>(p);
       }
     }
     // no copy may still be writing this workgroup's LDS when it exits
@@ -995,13 +997,19 @@ hipError_t launch_decode_stream(const DecodeParams& p, bool run_plan, hipEvent_t
   // times (recorded with the dispatch, no separate marker packets)
   void* args[] = {const_cast<DecodeParams*>(&p)};
   const void* fn;
+  // the launch of every shard reads the global block table (no shard
+  // metadata) and is an instantiation of its own
   const bool local = p.local_kv_indices != nullptr;
+  const bool fold = p.fold > 1;
+  if (fold && local) return hipErrorInvalidValue;
   if (p.kv_fp8)
-    fn = local ? reinterpret_cast<const void*>(&attn_ws_kernel<true, true>)
-               : reinterpret_cast<const void*>(&attn_ws_kernel<false, true>);
+    fn = fold    ? reinterpret_cast<const void*>(&attn_ws_kernel<false, true, true>)
+         : local ? reinterpret_cast<const void*>(&attn_ws_kernel<true, true, false>)
+                 : reinterpret_cast<const void*>(&attn_ws_kernel<false, true, false>);
   else
-    fn = local ? reinterpret_cast<const void*>(&attn_ws_kernel<true, false>)
-               : reinterpret_cast<const void*>(&attn_ws_kernel<false, false>);
+    fn = fold    ? reinterpret_cast<const void*>(&attn_ws_kernel<false, false, true>)
+         : local ? reinterpret_cast<const void*>(&attn_ws_kernel<true, false, false>)
+                 : reinterpret_cast<const void*>(&attn_ws_kernel<false, false, false>);
   err = hipExtLaunchKernel(fn, dim3(p.grid), dim3(512), args, 0, stream, ev_begin, ev_end, 0);
   if (err != hipSuccess) return err;
   return launch_combine(p, stream);
