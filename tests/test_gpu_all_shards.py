@@ -200,3 +200,40 @@ def test_all_shards_matches_the_separate_step_and_graph_replays():
                            eager_o.view(torch.int16) if eager_o.dtype == torch.bfloat16 else eager_o.view(torch.int32)), rep
         assert torch.equal(bufs.lse.view(torch.int32), eager_l.view(torch.int32)), rep
         del scratch
+
+
+def test_all_shards_short_requests_with_empty_shards():
+    """Lengths 0..7 with S = 8: most shards own nothing; the merged rows match
+    the oracle and the request of length 0 is exactly (+0, -inf)."""
+    wl = make_workload("short", batch=8, heads=32, q_len=1, shards=8, kv_dtype="bf16",
+                       lens=("fixed", (1, 2, 3, 4, 5, 6, 7, 0)), seed=5, out_dtype="bf16")
+    dw = ST.DeviceWorkload.upload(wl)
+    bufs = ST.StepBuffers(dw)
+    bufs.fill_nan()
+    _flush("all shards short requests, S 8")
+    ST.run_all_shards(dw, bufs, out_base=L.LSE_BASE_2)
+    torch.cuda.synchronize()
+    _check(wl, bufs, "short", out_base="2")
+    mo, ml = bufs.out.float().cpu().numpy(), bufs.lse.cpu().numpy()
+    assert np.all(mo[7] == 0) and not np.signbit(mo[7]).any() and np.all(np.isneginf(ml[7]))
+    assert np.all(np.isfinite(ml[:7]))
+
+
+def test_all_shards_bad_page_ids_poison_instead_of_faulting():
+    """A page id outside the pool (and a negative one) reads the NaN row:
+    the request that owns it is poisoned on every shard's share, the other
+    request is untouched."""
+    wl = make_workload("bad", batch=3, heads=16, q_len=1, shards=2, kv_dtype="bf16",
+                       lens=("fixed", (100, 50, 130)), seed=9)
+    ok_o, ok_l = O.decode_full(wl, requests=[1])
+    wl.block_table[0, 1] = 10_000          # outside the pool
+    wl.block_table[2, 2] = -5              # negative
+    dw = ST.DeviceWorkload.upload(wl)
+    bufs = ST.StepBuffers(dw)
+    bufs.fill_nan()
+    _flush("all shards bad page ids")
+    ST.run_all_shards(dw, bufs)
+    torch.cuda.synchronize()
+    o = bufs.out.float().cpu().numpy()
+    assert np.isnan(o[0]).any() and np.isnan(o[2]).any()
+    U.assert_partial_close(bufs.out[[1]], bufs.lse[[1]], ok_o, ok_l, "e", U.TOL["bf16"], "untouched request")
