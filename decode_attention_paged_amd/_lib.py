@@ -58,6 +58,9 @@ class DecodeArgs(ctypes.Structure):
         ("event_end", ctypes.c_void_p),
         ("reuse_plan", ctypes.c_int32),
         ("q_lens", ctypes.c_void_p),
+        ("q_rope", ctypes.c_void_p),
+        ("q_row_stride", ctypes.c_int64),
+        ("q_rope_row_stride", ctypes.c_int64),
     ]
 
 
@@ -202,6 +205,17 @@ def mla_build_shard_metadata(seq_lens, block_table, max_seq_len: int, shard_id: 
     return int(lmax.value)
 
 
+def mla_shard_local_max(max_seq_len: int, shard_id: int, num_shards: int) -> int:
+    """The shard-local length bound (the local max) for a step whose longest
+    request has ``max_seq_len`` tokens, from mla_build_shard_metadata with an
+    empty batch (host only: nothing is enqueued and no device memory read)."""
+    lib = load()
+    lmax = ctypes.c_int32(0)
+    _check(lib.mla_build_shard_metadata(None, None, 0, 1, PAGE_SIZE, int(max_seq_len), int(shard_id),
+                                        int(num_shards), None, None, 0, ctypes.byref(lmax), None))
+    return int(lmax.value)
+
+
 def mla_decode_workspace_bytes(batch: int, num_heads: int, q_len: int) -> int:
     return int(load().mla_decode_workspace_bytes(int(batch), int(num_heads), int(q_len)))
 
@@ -211,13 +225,33 @@ def mla_decode_all_shards_workspace_bytes(batch: int, num_heads: int, q_len: int
                                                             int(num_shards)))
 
 
+def _row_stride(t, dims: int, what: str) -> int:
+    """Elements between consecutive query rows of a [B, q_len, H, dims] view
+    whose rows are evenly spaced (the last dim contiguous)."""
+    if t.dim() != 4 or int(t.shape[3]) != dims or t.stride(3) != 1:
+        raise ValueError(f"{what} must be a [B, q_len, H, {dims}] view with a contiguous last dim")
+    B, ql, H = int(t.shape[0]), int(t.shape[1]), int(t.shape[2])
+    rs = t.stride(2)
+    if (ql > 1 and t.stride(1) != H * rs) or (B > 1 and t.stride(0) != ql * H * rs):
+        raise ValueError(f"{what}: query rows must be evenly spaced in (b, i, h) order")
+    return int(rs)
+
+
 def _decode_args(q, kv_pages, block_table, seq_lens, shard_id, num_shards, q_len, out, lse, workspace,
                  kv_scale, softmax_scale, lse_base, local_seq_lens, local_kv_indices, split_target, events,
-                 reuse_plan, q_lens=None):
+                 reuse_plan, q_lens=None, q_rope=None):
     a = DecodeArgs()
     B, ql, H = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
     if ql != q_len:
         raise ValueError("q.shape[1] must equal q_len")
+    if q_rope is None:
+        a.q_row_stride = _row_stride(q, D_QK, "q")
+    else:
+        if tuple(q_rope.shape[:3]) != (B, ql, H):
+            raise ValueError("q and q_rope must agree in [B, q_len, H]")
+        a.q_row_stride = _row_stride(q, 512, "q (latent part)")
+        a.q_rope_row_stride = _row_stride(q_rope, D_QK - 512, "q_rope")
+        a.q_rope = _ptr(q_rope)
     a.q, a.kv_pages, a.block_table, a.seq_lens = _ptr(q), _ptr(kv_pages), _ptr(block_table), _ptr(seq_lens)
     a.local_seq_lens, a.local_kv_indices = _ptr(local_seq_lens), _ptr(local_kv_indices)
     a.local_kv_stride = int(local_kv_indices.shape[1]) if local_kv_indices is not None else 0
@@ -241,7 +275,7 @@ def mla_decode_partial(q, kv_pages, block_table, seq_lens, shard_id: int, num_sh
                        out, lse, workspace, *, kv_scale: float = 1.0, softmax_scale: float,
                        lse_base: int = LSE_BASE_E, local_seq_lens=None, local_kv_indices=None,
                        split_target: int = 0, events=None, reuse_plan: bool = False, q_lens=None,
-                       stream=None) -> int:
+                       q_rope=None, stream=None) -> int:
     """Rank-local (out, lse) of one shard; returns the LSE base written.
 
     q [B, q_len, H, 576] bf16; kv_pages [P, 64, 576] bf16 or uint8 (e4m3);
@@ -251,12 +285,14 @@ def mla_decode_partial(q, kv_pages, block_table, seq_lens, shard_id: int, num_sh
     timing events recorded around the attention kernel. ``reuse_plan``: the
     workspace holds the schedule mla_decode_plan built for the same inputs.
     ``q_lens``: optional [B] i32 decode depth per request (rows past it are
-    padding, written (0, -inf)).
+    padding, written (0, -inf)). ``q_rope``: optional [B, q_len, H, 64] bf16
+    rope part of the query; then ``q`` is the [B, q_len, H, 512] latent part
+    (either may be a strided view, e.g. two slices of one buffer).
     """
     lib = load()
     a = _decode_args(q, kv_pages, block_table, seq_lens, shard_id, num_shards, q_len, out, lse, workspace,
                      kv_scale, softmax_scale, lse_base, local_seq_lens, local_kv_indices, split_target, events,
-                     reuse_plan, q_lens)
+                     reuse_plan, q_lens, q_rope)
     written = ctypes.c_int(-1)
     _check(lib.mla_decode_partial(ctypes.byref(a), ctypes.byref(written), _stream_ptr(stream)))
     return int(written.value)
@@ -265,15 +301,17 @@ def mla_decode_partial(q, kv_pages, block_table, seq_lens, shard_id: int, num_sh
 def mla_decode_all_shards(q, kv_pages, block_table, seq_lens, num_shards: int, q_len: int, out, lse, workspace,
                           *, kv_scale: float = 1.0, softmax_scale: float, lse_base: int = LSE_BASE_E,
                           split_target: int = 0, events=None, reuse_plan: bool = False, q_lens=None,
-                          stream=None) -> int:
+                          q_rope=None, stream=None) -> int:
     """Every shard of the cyclic split in one launch, merged: out / lse get
     the full-context result. Shapes as mla_decode_partial; workspace of at
     least mla_decode_all_shards_workspace_bytes(B, H, q_len, num_shards).
     ``reuse_plan``: the workspace holds the schedule an earlier call built
-    for the same inputs. Returns the LSE base written."""
+    for the same inputs. ``q_rope``: as for mla_decode_partial. Returns the
+    LSE base written."""
     lib = load()
     a = _decode_args(q, kv_pages, block_table, seq_lens, 0, num_shards, q_len, out, lse, workspace,
-                     kv_scale, softmax_scale, lse_base, None, None, split_target, events, reuse_plan, q_lens)
+                     kv_scale, softmax_scale, lse_base, None, None, split_target, events, reuse_plan, q_lens,
+                     q_rope)
     written = ctypes.c_int(-1)
     _check(lib.mla_decode_all_shards(ctypes.byref(a), ctypes.byref(written), _stream_ptr(stream)))
     return int(written.value)

@@ -232,6 +232,19 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
     if (!a->q || !a->kv_pages || !a->block_table || !a->seq_lens || !a->out || !a->lse || !a->workspace)
       return fail(MLA_STATUS_INVALID_ARGUMENT, "q, kv_pages, block_table, seq_lens, out, lse and workspace are required");
   }
+  {
+    const bool split = a->q_rope != nullptr;
+    const int64_t qs = a->q_row_stride == 0 ? (split ? 512 : MLA_D_QK) : a->q_row_stride;
+    const int64_t rs = a->q_rope_row_stride == 0 ? 64 : a->q_rope_row_stride;
+    if (qs < (split ? 512 : MLA_D_QK) || qs % 8 != 0)
+      return fail(MLA_STATUS_INVALID_ARGUMENT, "q_row_stride %lld must be a multiple of 8 and >= %d",
+                  (long long)a->q_row_stride, split ? 512 : MLA_D_QK);
+    if (split && (rs < 64 || rs % 8 != 0))
+      return fail(MLA_STATUS_INVALID_ARGUMENT, "q_rope_row_stride %lld must be a multiple of 8 and >= 64",
+                  (long long)a->q_rope_row_stride);
+    if (((uintptr_t)a->q & 15) != 0 || ((uintptr_t)a->q_rope & 15) != 0)
+      return fail(MLA_STATUS_INVALID_ARGUMENT, "q and q_rope must be 16-byte aligned");
+  }
   const int32_t rows = a->num_heads * a->q_len;
   const int32_t fold = all_shards ? a->num_shards : 1;
   if ((int64_t)a->batch * fold > 0x7FFFFFFFLL)
@@ -245,6 +258,15 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
   if (device_cus(&cus) != 0) return fail(MLA_STATUS_DEVICE_ERROR, "cannot query the current device");
   p = mla::DecodeParams{};
   p.q = (const uint16_t*)a->q;
+  if (a->q_rope != nullptr) {
+    p.q_rope = (const uint16_t*)a->q_rope;
+    p.q_stride = a->q_row_stride == 0 ? 512 : a->q_row_stride;
+    p.q_rope_stride = a->q_rope_row_stride == 0 ? 64 : a->q_rope_row_stride;
+  } else {
+    p.q_rope = p.q + 512;
+    p.q_stride = a->q_row_stride == 0 ? MLA_D_QK : a->q_row_stride;
+    p.q_rope_stride = p.q_stride;
+  }
   p.kv = (const uint8_t*)a->kv_pages;
   p.block_table = a->block_table;
   p.seq_lens = a->seq_lens;

@@ -13,10 +13,14 @@
 namespace mla {
 namespace {
 
+// Max over the wave that propagates NaN: a piece that read a poisoned KV
+// row carries a NaN LSE, and the row it contributes to must come out NaN
+// (out and LSE), not be skipped as if it were empty (fmaxf alone drops NaN).
 __device__ __forceinline__ float wave_max(float x) {
+  const bool nan = __ballot(x != x) != 0;
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
-  return x;
+  return nan ? __builtin_nanf("") : x;
 }
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -65,7 +69,10 @@ __global__ __launch_bounds__(256) void stream_combine_kernel(DecodeParams p) {
     for (int u = 0; u < kPieces; ++u)
       if (u < np) xs[u] = piece_o(u);
     mx = wave_max(lse_lo);
-    for (int c0 = 64; c0 < np; c0 += 64) mx = fmaxf(mx, wave_max(piece_lse(c0 + lane)));
+    for (int c0 = 64; c0 < np; c0 += 64) {
+      const float m2 = wave_max(piece_lse(c0 + lane));
+      mx = (m2 != m2 || mx != mx) ? __builtin_nanf("") : fmaxf(mx, m2);
+    }
     if (mx != kNegInf) {
       for (int c0 = 0; c0 < np; c0 += 64) {
         const float l = c0 == 0 ? lse_lo : piece_lse(c0 + lane);
@@ -93,7 +100,8 @@ __global__ __launch_bounds__(256) void stream_combine_kernel(DecodeParams p) {
       }
     }
   }
-  const bool any = wsum > 0.f;
+  // wsum is NaN when a piece was poisoned: then out and LSE are NaN too
+  const bool any = wsum > 0.f || wsum != wsum;
   const float inv = any ? 1.f / wsum : 0.f;
   acc0 *= inv;
   acc1 *= inv;

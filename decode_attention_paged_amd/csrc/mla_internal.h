@@ -16,7 +16,9 @@ constexpr int kMaxShards = 16;
 
 // Everything the plan / attention / combine kernels need for one shard.
 struct DecodeParams {
-  const uint16_t* q;              // bf16 [B][q_len][H][576]
+  const uint16_t* q;              // bf16 query rows, dims 0..511 (and 512..575 unless q_rope)
+  const uint16_t* q_rope;         // bf16 rope dims 512..575 of every row (q + 512 when not split)
+  int64_t q_stride, q_rope_stride;   // elements between consecutive query rows
   const uint8_t* kv;              // [num_pages][64][576] bf16 or e4m3
   const int32_t* block_table;     // [B][max_pages]
   const int32_t* seq_lens;        // [B] global lengths

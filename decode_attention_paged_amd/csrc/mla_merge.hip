@@ -102,10 +102,18 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeParams p) 
   for (int u = 0; u < kV; ++u) {
     const long long vec = vec0 + u;
     if (vec >= p.vectors) break;
+    // the max propagates NaN (a poisoned shard poisons the merged row, out
+    // and LSE); -inf stays -inf (multiplier > 0)
     float mx = kNegInf;
+    bool nan = false;
 #pragma unroll
-    for (int r = 0; r < kS; ++r)
-      if (r < S) mx = fmaxf(mx, lse2[u][r]);   // -inf stays -inf (multiplier > 0)
+    for (int r = 0; r < kS; ++r) {
+      if (r < S) {
+        mx = fmaxf(mx, lse2[u][r]);
+        nan |= lse2[u][r] != lse2[u][r];
+      }
+    }
+    if (nan) mx = __builtin_nanf("");
     float w[kS];
     float wsum = 0.f;
 #pragma unroll
@@ -115,7 +123,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeParams p) 
         wsum += w[r];
       }
     }
-    const bool any = wsum > 0.f;
+    const bool any = wsum > 0.f || wsum != wsum;
     const float inv = any ? 1.f / wsum : 0.f;
 
     for (int e0 = e_first; e0 < p.dv; e0 += 512) {

@@ -617,13 +617,16 @@ void attn_ws_kernel(DecodeParams p) {
       const int row = rb * kWsRows + rg * 32 + tok;
       const bool row_ok = row < p.rows;
       {
-        const uint16_t* qrow = p.q + ((long long)b * p.rows + (row_ok ? row : 0)) * kDqk;
+        const long long qn = (long long)b * p.rows + (row_ok ? row : 0);
+        const uint16_t* qrow = p.q + qn * p.q_stride;
+        const uint16_t* rrow = p.q_rope + qn * p.q_rope_stride - 512;
 #pragma unroll
         for (int i = 0; i < kKS; ++i) {
           int d0;
           if constexpr (kFp8) d0 = 32 * (2 * (i >> 1) + ds) + 16 * hi + 8 * (i & 1);
           else d0 = 16 * (4 * (i / kG) + kG * ds + i % kG) + 8 * hi;
-          const bf16x8_t x = *(const bf16x8_t*)(qrow + d0);
+          // steps 0..15 read latent dims (< 512), steps 16, 17 rope dims
+          const bf16x8_t x = *(const bf16x8_t*)((i < 16 ? qrow : rrow) + d0);
           qreg[i] = row_ok ? x : bf16x8_t{};
         }
       }

@@ -55,8 +55,7 @@ class DeviceWorkload:
                     if getattr(wl, "q_lens", None) is not None else None))
 
     def local_max(self, shard: int) -> int:
-        M, S = self.max_seq_len, self.shards
-        return max(M // S + int(shard < M % S), 1)
+        return L.mla_shard_local_max(self.max_seq_len, shard, self.shards)
 
 
 class StepBuffers:

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 6
+#define MLA_ABI_VERSION 7
 #define MLA_PAGE_SIZE 64
 #define MLA_D_QK 576
 #define MLA_D_V 512
@@ -118,7 +118,8 @@ mla_status_t mla_build_shard_metadata(const int32_t* seq_lens, const int32_t* bl
  * ---------------------------------------------------------------------- */
 typedef struct mla_decode_args {
   /* inputs (device) */
-  const void* q;                 /* [batch][q_len][num_heads][576] bf16          */
+  const void* q;                 /* [batch][q_len][num_heads][576] bf16, or the
+                                    512 latent dims only when q_rope is given   */
   const void* kv_pages;          /* [num_pages][64][576] bf16 or fp8 e4m3        */
   const int32_t* block_table;    /* [batch][max_pages] i32, page ids             */
   const int32_t* seq_lens;       /* [batch] i32, global KV length per request    */
@@ -171,6 +172,22 @@ typedef struct mla_decode_args {
    * clamped to [0, q_len]. NULL: every request is q_len deep. The work
    * schedule does not depend on it. */
   const int32_t* q_lens;
+  /* optional split query ([DCP decode] 实现拆解 steps 3-4: the fused
+   * concat-and-write of q_nope and q_pe into one query buffer is what the
+   * DCP path turns off): when q_rope is not NULL, `q` holds the 512 latent
+   * dims of every query row and q_rope its 64 rope dims, each read in place
+   * with its own row stride, so no concatenation pass runs before the
+   * decode. Query rows are ordered (b, i, h) as in the [batch][q_len]
+   * [num_heads] layout; row n starts at element n * q_row_stride of `q` and
+   * n * q_rope_row_stride of q_rope. q_row_stride = 0 means 576 (512 with
+   * q_rope), q_rope_row_stride = 0 means 64. Strides must be multiples of 8
+   * elements and both pointers 16-byte aligned (rows are read 16 bytes at a
+   * time); e.g. two slices of one [rows][576] buffer are
+   * (q, q + 512) with strides (576, 576). The query is never quantised: it
+   * is read as bf16 for either KV dtype. */
+  const void* q_rope;            /* [rows] x 64 bf16 at q_rope_row_stride, or NULL */
+  int64_t q_row_stride;
+  int64_t q_rope_row_stride;
 } mla_decode_args_t;
 
 /* Bytes of workspace mla_decode_partial needs for these sizes (host only,
@@ -179,6 +196,9 @@ size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t q_le
 
 /* Errors: INVALID_ARGUMENT for a null q / kv_pages / block_table / seq_lens /
  * out / lse / workspace, only one of the two metadata pointers, batch < 0,
+ * a query stride that is negative, not a multiple of 8 or below the dims it
+ * holds (576, or 512 with q_rope; 64 for q_rope), a query pointer that is
+ * not 16-byte aligned,
  * num_heads not a positive multiple of 16, q_len outside [1, 4],
  * page_size != 64, bad shard ids, num_pages < 1, max_pages < 1,
  * split_target outside [0, 1024], a dtype other than those listed;

@@ -39,7 +39,7 @@ def test_struct_layouts_and_version(lib):
     assert lib.mla_sizeof_decode_args() == ctypes.sizeof(L.DecodeArgs)
     assert lib.mla_sizeof_merge_args() == ctypes.sizeof(L.MergeArgs)
     assert lib.mla_sizeof_append_args() == ctypes.sizeof(L.AppendArgs)
-    assert lib.mla_abi_version() == 6
+    assert lib.mla_abi_version() == 7
     assert lib.mla_status_string(L.STATUS_INVALID_ARGUMENT) == b"invalid argument"
 
 
@@ -91,6 +91,26 @@ def test_decode_argument_errors(lib, field, value, status):
     st = lib.mla_decode_partial(ctypes.byref(a), None, None)
     assert st == status, lib.mla_last_error()
     assert lib.mla_last_error()
+
+
+@pytest.mark.parametrize("fields", [
+    dict(q_row_stride=100),                                 # not a multiple of 8
+    dict(q_row_stride=512),                                 # below 576 without q_rope
+    dict(q_row_stride=-8),
+    dict(q=0x1008),                                         # not 16-byte aligned
+    dict(q_rope=0x2000, q_row_stride=504),                  # below 512 with q_rope
+    dict(q_rope=0x2000, q_rope_row_stride=60),              # below 64
+    dict(q_rope=0x2000, q_rope_row_stride=68),              # not a multiple of 8
+    dict(q_rope=0x2004),                                    # not 16-byte aligned
+])
+def test_split_query_argument_errors(lib, fields):
+    for fn in (lib.mla_decode_partial, lib.mla_decode_all_shards):
+        a = _valid_args()
+        a.workspace_bytes = 1 << 40
+        for k, v in fields.items():
+            setattr(a, k, v)
+        assert fn(ctypes.byref(a), None, None) == L.STATUS_INVALID_ARGUMENT, fields
+        assert "q" in lib.mla_last_error().decode()
 
 
 def test_empty_batch_is_ok_without_device(lib):

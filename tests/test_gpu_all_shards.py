@@ -219,21 +219,26 @@ def test_all_shards_short_requests_with_empty_shards():
     assert np.all(np.isfinite(ml[:7]))
 
 
-def test_all_shards_bad_page_ids_poison_instead_of_faulting():
-    """A page id outside the pool (and a negative one) reads the NaN row:
-    the request that owns it is poisoned on every shard's share, the other
-    request is untouched."""
-    wl = make_workload("bad", batch=3, heads=16, q_len=1, shards=2, kv_dtype="bf16",
-                       lens=("fixed", (100, 50, 130)), seed=9)
-    ok_o, ok_l = O.decode_full(wl, requests=[1])
+@pytest.mark.parametrize("split_target", [8, 64])
+def test_all_shards_bad_page_ids_poison_instead_of_faulting(split_target):
+    """A page id outside the pool (and a negative one) reads the NaN row: the
+    request that owns it comes out NaN in every row, out and LSE (the fused
+    merge must not take a poisoned shard for an empty one), whether its
+    shards' segments are whole or cut into pieces; the other requests match
+    the oracle."""
+    wl = make_workload("bad", batch=16, heads=16, q_len=1, shards=2, kv_dtype="bf16",
+                       lens=("fixed", (200,) * 15 + (130,)), seed=9)
+    ok = list(range(1, wl.batch - 1))
+    ok_o, ok_l = O.decode_full(wl, requests=ok)
     wl.block_table[0, 1] = 10_000          # outside the pool
-    wl.block_table[2, 2] = -5              # negative
+    wl.block_table[15, 2] = -5             # negative
     dw = ST.DeviceWorkload.upload(wl)
     bufs = ST.StepBuffers(dw)
     bufs.fill_nan()
-    _flush("all shards bad page ids")
-    ST.run_all_shards(dw, bufs)
+    _flush(f"all shards bad page ids split={split_target}")
+    ST.run_all_shards(dw, bufs, split_target=split_target)
     torch.cuda.synchronize()
-    o = bufs.out.float().cpu().numpy()
-    assert np.isnan(o[0]).any() and np.isnan(o[2]).any()
-    U.assert_partial_close(bufs.out[[1]], bufs.lse[[1]], ok_o, ok_l, "e", U.TOL["bf16"], "untouched request")
+    o, l = bufs.out.float().cpu().numpy(), bufs.lse.cpu().numpy()
+    for b in (0, 15):
+        assert np.isnan(o[b]).all() and np.isnan(l[b]).all(), f"request {b} not poisoned"
+    U.assert_partial_close(bufs.out[ok], bufs.lse[ok], ok_o, ok_l, "e", U.TOL["bf16"], "untouched requests")

@@ -6,8 +6,12 @@ scaled down so the oracle finishes in seconds while still spanning several
 sizes are checked on sampled requests in test_gpu_fullsize.py). Outputs are
 pre-filled with NaN so an unwritten row fails.
 Tolerances: out and LSE max-abs 2e-2 (bf16 KV) / 6e-2 (fp8 KV), LSE in nats;
-neutral rows exactly (+0, -inf); merge 1e-5 relative (fp32) or within one
-bf16 ulp of the rounded oracle; metadata bit-exact.
+neutral rows exactly (+0, -inf); metadata bit-exact. Merge: fp32 output
+within 1e-5 of each (row, head) vector's largest magnitude, LSE within
+1e-5 * max(1, |lse|); bf16 output within one bf16 ulp of the fp64 result plus
+that same fp32 bound (the kernel accumulates in fp32, so its error is relative
+to the vector's largest term, which can exceed a small result's ulp under
+cancellation, and then rounds once to bf16).
 """
 import math
 
@@ -249,17 +253,49 @@ def test_empty_shards_are_exactly_neutral():
     U.assert_partial_close(bufs.out, bufs.lse, ref_o, ref_l, "e", 2e-2, "merged short")
 
 
-def test_bad_page_ids_poison_instead_of_faulting():
-    wl = make_workload("bad", batch=2, heads=16, q_len=1, shards=1, kv_dtype="bf16",
-                       lens=("fixed", (100, 50)), seed=9)
-    wl.block_table[0, 1] = 10_000          # outside the pool
+def _poisoned_workload(S):
+    """16 requests of 200 tokens; request 0's second page id lies outside the
+    pool, so every shard's share of it reads the NaN row."""
+    wl = make_workload("bad", batch=16, heads=16, q_len=1, shards=S, kv_dtype="bf16",
+                       lens=("fixed", (200,) * 16), seed=9, out_dtype="bf16")
+    wl.block_table[0, 1] = 10_000
+    return wl
+
+
+@pytest.mark.parametrize("split_target", [8, 64])
+@pytest.mark.parametrize("use_metadata", [False, True])
+def test_bad_page_ids_poison_out_and_lse_per_shard_and_merged(split_target, use_metadata):
+    """A page id outside the pool reads as NaN instead of faulting, and the
+    NaN reaches both the partial out and its LSE on every shard that owns a
+    token of that page, then the merged row (a NaN LSE must not be taken for
+    an empty shard). With 8 workgroups every segment is held whole by one
+    workgroup (finalised in place); with 64 each is cut into pieces that the
+    combine merges. The other requests match the oracle."""
+    S = 2
+    wl = _poisoned_workload(S)
     dw = ST.DeviceWorkload.upload(wl)
     bufs = ST.StepBuffers(dw)
-    ST.run_partial(dw, bufs, 0, use_metadata=False)
+    bufs.fill_nan()
+    ok = list(range(1, wl.batch))
+    parts = []
+    for r in range(S):
+        _flush(f"bad page shard {r}/{S} split={split_target} meta={use_metadata}")
+        if use_metadata:
+            ST.run_metadata(dw, bufs, r)
+        ST.run_partial(dw, bufs, r, use_metadata=use_metadata, split_target=split_target)
+        torch.cuda.synchronize()
+        o, l = bufs.outs[r].float().cpu().numpy(), bufs.lses[r].cpu().numpy()
+        assert np.isnan(o[0]).all() and np.isnan(l[0]).all(), f"shard {r}: poisoned request not NaN"
+        ref_o, ref_l = O.decode_partial(wl, r, S, wl.lse_base, requests=ok)
+        parts.append((ref_o, ref_l))
+        U.assert_partial_close(bufs.outs[r][ok], bufs.lses[r][ok], ref_o, ref_l, wl.lse_base, U.TOL["bf16"],
+                               f"untouched requests shard {r}")
+    ST.run_merge(dw, bufs)
     torch.cuda.synchronize()
-    o = bufs.outs[0].cpu().numpy()
-    assert np.isnan(o[0]).any()            # request 0 reads a bad page -> NaN
-    assert not np.isnan(o[1]).any()        # request 1 unaffected
+    mo, ml = bufs.out.float().cpu().numpy(), bufs.lse.cpu().numpy()
+    assert np.isnan(mo[0]).all() and np.isnan(ml[0]).all(), "merged poisoned request not NaN"
+    ref_o, ref_l = O.merge([p_[0] for p_ in parts], [p_[1] for p_ in parts], [wl.lse_base] * S)
+    U.assert_partial_close(bufs.out[ok], bufs.lse[ok], ref_o, ref_l, "e", U.TOL["bf16"], "merged untouched")
 
 
 # --------------------------------------------------------------------------
@@ -359,6 +395,49 @@ def test_merge_single_shard_and_neutral_extra():
     assert torch.equal(out2, out) and torch.equal(lse2, lse)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_merge_propagates_nan(dtype):
+    """A shard whose LSE is NaN (it read a poisoned KV row) poisons the merged
+    vector, out and LSE, as the fp64 definition does; a NaN output with a
+    finite LSE poisons the out only; all-NaN vectors stay NaN (they are not
+    the neutral state). Vectors without NaN are unchanged."""
+    S, T, H = 4, 6, 16
+    mi = make_merge_inputs(T, shards=S, heads=H, dtype=dtype, neutral_frac=0.1, seed=91)
+    lses = mi.lses.copy()
+    outs = mi.outs.copy()
+    lses[1, 0, 3] = np.nan                 # one shard
+    lses[:, 2, 5] = np.nan                 # every shard
+    lses[0, 4, 0] = -np.inf                # a neutral shard next to a NaN one
+    lses[2, 4, 0] = np.nan
+    nan_bits = np.uint16(0x7FC0) if dtype == "bf16" else np.float32(np.nan)
+    outs[3, 5, 7, 11] = nan_bits           # NaN out, finite LSE
+    lses[3, 5, 7] = 9.0
+    if dtype == "bf16":
+        d_outs = [torch.from_numpy(outs[r]).view(torch.bfloat16).cuda() for r in range(S)]
+        ref_outs = [O.decode_bf16(outs[r]) for r in range(S)]
+        odt = torch.bfloat16
+    else:
+        d_outs = [torch.from_numpy(outs[r]).cuda() for r in range(S)]
+        ref_outs = [outs[r].astype(np.float64) for r in range(S)]
+        odt = torch.float32
+    d_lses = [torch.from_numpy(lses[r]).cuda() for r in range(S)]
+    out = torch.zeros((T, H, 512), dtype=odt, device="cuda")
+    lse = torch.zeros((T, H), dtype=torch.float32, device="cuda")
+    L.mla_merge_partials(d_outs, d_lses, [L.LSE_BASE_E] * S, out, lse)
+    torch.cuda.synchronize()
+    ro, rl = O.merge(ref_outs, [lses[r].astype(np.float64) for r in range(S)], ["e"] * S)
+    go, gl = U.to_np(out), U.to_np(lse)
+    assert np.array_equal(np.isnan(go), np.isnan(ro)), "NaN pattern of out differs from the definition"
+    assert np.array_equal(np.isnan(gl), np.isnan(rl)), "NaN pattern of lse differs from the definition"
+    assert np.isnan(go[0, 3]).all() and np.isnan(gl[0, 3]) and np.isnan(go[2, 5]).all() and np.isnan(gl[2, 5])
+    assert np.isnan(go[4, 0]).all() and np.isnan(gl[4, 0])
+    assert np.isnan(go[5, 7]).all() and np.isfinite(gl[5, 7])
+    fin = ~np.isnan(ro)
+    vec = np.abs(np.where(fin, ro, 0)).max(axis=-1, keepdims=True)
+    bound = (U.bf16_ulp(ro) if dtype == "bf16" else 0) + 1e-5 * vec
+    assert np.all(np.abs(go - ro)[fin] <= np.broadcast_to(bound, ro.shape)[fin])
+
+
 def test_many_segments_plan_in_workspace():
     """More segments (request x 64-row block) than the schedule keeps in LDS
     (6144): 6300 short requests over 2 shards, so the plan's offset tables
@@ -418,3 +497,52 @@ def test_zero_length_and_tiny_requests(kv_dtype):
         torch.cuda.synchronize()
         full_o, full_l = O.decode_full(wl)
         U.assert_partial_close(bufs.out, bufs.lse, full_o, full_l, "e", tol, "zero merged")
+
+
+# --------------------------------------------------------------------------
+# split query: q_nope and q_rope read in place
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("layout", ["slices_of_one_buffer", "separate_tensors"])
+@pytest.mark.parametrize("name", ["kimi_like", "deepseek_like_fp8", "mtp_q4"])
+def test_split_query_matches_concatenated(name, layout):
+    """The query given as its 512 latent dims and its 64 rope dims, each read
+    in place with its own row stride (no concatenation pass), gives the same
+    bytes as the concatenated [.., 576] query, per shard and in the single
+    launch of every shard, and matches the oracle."""
+    wl = _small(name)
+    dw = ST.DeviceWorkload.upload(wl)
+    B, q, H = wl.batch, wl.q_len, wl.heads
+    if layout == "slices_of_one_buffer":
+        # rows of 704 elements: [pad 64 | rope 64 | pad 32 | nope 512 | pad 32]
+        buf = torch.full((B, q, H, 704), float("nan"), dtype=torch.bfloat16, device="cuda")
+        buf[..., 64:128] = dw.q[..., 512:]
+        buf[..., 160:672] = dw.q[..., :512]
+        q_nope, q_rope = buf[..., 160:672], buf[..., 64:128]
+    else:
+        q_nope, q_rope = dw.q[..., :512].contiguous(), dw.q[..., 512:].contiguous()
+    ref = ST.StepBuffers(dw)
+    got = ST.StepBuffers(dw)
+    tol = U.TOL[wl.kv_dtype]
+    for r in range(wl.shards):
+        _flush(f"split query {name} {layout} shard {r}/{wl.shards}")
+        ST.run_metadata(dw, ref, r)
+        ST.run_metadata(dw, got, r)
+        ST.run_partial(dw, ref, r)
+        L.mla_decode_partial(q_nope, dw.kv_pages, dw.block_table, dw.seq_lens, r, wl.shards, q,
+                             got.outs[r], got.lses[r], got.workspace, kv_scale=dw.kv_scale,
+                             softmax_scale=dw.softmax_scale, lse_base=dw.lse_base,
+                             local_seq_lens=got.local_seq_lens[r], local_kv_indices=got.local_kv_indices[r],
+                             q_rope=q_rope)
+        torch.cuda.synchronize()
+        assert torch.equal(got.outs[r].view(torch.int16 if got.outs[r].dtype == torch.bfloat16 else torch.int32),
+                           ref.outs[r].view(torch.int16 if ref.outs[r].dtype == torch.bfloat16 else torch.int32))
+        assert torch.equal(got.lses[r].view(torch.int32), ref.lses[r].view(torch.int32))
+        ref_o, ref_l = O.decode_partial(wl, r, wl.shards, wl.lse_base)
+        U.assert_partial_close(got.outs[r], got.lses[r], ref_o, ref_l, wl.lse_base, tol, f"split q shard {r}")
+    ws = ST.all_shards_workspace(dw, got)
+    got.fill_nan()
+    L.mla_decode_all_shards(q_nope, dw.kv_pages, dw.block_table, dw.seq_lens, wl.shards, q, got.out, got.lse, ws,
+                            kv_scale=dw.kv_scale, softmax_scale=dw.softmax_scale, q_rope=q_rope)
+    torch.cuda.synchronize()
+    full_o, full_l = O.decode_full(wl)
+    U.assert_partial_close(got.out, got.lse, full_o, full_l, "e", tol, f"split q all shards {name}")

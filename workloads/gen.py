@@ -284,6 +284,49 @@ def make_config(index: int, seed: Optional[int] = None, **overrides) -> Workload
     return make_workload(spec.pop("name"), seed=1000 + index if seed is None else seed, **spec)
 
 
+def _decode_bf16_bits(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns to float32 (exact widening), for building inputs."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def plant_rising_keys(wl: Workload, tiles=(2, 5), magnitudes=(1.5, 2.5), group: int = 16) -> Workload:
+    """Overwrite the latent rows of chosen token ranges with keys aligned to
+    the request's queries, so that the scores of later tiles rise far above
+    those of the first tile (inputs that make an online softmax move its
+    running maximum several times per row).
+
+    For each request and each entry k of ``tiles``, every token of the
+    global range [32 S tiles[k], 32 S (tiles[k] + 1)) (owned-token tile
+    ``tiles[k]`` of every one of the S shards) gets the row
+    ``magnitudes[k] * sign(sum of the query rows of one group)``, all 576
+    dims. The query rows (draft row i, head h; row = i H + h) are dealt to
+    groups of ``group`` consecutive rows, and a planted token t goes to group
+    (t // S) mod (number of groups), its index within the shard that owns
+    it, so that every shard's planted tile holds keys of every group. Values
+    are encoded like the rest of the pool (bf16 RNE, or e4m3 with the pool's
+    scale). Only tokens below the request's length are
+    touched. Returns ``wl`` (modified in place).
+    """
+    S, H, q = wl.shards, wl.heads, wl.q_len
+    rows = q * H
+    ngroups = (rows + group - 1) // group
+    for b in range(wl.batch):
+        L = int(wl.seq_lens[b])
+        qf = _decode_bf16_bits(wl.q[b]).reshape(rows, D_QK).astype(np.float64)
+        gsign = np.stack([np.sign(qf[g * group:(g + 1) * group].sum(axis=0)) for g in range(ngroups)])
+        gsign[gsign == 0] = 1.0
+        for tile, mag in zip(tiles, magnitudes):
+            t0, t1 = 32 * S * tile, min(32 * S * (tile + 1), L)
+            for t in range(t0, t1):
+                row = (mag * gsign[(t // S) % ngroups]).astype(np.float32)
+                page = int(wl.block_table[b, t // PAGE_SIZE])
+                if wl.kv_dtype == "bf16":
+                    wl.kv_pages[page, t % PAGE_SIZE] = f32_to_bf16_bits(row)
+                else:
+                    wl.kv_pages[page, t % PAGE_SIZE] = f32_to_e4m3_bits(row / np.float32(wl.kv_scale))
+    return wl
+
+
 @dataclasses.dataclass
 class MergeInputs:
     outs: np.ndarray      # [S, N, H, Dv] uint16 (bf16) or float32
