@@ -101,7 +101,8 @@ class AppendArgs(ctypes.Structure):
     ]
 
 
-EXPORTS = ("mla_build_shard_metadata", "mla_decode_workspace_bytes", "mla_decode_partial", "mla_decode_plan",
+EXPORTS = ("mla_build_shard_metadata", "mla_decode_workspace_bytes", "mla_decode_partial",
+           "mla_decode_partial_noalloc", "mla_decode_plan",
            "mla_decode_all_shards", "mla_decode_all_shards_workspace_bytes", "mla_merge_partials", "mla_append_kv", "mla_status_string", "mla_last_error", "mla_abi_version",
            "mla_sizeof_decode_args", "mla_sizeof_merge_args", "mla_sizeof_append_args")
 
@@ -127,6 +128,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_decode_workspace_bytes.restype = sz
     lib.mla_decode_partial.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_int), vp]
     lib.mla_decode_partial.restype = ctypes.c_int
+    lib.mla_decode_partial_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_int), vp]
+    lib.mla_decode_partial_noalloc.restype = ctypes.c_int
     lib.mla_decode_plan.argtypes = [ctypes.POINTER(DecodeArgs), vp]
     lib.mla_decode_plan.restype = ctypes.c_int
     lib.mla_decode_all_shards.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_int), vp]
@@ -262,7 +265,8 @@ def _decode_args(q, kv_pages, block_table, seq_lens, shard_id, num_shards, q_len
     a.kv_scale, a.softmax_scale = float(kv_scale), float(softmax_scale)
     a.lse_base = int(lse_base)
     a.out, a.out_dtype, a.lse = _ptr(out), _dtype_code(out), _ptr(lse)
-    a.workspace, a.workspace_bytes = _ptr(workspace), int(workspace.numel() * workspace.element_size())
+    if workspace is not None:
+        a.workspace, a.workspace_bytes = _ptr(workspace), int(workspace.numel() * workspace.element_size())
     a.split_target = int(split_target)
     if events is not None:
         a.event_begin, a.event_end = int(events[0].cuda_event), int(events[1].cuda_event)
@@ -295,6 +299,22 @@ def mla_decode_partial(q, kv_pages, block_table, seq_lens, shard_id: int, num_sh
                      reuse_plan, q_lens, q_rope)
     written = ctypes.c_int(-1)
     _check(lib.mla_decode_partial(ctypes.byref(a), ctypes.byref(written), _stream_ptr(stream)))
+    return int(written.value)
+
+
+def mla_decode_partial_noalloc(q, kv_pages, block_table, seq_lens, shard_id: int, num_shards: int, q_len: int,
+                               out, lse, *, kv_scale: float = 1.0, softmax_scale: float,
+                               lse_base: int = LSE_BASE_E, local_seq_lens=None, local_kv_indices=None,
+                               split_target: int = 0, events=None, q_lens=None, q_rope=None, stream=None) -> int:
+    """mla_decode_partial without a workspace: the library's own device
+    scratch holds the schedule and partials (calls on one device must not
+    overlap). Returns the LSE base written."""
+    lib = load()
+    a = _decode_args(q, kv_pages, block_table, seq_lens, shard_id, num_shards, q_len, out, lse, None,
+                     kv_scale, softmax_scale, lse_base, local_seq_lens, local_kv_indices, split_target, events,
+                     False, q_lens, q_rope)
+    written = ctypes.c_int(-1)
+    _check(lib.mla_decode_partial_noalloc(ctypes.byref(a), ctypes.byref(written), _stream_ptr(stream)))
     return int(written.value)
 
 

@@ -57,16 +57,42 @@ int device_cus(int* out) {
   return 0;
 }
 
+// Scratch of the allocation-free decode (mla_decode_partial_noalloc): the
+// work schedule and the piece partials live in this file-scope device array
+// instead of a caller's workspace. Each device the library runs on holds its
+// own copy until the process ends; host code reaches it only through the
+// address hipGetSymbolAddress returns for the current device (the array's
+// name is a host-side stand-in, not a device address).
+constexpr size_t kScratchBytes = size_t(80) << 20;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (that device current) and cached; nullptr if the lookup fails.
+void* scratch_address() {
+  static std::mutex mu;
+  static std::vector<void*> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, nullptr);
+  if (cache[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    cache[dev] = ptr;
+  }
+  return cache[dev];
+}
+
 }  // namespace
 
 namespace mla {
 
-WorkspaceLayout decode_workspace_layout(int32_t batch, int32_t rows) {
+WorkspaceLayout decode_workspace_layout(int32_t batch, int32_t rows, int32_t max_slots) {
   WorkspaceLayout w{};
   const int32_t rows_blk = stream_rows_per_block(rows);
   const int64_t nseg = (int64_t)batch * ((rows + rows_blk - 1) / rows_blk);
   // a segment is cut into pieces only at workgroup boundaries
-  w.max_slots = (int32_t)(nseg + kMaxGrid);
+  w.max_slots = max_slots >= 0 ? max_slots : (int32_t)(nseg + kMaxGrid);
   size_t off = 0;
   w.plan = off;      off = align_up(off + 64, 256);
   w.req_cnt = off;   off = align_up(off + sizeof(int32_t) * (size_t)batch, 256);
@@ -190,7 +216,7 @@ size_t mla_decode_all_shards_workspace_bytes(int32_t batch, int32_t num_heads, i
 // false when there is nothing to run (batch 0). `all_shards`: one launch for
 // every shard (shard_id ignored, no shard metadata, merged output).
 static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams& p, bool& launch,
-                                   bool all_shards = false) {
+                                   bool all_shards = false, bool noalloc = false) {
   launch = false;
   if (a == nullptr) return fail(MLA_STATUS_INVALID_ARGUMENT, "args is NULL");
   if (a->batch < 0) return fail(MLA_STATUS_INVALID_ARGUMENT, "batch must be >= 0 (got %d)", a->batch);
@@ -228,8 +254,10 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
     return fail(MLA_STATUS_INVALID_ARGUMENT, "reuse_plan must be 0 or 1 (got %d)", a->reuse_plan);
   if (a->split_target < 0 || a->split_target > mla::kMaxGrid)
     return fail(MLA_STATUS_INVALID_ARGUMENT, "split_target must be in [0, %d] (got %d)", mla::kMaxGrid, a->split_target);
+  if (noalloc && a->reuse_plan != 0)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "the allocation-free decode rebuilds its schedule in every call: reuse_plan must be 0");
   if (a->batch > 0) {
-    if (!a->q || !a->kv_pages || !a->block_table || !a->seq_lens || !a->out || !a->lse || !a->workspace)
+    if (!a->q || !a->kv_pages || !a->block_table || !a->seq_lens || !a->out || !a->lse || (!a->workspace && !noalloc))
       return fail(MLA_STATUS_INVALID_ARGUMENT, "q, kv_pages, block_table, seq_lens, out, lse and workspace are required");
   }
   {
@@ -249,13 +277,39 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
   const int32_t fold = all_shards ? a->num_shards : 1;
   if ((int64_t)a->batch * fold > 0x7FFFFFFFLL)
     return fail(MLA_STATUS_INVALID_ARGUMENT, "batch %d x %d shards is too large", a->batch, fold);
-  const mla::WorkspaceLayout w = mla::decode_workspace_layout(a->batch * fold, rows);
-  if (a->batch > 0 && a->workspace_bytes < w.total)
+  mla::WorkspaceLayout w = mla::decode_workspace_layout(a->batch * fold, rows);
+  if (!noalloc && a->batch > 0 && a->workspace_bytes < w.total)
     return fail(MLA_STATUS_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", w.total, a->workspace_bytes);
   if (a->batch == 0) return ok();
 
   int cus = 0;
   if (device_cus(&cus) != 0) return fail(MLA_STATUS_DEVICE_ERROR, "cannot query the current device");
+  int32_t grid;
+  {
+    // one persistent workgroup per CU but one in 16 (a multiple of 8 so that
+    // the workgroup order can follow the XCDs) unless the caller fixes the
+    // count: the free CUs run the small kernels of concurrent shards (their
+    // combine) alongside, which shortens a step of concurrent partials
+    // (the single launch of every shard with fp8 KV, compute-bound, takes
+    // every CU: 325 -> 303 µs on the deepseek-like fp8 step, where bf16
+    // shapes gain nothing or lose)
+    const bool all_cus = all_shards && a->num_shards > 1 && a->kv_dtype == MLA_DTYPE_FP8_E4M3;
+    grid = a->split_target > 0 ? a->split_target : all_cus ? (cus / 8) * 8 : ((cus - cus / 16) / 8) * 8;
+    if (grid < 8) grid = 8;
+    if (grid > mla::kMaxGrid) grid = mla::kMaxGrid;
+  }
+  uint8_t* ws = (uint8_t*)a->workspace;
+  if (noalloc) {
+    // only segments cut at a workgroup boundary take partial slots, one per
+    // piece: at most two per boundary, so 2 x grid slots always suffice
+    w = mla::decode_workspace_layout(a->batch, rows, 2 * grid);
+    if (w.total > kScratchBytes)
+      return fail(MLA_STATUS_WORKSPACE_TOO_SMALL,
+                  "batch %d x %d rows with %d workgroups needs %zu bytes of scratch; the allocation-free decode "
+                  "holds %zu", a->batch, rows, grid, w.total, kScratchBytes);
+    ws = (uint8_t*)scratch_address();
+    if (ws == nullptr) return fail(MLA_STATUS_DEVICE_ERROR, "cannot resolve the scratch address on the current device");
+  }
   p = mla::DecodeParams{};
   p.q = (const uint16_t*)a->q;
   if (a->q_rope != nullptr) {
@@ -290,7 +344,6 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
   p.out_bf16 = a->out_dtype == MLA_DTYPE_BF16;
   p.out = a->out;
   p.lse = a->lse;
-  uint8_t* ws = (uint8_t*)a->workspace;
   p.plan = (int32_t*)(ws + w.plan);
   p.req_cnt = (int32_t*)(ws + w.req_cnt);
   p.seg_off = (int32_t*)(ws + w.seg_off);
@@ -304,20 +357,7 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
   p.rows_blk = mla::stream_rows_per_block(rows);
   p.row_blocks = (rows + p.rows_blk - 1) / p.rows_blk;
   p.kv_fp8 = a->kv_dtype == MLA_DTYPE_FP8_E4M3;
-  {
-    // one persistent workgroup per CU but one in 16 (a multiple of 8 so that
-    // the workgroup order can follow the XCDs) unless the caller fixes the
-    // count: the free CUs run the small kernels of concurrent shards (their
-    // combine) alongside, which shortens a step of concurrent partials
-    // (the single launch of every shard with fp8 KV, compute-bound, takes
-    // every CU: 325 -> 303 µs on the deepseek-like fp8 step, where bf16
-    // shapes gain nothing or lose)
-    const bool all_cus = all_shards && a->num_shards > 1 && a->kv_dtype == MLA_DTYPE_FP8_E4M3;
-    int32_t grid = a->split_target > 0 ? a->split_target : all_cus ? (cus / 8) * 8 : ((cus - cus / 16) / 8) * 8;
-    if (grid < 8) grid = 8;
-    if (grid > mla::kMaxGrid) grid = mla::kMaxGrid;
-    p.grid = grid;
-  }
+  p.grid = grid;
   launch = true;
   return ok();
 }
@@ -346,6 +386,20 @@ mla_status_t mla_decode_all_shards(const mla_decode_args_t* a, mla_lse_base_t* l
   if (!launch) return ok();
   hipError_t err = mla::launch_decode_stream(p, a->reuse_plan == 0, (hipEvent_t)a->event_begin,
                                              (hipEvent_t)a->event_end, (hipStream_t)stream);
+  if (err != hipSuccess) return device_fail(err, "decode launch");
+  return ok();
+}
+
+mla_status_t mla_decode_partial_noalloc(const mla_decode_args_t* a, mla_lse_base_t* lse_base_written,
+                                        void* stream) {
+  mla::DecodeParams p;
+  bool launch = false;
+  const mla_status_t st = prepare_decode(a, p, launch, false, true);
+  if (st != MLA_STATUS_OK) return st;
+  if (lse_base_written) *lse_base_written = a->lse_base;
+  if (!launch) return ok();
+  hipError_t err = mla::launch_decode_stream(p, true, (hipEvent_t)a->event_begin, (hipEvent_t)a->event_end,
+                                             (hipStream_t)stream);
   if (err != hipSuccess) return device_fail(err, "decode launch");
   return ok();
 }

@@ -78,7 +78,8 @@ struct WorkspaceLayout {
   size_t plan, req_cnt, seg_off, seg_coff, seg_info, wg_start, wg_ustart, wg_rec, spart_lse, spart_o, total;
   int32_t max_slots;
 };
-WorkspaceLayout decode_workspace_layout(int32_t batch, int32_t rows);
+// max_slots < 0: the bound every schedule fits (segments + the largest grid)
+WorkspaceLayout decode_workspace_layout(int32_t batch, int32_t rows, int32_t max_slots = -1);
 
 struct MergeParams {
   const void* outs[kMaxShards];

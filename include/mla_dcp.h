@@ -208,6 +208,28 @@ size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t q_le
 mla_status_t mla_decode_partial(const mla_decode_args_t* args, mla_lse_base_t* lse_base_written,
                                 void* stream);
 
+/* Allocation-free variant of mla_decode_partial, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same decode and results, with the
+ * work schedule and the piece partials in a scratch array the library holds
+ * in device memory (80 MiB, one copy per device the library runs on, kept
+ * until the process ends) instead of args->workspace, which is ignored (may
+ * be NULL). The call allocates nothing and calls no allocating routine.
+ * Limits: the schedule is rebuilt by every call (reuse_plan must be 0), and
+ * the scratch holds the schedule of `batch` requests of num_heads * q_len
+ * rows plus 2 x (workgroups) partial slots of (64 or 128 rows) x 512 bf16:
+ * with the default workgroup count (split_target 0) that covers every
+ * num_heads <= 128, q_len <= 4 and batch up to tens of thousands; larger
+ * sizes or split_target return WORKSPACE_TOO_SMALL with the bytes needed.
+ * Every call on a device shares that device's scratch: calls that overlap
+ * in time on one device (different streams, or graph replays in flight
+ * together) race and must be serialised by the caller. No part of the
+ * scratch needs to start at zero; every call writes what it later reads.
+ * Other arguments and errors as mla_decode_partial; DEVICE_ERROR if the
+ * scratch's device address cannot be resolved. */
+mla_status_t mla_decode_partial_noalloc(const mla_decode_args_t* args, mla_lse_base_t* lse_base_written,
+                                        void* stream);
+
 /* Builds the work schedule of a partial decode into args->workspace without
  * running the decode (same arguments and errors as mla_decode_partial; the
  * inputs are not read beyond seq_lens / local_seq_lens and the output
