@@ -12,10 +12,13 @@ two copies of the KV pool and queries are alternated so the 256 MB
 Infinity Cache cannot serve repeated reads.
 
 Default: the Kimi-K2.5-like workload (batch 64, 64 heads, q_len 1, 4 shards,
-bf16 KV, lengths uniform in [4096, 8192]) plus the merge-only sweep
-(4 partials of T x 64 heads x 512 bf16 + fp32 LSE, T in 1..128).
-Prints ONE JSON line on stdout. ``--all`` also measures the other four
-workloads and writes them to ``--details`` (JSON).
+bf16 KV, lengths uniform in [4096, 8192]) is the headline (`value`,
+`roofline`); the other four workloads (tiny; DeepSeek-like fp8, 8 shards;
+MTP q_len 4; skewed lengths, 8 shards, base-2 LSE) are measured the same way
+and reported per workload under `configs`; plus the merge-only sweep (4
+partials of T x 64 heads x 512 bf16 + fp32 LSE, T in 1..128). Prints ONE JSON
+line on stdout. ``--configs`` narrows the per-workload list (e.g. for a
+profiler run of one workload).
 
 Reported:
   value         KV-GB/s of the step = bytes of every visible token's latent
@@ -362,6 +365,7 @@ def bench_all_shards(wl, dws, bufs, steps: int, warmup: int, kv_bytes: int, flop
                 attn_kernel_us=1e3 * attn_ms, call_bytes=call_bytes,
                 attn_kernel_gbs=call_bytes / (attn_ms * 1e-3) / 1e9,
                 attn_kernel_hbm_frac=call_bytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                attn_kernel_mfma_frac=flops / (attn_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                 max_abs_diff_vs_separate=dict(out=d_out, lse=d_lse))
 
 
@@ -474,32 +478,89 @@ def bench_append(calls: int = 16, replays: int = 10):
 # --------------------------------------------------------------------------
 # CPU oracle baseline
 # --------------------------------------------------------------------------
-def cpu_baseline(wl, seconds: float):
-    import numpy as np
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(wl, seconds: float, repeats: int = 3):
+    """The fp64 oracle on the first requests of the workload (all shard
+    partials + merge), on as many requests as fit in about seconds / repeats,
+    timed `repeats` times; the median rate."""
+    import numpy as np  # noqa: F401
 
     from oracle import mla_oracle as O
     try:
         import threadpoolctl
         info = threadpoolctl.threadpool_info()
         threads = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = ",".join(sorted({str(i.get("internal_api")) for i in info})) or "unknown"
     except Exception:  # pragma: no cover
-        threads = 1
+        threads, blas = 1, "unknown"
     row_bytes = 576 * (1 if wl.kv_dtype == "fp8" else 2)
-    order = list(range(wl.batch))
-    done, nbytes = [], 0
-    t0 = time.perf_counter()
-    for b in order:
+    # size the sample with a first pass, then time it `repeats` times
+    budget = seconds / repeats
+    sample, t0 = [], time.perf_counter()
+    for b in range(wl.batch):
         O.decode_step(wl, [b])
-        done.append(b)
-        nbytes += int(wl.seq_lens[b]) * row_bytes
-        if time.perf_counter() - t0 >= seconds:
+        sample.append(b)
+        if time.perf_counter() - t0 >= budget:
             break
-    el = time.perf_counter() - t0
-    return dict(value=nbytes / el / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
-                sample=f"{len(done)} of {wl.batch} requests ({sum(int(wl.seq_lens[b]) for b in done)} tokens) "
-                       f"of the {wl.name} workload: all {wl.shards} shard partials + merge, fp64 NumPy, "
-                       f"{el:.1f} s",
-                seconds=el)
+    nbytes = sum(int(wl.seq_lens[b]) for b in sample) * row_bytes
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        O.decode_step(wl, sample)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    return dict(value=nbytes / med / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
+                cpu_model=cpu_model(), blas=blas, os_cpu_count=os.cpu_count(),
+                sample=f"first {len(sample)} of {wl.batch} requests "
+                       f"({sum(int(wl.seq_lens[b]) for b in sample)} tokens) of the {wl.name} workload: "
+                       f"all {wl.shards} shard partials + merge, fp64 NumPy, median of {repeats} runs "
+                       f"({', '.join(f'{t:.2f}' for t in times)} s)",
+                seconds=med)
+
+
+def binding_roof(r):
+    """The attention kernel against the roof that binds it: HBM bytes or bf16
+    MFMA flops (both KV types run bf16 MFMAs), whichever fraction is larger."""
+    if r["attn_kernel_mfma_frac"] > r["attn_kernel_hbm_frac"]:
+        return dict(bound="mfma", achieved=round(r["attn_kernel_tflops"], 2), peak=BF16_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=round(r["attn_kernel_mfma_frac"], 4))
+    return dict(bound="hbm", achieved=round(r["attn_kernel_gbs"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(r["attn_kernel_hbm_frac"], 4))
+
+
+def config_summary(r):
+    """One workload's figures for the JSON line (`traffic`: HBM bytes per
+    attention launch from the committed counter summary of that workload,
+    null unless it was taken on the current kernel sources)."""
+    roof = binding_roof(r)
+    roof["traffic"] = traffic_from_profile(r["name"])
+    roof["algorithmic_bytes_per_launch"] = int(r["attn_kernel_bytes_per_launch"])
+    out = dict(
+        workload=f"batch {r['batch']}, {r['heads']} heads, q_len {r['q_len']}, {r['shards']} shards, "
+                 f"{r['kv_dtype']} KV, {r['tokens']} tokens",
+        ms_per_step=round(r["ms_per_step"], 5), kv_gbs=round(r["kv_gbs"], 1), tflops=round(r["tflops"], 2),
+        attn_kernel_us_per_shard=round(r["attn_kernel_mean_us"], 2),
+        attn_kernel=roof,
+        merge_step=dict(us=round(r["merge_us"], 2), gbs=round(r["merge_gbs"], 1),
+                        frac=round(r["merge_hbm_frac"], 4)),
+        step_timing=r["step_timing"])
+    if "all_shards" in r:
+        a = r["all_shards"]
+        out["all_shards_step"] = dict(ms_per_step=round(a["ms_per_step"], 5), kv_gbs=round(a["kv_gbs"], 1),
+                                      attn_kernel_us=round(a["attn_kernel_us"], 2),
+                                      attn_kernel_hbm_frac=round(a["attn_kernel_hbm_frac"], 4),
+                                      attn_kernel_mfma_frac=round(a.get("attn_kernel_mfma_frac", 0.0), 4))
+    return out
 
 
 def main() -> int:
@@ -508,12 +569,13 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload index 1..5 for the headline line")
-    ap.add_argument("--all", action="store_true", help="also measure every workload")
+    ap.add_argument("--configs", default="1,2,3,4,5",
+                    help="comma list of workloads measured under `configs` (the headline one always runs)")
     ap.add_argument("--details", default=None, help="write per-workload results (JSON) here")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-merge-sweep", action="store_true", help="skip the merge-only sweep and the append timing")
     ap.add_argument("--no-graph", action="store_true", help="time the step as eager launches")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--split-target", type=int, default=0,
                     help="KV chunks per launch per row block (0 = library default)")
     ap.add_argument("--sweep-split", default=None,
@@ -560,23 +622,24 @@ def main() -> int:
     append = None if args.no_merge_sweep else bench_append()
     if append:
         details["append_us_per_shard_call"] = append
-    if args.all:
-        for idx in (1, 2, 3, 4, 5):
-            if idx == args.config:
-                continue
-            _, r = bench_workload(idx, max(3, args.steps // 2), max(1, args.warmup // 2),
-                                  use_graph=not args.no_graph)
+    per_config = {}
+    for idx in [int(x) for x in args.configs.split(",") if x.strip()]:
+        if idx == args.config:
+            r = res
+        else:
+            _, r = bench_workload(idx, args.steps, args.warmup, use_graph=not args.no_graph)
             details[f"config{idx}"] = r
-            log(f"[bench] config {idx} {r['name']}: {r['ms_per_step']:.3f} ms/step, "
-                f"{r['kv_gbs']:.0f} KV-GB/s, {r['tflops']:.1f} TFLOP/s, attn kernel "
-                f"{r['attn_kernel_gbs']:.0f} GB/s ({100 * r['attn_kernel_hbm_frac']:.1f}% HBM, "
-                f"{100 * r['attn_kernel_mfma_frac']:.1f}% MFMA), merge {r['merge_us']:.1f} us "
-                f"({r['merge_gbs']:.0f} GB/s, {100 * r['merge_hbm_frac']:.1f}% HBM)")
-            if "all_shards" in r:
-                a = r["all_shards"]
-                log(f"[bench] config {idx} {r['name']} single launch: {a['ms_per_step']:.3f} ms/step, "
-                    f"{a['kv_gbs']:.0f} KV-GB/s, attn kernel {a['attn_kernel_us']:.1f} us "
-                    f"({100 * a['attn_kernel_hbm_frac']:.1f}% HBM)")
+        per_config[r["name"]] = config_summary(r)
+        log(f"[bench] config {idx} {r['name']}: {r['ms_per_step']:.3f} ms/step, "
+            f"{r['kv_gbs']:.0f} KV-GB/s, {r['tflops']:.1f} TFLOP/s, attn kernel "
+            f"{r['attn_kernel_gbs']:.0f} GB/s ({100 * r['attn_kernel_hbm_frac']:.1f}% HBM, "
+            f"{100 * r['attn_kernel_mfma_frac']:.1f}% MFMA), merge {r['merge_us']:.1f} us "
+            f"({r['merge_gbs']:.0f} GB/s, {100 * r['merge_hbm_frac']:.1f}% HBM)")
+        if "all_shards" in r:
+            a = r["all_shards"]
+            log(f"[bench] config {idx} {r['name']} single launch: {a['ms_per_step']:.3f} ms/step, "
+                f"{a['kv_gbs']:.0f} KV-GB/s, attn kernel {a['attn_kernel_us']:.1f} us "
+                f"({100 * a['attn_kernel_hbm_frac']:.1f}% HBM)")
 
     cpu = None if args.no_cpu else cpu_baseline(wl, args.cpu_seconds)
     mfma_bound = res["attn_kernel_mfma_frac"] > res["attn_kernel_hbm_frac"]
@@ -631,6 +694,7 @@ def main() -> int:
                                         "graph replay; schedule built once per step")
                             if "all_shards" in res else None),
         "roofline": roof,
+        "configs": per_config,
         "cpu_baseline": cpu,
     }
     if args.details:
