@@ -285,6 +285,12 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
   int cus = 0;
   if (device_cus(&cus) != 0) return fail(MLA_STATUS_DEVICE_ERROR, "cannot query the current device");
   int32_t grid;
+  const int32_t rows_blk = mla::stream_rows_per_block(rows);
+  const int32_t row_blocks = (rows + rows_blk - 1) / rows_blk;
+  // a request of several row blocks runs them on a group of that many
+  // neighbouring workgroups walking the same tiles, so that each tile is
+  // fetched from HBM once for all its row blocks
+  const int32_t rgroup = row_blocks;
   {
     // one persistent workgroup per CU but one in 16 (a multiple of 8 so that
     // the workgroup order can follow the XCDs) unless the caller fixes the
@@ -292,11 +298,23 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
     // combine) alongside, which shortens a step of concurrent partials
     // (the single launch of every shard with fp8 KV, compute-bound, takes
     // every CU: 325 -> 303 µs on the deepseek-like fp8 step, where bf16
-    // shapes gain nothing or lose)
+    // shapes gain nothing or lose). With row-block groups every XCD holds
+    // whole groups: per XCD a multiple of the group size, all its CUs when
+    // leaving one in 16 free would cost a whole group of 8.
     const bool all_cus = all_shards && a->num_shards > 1 && a->kv_dtype == MLA_DTYPE_FP8_E4M3;
-    grid = a->split_target > 0 ? a->split_target : all_cus ? (cus / 8) * 8 : ((cus - cus / 16) / 8) * 8;
+    if (a->split_target > 0) {
+      grid = a->split_target;
+    } else {
+      const int32_t per_xcd = cus / 8;
+      int32_t slots = all_cus ? per_xcd : per_xcd - per_xcd / 16;
+      slots = (slots / rgroup) * rgroup;
+      if (slots * 4 < per_xcd * 3) slots = (per_xcd / rgroup) * rgroup;
+      grid = 8 * slots;
+    }
     if (grid < 8) grid = 8;
     if (grid > mla::kMaxGrid) grid = mla::kMaxGrid;
+    grid = (grid / rgroup) * rgroup;
+    if (grid < rgroup) grid = rgroup;
   }
   uint8_t* ws = (uint8_t*)a->workspace;
   if (noalloc) {
@@ -354,8 +372,9 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
   p.wg_rec = (int32_t*)(ws + w.wg_rec);
   p.spart_lse = (float*)(ws + w.spart_lse);
   p.spart_o = (uint16_t*)(ws + w.spart_o);
-  p.rows_blk = mla::stream_rows_per_block(rows);
-  p.row_blocks = (rows + p.rows_blk - 1) / p.rows_blk;
+  p.rows_blk = rows_blk;
+  p.row_blocks = row_blocks;
+  p.rgroup = rgroup;
   p.kv_fp8 = a->kv_dtype == MLA_DTYPE_FP8_E4M3;
   p.grid = grid;
   launch = true;

@@ -62,6 +62,9 @@ struct DecodeParams {
   int32_t rows_blk;               // query rows per workgroup (64)
   int32_t kv_fp8;                 // KV pages hold e4m3 (else bf16)
   int32_t grid;                   // persistent workgroups
+  // workgroups per row-block group: a request's row_blocks row blocks run on
+  // that many neighbouring workgroups over the same tiles (1: plain schedule)
+  int32_t rgroup;
 };
 
 constexpr int kMaxGrid = 1024;  // persistent workgroups of the streaming kernel

@@ -103,29 +103,56 @@ __device__ __forceinline__ int seg_tiles(const DecodeParams& p, int s) {
 // One workgroup of 1024 threads; thread i handles a contiguous block of
 // segments. The segment offsets stay in LDS when they fit (the binary
 // searches then cost LDS latency only), else in the workspace.
+//
+// Row-block groups (p.rgroup = R > 1, a request with R row blocks): the
+// schedule is made over super-segments (request, shard), whose units are
+// their tiles, and over groups of R consecutive workgroups; workgroup
+// g = R gamma + j of group gamma takes row block j of the units its group
+// holds. The R workgroups of a group walk the same tiles of the same request
+// at the same time on one XCD (groups never straddle XCDs when the grid
+// divides into 8 x R), so each tile comes from HBM once for all row blocks
+// instead of once per row block. R = 1 is the plain schedule, where a
+// super-segment is a segment.
 constexpr int kPlanLdsSegs = 6144;
+
+// segment of super-segment `sup` for row block j
+__device__ __forceinline__ int seg_of_sup(const DecodeParams& p, int sup, int j) {
+  if (p.rgroup == 1) return sup;
+  const int b = sup / p.fold, ri = sup - b * p.fold;
+  return (b * p.row_blocks + j) * p.fold + ri;
+}
+// owned-token count of super-segment `sup`
+__device__ __forceinline__ int sup_count(const DecodeParams& p, int sup) {
+  if (p.rgroup == 1) return seg_count(p, sup);
+  const int b = sup / p.fold, ri = sup - b * p.fold;
+  return owned_count(p, b, p.fold > 1 ? ri : p.shard);
+}
 
 __global__ __launch_bounds__(1024) void stream_plan_kernel(DecodeParams p) {
   __shared__ int32_t s_arr[2 * (kPlanLdsSegs + 1)];
-  __shared__ int32_t s_cnt[kPlanLdsSegs];           // owned tokens per segment's request
-  __shared__ int32_t s_wgu[kMaxGrid + 1];
+  __shared__ int32_t s_cnt[kPlanLdsSegs];           // owned tokens of each super-segment
+  __shared__ int32_t s_wgu[kMaxGrid + 1];           // first unit of each group
   __shared__ int2 s_wave[16];
   const int tid = threadIdx.x;
-  const int RB = p.row_blocks;
+  const int RB = p.row_blocks, GR = p.rgroup;
   const int nseg = p.batch * RB * p.fold;
-  const bool in_lds = nseg <= kPlanLdsSegs;
-  int32_t* const off = in_lds ? s_arr : p.seg_off;              // unit offset of each segment
+  const int nsup = GR == 1 ? nseg : p.batch * p.fold;
+  const bool in_lds = nsup <= kPlanLdsSegs;
+  int32_t* const off = in_lds ? s_arr : p.seg_off;              // unit offset of each super-segment
   int32_t* const coff = in_lds ? s_arr + kPlanLdsSegs + 1 : p.seg_coff;   // cost offset
-  const int per = (nseg + 1023) / 1024;
-  const int s0 = min(tid * per, nseg), s1 = min(s0 + per, nseg);
+  const int per = (nsup + 1023) / 1024;
+  const int s0 = min(tid * per, nsup), s1 = min(s0 + per, nsup);
 
-  // tiles and costs (a segment costs its tiles plus kPieceCost for loading
-  // its queries) of this thread's segments, scanned over the block
+  // owned-token counts per request and shard
+  for (int q = tid; q < p.batch * p.fold; q += 1024) {
+    const int b = q / p.fold, ri = q - b * p.fold;
+    p.req_cnt[q] = owned_count(p, b, p.fold > 1 ? ri : p.shard);
+  }
+  // tiles and costs (a super-segment costs its tiles plus kPieceCost for
+  // loading its queries) of this thread's super-segments, scanned over the block
   int su = 0, sc = 0;
   for (int s = s0; s < s1; ++s) {
-    const SegId id = seg_id(p, s);
-    const int cnt = owned_count(p, id.b, id.r);
-    if (id.rb == 0) p.req_cnt[id.b * p.fold + id.ri] = cnt;
+    const int cnt = sup_count(p, s);
     if (in_lds) s_cnt[s] = cnt;
     const int n = (cnt + kTile - 1) / kTile;
     su += n;
@@ -136,7 +163,7 @@ __global__ __launch_bounds__(1024) void stream_plan_kernel(DecodeParams p) {
   {
     int u = ex.x, c = ex.y;
     for (int s = s0; s < s1; ++s) {
-      const int n = seg_tiles(p, s);
+      const int n = ((in_lds ? s_cnt[s] : sup_count(p, s)) + kTile - 1) / kTile;
       off[s] = u;
       coff[s] = c;
       u += n;
@@ -144,25 +171,26 @@ __global__ __launch_bounds__(1024) void stream_plan_kernel(DecodeParams p) {
     }
   }
   const int U = tot.x, C = tot.y;
-  // workgroups in use: at most one per cost unit, so consecutive workgroup
-  // boundaries differ and only a piece's first workgroup can start inside
-  // its query-load cost
-  const int G = min(p.grid, C);
+  // groups in use: at most one per cost unit, so consecutive group
+  // boundaries differ and only a piece's first group can start inside its
+  // query-load cost
+  const int NG = min(p.grid / GR, C);
   if (tid == 0) {
-    off[nseg] = U;
-    coff[nseg] = C;
+    off[nsup] = U;
+    coff[nsup] = C;
     p.plan[0] = U;
-    p.plan[1] = G;
-    s_wgu[G] = U;
-    p.wg_ustart[G] = U;
+    p.plan[1] = NG * GR;
+    s_wgu[NG] = U;
+    p.wg_ustart[NG] = U;
   }
   __syncthreads();
 
-  // first unit of each workgroup: cost boundary g C / G mapped to the unit
-  // sequence (a boundary inside a segment's query cost maps to its first tile)
-  for (int g = tid; g < G; g += 1024) {
-    const long long x = (long long)g * C / G;
-    const int s = last_le(coff, nseg + 1, x);
+  // first unit of each group: cost boundary gamma C / NG mapped to the unit
+  // sequence (a boundary inside a super-segment's query cost maps to its
+  // first tile)
+  for (int g = tid; g < NG; g += 1024) {
+    const long long x = (long long)g * C / NG;
+    const int s = last_le(coff, nsup + 1, x);
     const int n = off[s + 1] - off[s];
     long long k = x - coff[s] - kPieceCost;
     k = k < 0 ? 0 : (k > n - 1 ? n - 1 : k);
@@ -172,22 +200,26 @@ __global__ __launch_bounds__(1024) void stream_plan_kernel(DecodeParams p) {
   }
   __syncthreads();
 
-  // start record of each workgroup: its range, its first unit with the
-  // owned-token count of that request, and the segment (with its count) of
-  // the unit after its first segment, so that the decode kernel resolves
-  // the rows of its first two tiles after a single round of loads
+  // start record of each workgroup (group w / GR, row block w % GR): its
+  // range, its first unit with the owned-token count of that request, and
+  // the segment (with its count) of the unit after its first super-segment,
+  // so that the decode kernel resolves the rows of its first two tiles after
+  // a single round of loads
   for (int w = tid; w < p.grid; w += 1024) {
     int32_t* rec = p.wg_rec + (long long)w * kRecInts;
-    const int u0 = w < G ? s_wgu[w] : 0, u1 = w < G ? s_wgu[w + 1] : 0;
+    const int grp = w / GR, j = w - grp * GR;
+    const int u0 = grp < NG ? s_wgu[grp] : 0, u1 = grp < NG ? s_wgu[grp + 1] : 0;
     int seg = 0, tile = 0, cnt = 0, seg1 = 0, cnt1 = 0;
     if (u1 > u0) {
-      seg = last_le(off, nseg + 1, u0);
-      tile = u0 - off[seg];
-      cnt = in_lds ? s_cnt[seg] : seg_count(p, seg);
-      const int un = off[seg + 1];          // first unit past the first segment
+      const int sp = last_le(off, nsup + 1, u0);
+      tile = u0 - off[sp];
+      seg = seg_of_sup(p, sp, j);
+      cnt = in_lds ? s_cnt[sp] : sup_count(p, sp);
+      const int un = off[sp + 1];          // first unit past the first super-segment
       if (un < u1) {
-        seg1 = last_le(off, nseg + 1, un);
-        cnt1 = in_lds ? s_cnt[seg1] : seg_count(p, seg1);
+        const int sp1 = last_le(off, nsup + 1, un);
+        seg1 = seg_of_sup(p, sp1, j);
+        cnt1 = in_lds ? s_cnt[sp1] : sup_count(p, sp1);
       }
     }
     rec[0] = u1 - u0;
@@ -198,27 +230,38 @@ __global__ __launch_bounds__(1024) void stream_plan_kernel(DecodeParams p) {
     rec[5] = cnt1;
   }
 
-  // pieces of each segment (one per non-empty workgroup it meets) and
-  // partial slots (only for segments cut into several pieces, unless the
-  // launch runs several shards: then every piece leaves a partial)
+  // pieces of each segment (one per non-empty group its super-segment
+  // meets) and partial slots (only for segments cut into several pieces,
+  // unless the launch runs several shards: then every piece leaves a
+  // partial), allocated in segment order so that the shards of one row
+  // block have consecutive slots
   const int np_slot = p.fold > 1 ? 1 : 2;
-  int ms = 0;
-  for (int s = s0; s < s1; ++s) {
-    const int o = off[s], n = off[s + 1] - o;
-    if (n > 0) {
-      const int np = last_le(s_wgu, G, o + n - 1) - last_le(s_wgu, G, o) + 1;
-      ms += np >= np_slot ? np : 0;
+  const int sper = (nseg + 1023) / 1024;
+  const int q0 = min(tid * sper, nseg), q1 = min(q0 + sper, nseg);
+  auto seg_pieces = [&](int s, int& first) {
+    int sp = s;
+    if (GR > 1) {
+      const int q = s / p.fold, ri = s - q * p.fold;
+      const int b = q / RB;
+      sp = b * p.fold + ri;
     }
+    const int o = off[sp], n = off[sp + 1] - o;
+    first = 0;
+    if (n <= 0) return 0;
+    first = last_le(s_wgu, NG, o);
+    return last_le(s_wgu, NG, o + n - 1) - first + 1;
+  };
+  int ms = 0;
+  for (int s = q0; s < q1; ++s) {
+    int first;
+    const int np = seg_pieces(s, first);
+    ms += np >= np_slot ? np : 0;
   }
   const int2 ex2 = block_excl_scan2(ms, 0, s_wave, tot);
   int slot = ex2.x;
-  for (int s = s0; s < s1; ++s) {
-    const int o = off[s], n = off[s + 1] - o;
-    int np = 0, first = 0;
-    if (n > 0) {
-      first = last_le(s_wgu, G, o);
-      np = last_le(s_wgu, G, o + n - 1) - first + 1;
-    }
+  for (int s = q0; s < q1; ++s) {
+    int first;
+    const int np = seg_pieces(s, first);
     p.seg_info[s] = make_int4(slot, np, first, 0);
     slot += np >= np_slot ? np : 0;
   }
@@ -248,6 +291,20 @@ struct Cursor {
   __device__ __forceinline__ void advance(const DecodeParams& p) {
     if (++tile < ntiles) return;
     tile = 0;
+    if (p.rgroup > 1) {
+      // row-block groups: the same row block of the next (request, shard)
+      for (;;) {
+        if (kFold && ++r < p.fold) {
+        } else {
+          ++b;
+          r = kFold ? 0 : r;
+        }
+        seg = (b * p.row_blocks + rb) * p.fold + (kFold ? r : 0);
+        cnt = ld_const(p.req_cnt + b * p.fold + (kFold ? r : 0));
+        ntiles = (cnt + kTile - 1) / kTile;
+        if (ntiles > 0) return;
+      }
+    }
     for (;;) {
       ++seg;
       if (kFold && ++r < p.fold) {
@@ -763,7 +820,7 @@ void attn_ws_kernel(DecodeParams p) {
             p.lse[(long long)b * p.rows + row] = p.lse_base2 ? lse2 : lse2 * kLn2;
           } else {
             const int4 si = ld_const(p.seg_info + seg);
-            p.spart_lse[(long long)(si.x + g - si.z) * kWsRows + (row - rb * kWsRows)] = lse2;
+            p.spart_lse[(long long)(si.x + g / p.rgroup - si.z) * kWsRows + (row - rb * kWsRows)] = lse2;
           }
         }
       }
@@ -962,7 +1019,7 @@ void attn_ws_kernel(DecodeParams p) {
           obase = (__bf16*)p.out + ((long long)b * p.rows + row0) * kDv;
         } else {
           const int4 si = ld_const(p.seg_info + seg);
-          obase = (__bf16*)p.spart_o + ((long long)(si.x + g - si.z) * kWsRows) * kDv;
+          obase = (__bf16*)p.spart_o + ((long long)(si.x + g / p.rgroup - si.z) * kWsRows) * kDv;
         }
         const int rr0 = lane >> 4, c16 = lane & 15;
 #pragma unroll
