@@ -295,21 +295,20 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
     // one persistent workgroup per CU but one in 16 (a multiple of 8 so that
     // the workgroup order can follow the XCDs) unless the caller fixes the
     // count: the free CUs run the small kernels of concurrent shards (their
-    // combine) alongside, which shortens a step of concurrent partials
-    // (the single launch of every shard with fp8 KV, compute-bound, takes
-    // every CU: 325 -> 303 µs on the deepseek-like fp8 step, where bf16
-    // shapes gain nothing or lose). With row-block groups every XCD holds
-    // whole groups: per XCD a multiple of the group size, all its CUs when
-    // leaving one in 16 free would cost a whole group of 8.
-    const bool all_cus = all_shards && a->num_shards > 1 && a->kv_dtype == MLA_DTYPE_FP8_E4M3;
+    // combine) alongside, which shortens a step of concurrent partials of
+    // one-row-block requests. Requests of several row blocks (row-block
+    // groups, every XCD holding whole groups) and the single launch of every
+    // shard with fp8 KV (compute-bound) take every CU the group size fits:
+    // there the extra workgroups gain more than the free CUs (deepseek-like
+    // fp8 step 0.424 -> 0.403 ms, q_len 4 0.438 -> 0.390, skewed 0.645 ->
+    // 0.628; the one-row-block kimi-like step is within noise either way).
+    const bool all_cus = rgroup > 1 || (all_shards && a->num_shards > 1 && a->kv_dtype == MLA_DTYPE_FP8_E4M3);
     if (a->split_target > 0) {
       grid = a->split_target;
     } else {
       const int32_t per_xcd = cus / 8;
-      int32_t slots = all_cus ? per_xcd : per_xcd - per_xcd / 16;
-      slots = (slots / rgroup) * rgroup;
-      if (slots * 4 < per_xcd * 3) slots = (per_xcd / rgroup) * rgroup;
-      grid = 8 * slots;
+      const int32_t slots = all_cus ? (per_xcd / rgroup) * rgroup : per_xcd - per_xcd / 16;
+      grid = 8 * (slots > 0 ? slots : 1);
     }
     if (grid < 8) grid = 8;
     if (grid > mla::kMaxGrid) grid = mla::kMaxGrid;
