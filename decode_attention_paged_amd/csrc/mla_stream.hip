@@ -971,7 +971,10 @@ void attn_ws_kernel(DecodeParams p) {
       const float l0 = lbuf[tok], l1 = lbuf[32 + tok];
       __syncthreads();   // every output wave is done with the stages
       // epilogue: lane l holds rows r * 32 + (l & 31); o[db][r][v] is dim
-      // 128 wq + 32 db + 8 (v >> 2) + 4 hi + (v & 3)
+      // 128 wq + 32 db + 8 (v >> 2) + 4 hi + (v & 3). The rows are stored
+      // non-temporally: nothing in this launch reads them again, and rows
+      // left dirty in the XCDs' L2 caches would all be written back when the
+      // launch ends (kimi-like shard 34.8 -> 32.3 µs, fp8 52 -> 50 µs)
       float inv[2];
       {
         const bool a0 = l0 > 0.f || l0 != l0, a1 = l1 > 0.f || l1 != l1;
@@ -992,7 +995,7 @@ void attn_ws_kernel(DecodeParams p) {
               for (int q = 0; q < 4; ++q) {
                 const f32x4_t x = {o[db][r][4 * q] * inv[r], o[db][r][4 * q + 1] * inv[r],
                                    o[db][r][4 * q + 2] * inv[r], o[db][r][4 * q + 3] * inv[r]};
-                *(f32x4_t*)(dst + 32 * db + 8 * q) = x;
+                __builtin_nontemporal_store(x, (f32x4_t*)(dst + 32 * db + 8 * q));
               }
           }
         }
@@ -1026,7 +1029,7 @@ void attn_ws_kernel(DecodeParams p) {
         for (int i = 0; i < kWsRows / 4; ++i) {
           const int rr = 4 * i + rr0;
           const bf16x8_t x = *(const bf16x8_t*)(sb + kWsStagePitch * rr + 16 * c16);
-          if (row0 + rr < p.rows) *(bf16x8_t*)(obase + (long long)rr * kDv + 128 * wq + 8 * c16) = x;
+          if (row0 + rr < p.rows) __builtin_nontemporal_store(x, (bf16x8_t*)(obase + (long long)rr * kDv + 128 * wq + 8 * c16));
         }
       }
       t += n;
