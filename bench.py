@@ -289,8 +289,8 @@ def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True, spl
         metadata_us_per_shard=metadata_us, plan_us_per_shard=plan_us, step_timing=step_timing,
         eager_ms_per_step=eager_ms_step,
     )
-    if use_graph and split_target == 0:
-        res["all_shards"] = bench_all_shards(wl, dws, bufs, steps, warmup, kv_bytes, flops)
+    if split_target == 0:
+        res["all_shards"] = bench_all_shards(wl, dws, bufs, steps, warmup, kv_bytes, flops, use_graph)
     # the contraction runs on bf16 MFMAs for both KV types (fp8 pages are
     # converted to bf16 exactly, in registers), so its peak is the bf16 one
     peak_tf = BF16_PEAK_TFLOPS
@@ -301,14 +301,15 @@ def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True, spl
     return wl, res
 
 
-def bench_all_shards(wl, dws, bufs, steps: int, warmup: int, kv_bytes: int, flops: float):
+def bench_all_shards(wl, dws, bufs, steps: int, warmup: int, kv_bytes: int, flops: float,
+                     use_graph: bool = True):
     """The same step as one call: every shard in one launch, the merge fused
     into the piece combine (mla_decode_all_shards). Its schedule is built
     once per decode step and reused; the call is captured as a HIP graph per
     input set, checked bit for bit against the eager call and against the
     separate step's merged output (within the KV type's tolerance), then
-    replayed for the step time. The attention kernel is timed on its own
-    dispatch in eager calls."""
+    replayed for the step time (use_graph False: timed as eager calls). The
+    attention kernel is timed on its own dispatch in eager calls."""
     import torch
 
     from decode_attention_paged_amd import step as ST
@@ -326,10 +327,14 @@ def bench_all_shards(wl, dws, bufs, steps: int, warmup: int, kv_bytes: int, flop
     aev = [(HipEvent(), HipEvent()) for _ in range(steps)]
     for k in range(warmup):
         ST.run_all_shards(dws[k % len(dws)], bufs, reuse_plan=True)
+    t0 = time.perf_counter()
     for k in range(steps):
         ST.run_all_shards(dws[k % len(dws)], bufs, reuse_plan=True, events=aev[k])
     torch.cuda.synchronize()
+    eager_ms = 1e3 * (time.perf_counter() - t0) / steps
     attn_ms = statistics.mean(a.elapsed_ms(b) for a, b in aev)
+    if not use_graph:
+        return _all_shards_result(wl, kv_bytes, flops, eager_ms, attn_ms, d_out, d_lse, "eager calls")
     graphs = []
     for dw in dws:
         g = torch.cuda.CUDAGraph()
@@ -356,17 +361,22 @@ def bench_all_shards(wl, dws, bufs, steps: int, warmup: int, kv_bytes: int, flop
     torch.cuda.synchronize()
     ms = 1e3 * (time.perf_counter() - t0) / steps
     del graphs
-    # algorithmic bytes of the call: every owned row once, the queries once
-    # per shard (each shard's segments load them), the merged out and LSE
+    return _all_shards_result(wl, kv_bytes, flops, ms, attn_ms, d_out, d_lse, "graph replay")
+
+
+def _all_shards_result(wl, kv_bytes, flops, ms, attn_ms, d_out, d_lse, timing):
+    # algorithmic bytes of the call: every visible KV row once, the queries
+    # once, the merged out and LSE (the queries the kernel reads again for
+    # each shard's segments are overhead, as piece partials are)
     rows = wl.batch * wl.q_len * wl.heads
     out_elt = 2 if wl.out_dtype == "bf16" else 4
-    call_bytes = kv_bytes + wl.shards * rows * 576 * 2 + rows * (512 * out_elt + 4)
+    call_bytes = kv_bytes + rows * 576 * 2 + rows * (512 * out_elt + 4)
     return dict(ms_per_step=ms, kv_gbs=kv_bytes / (ms * 1e-3) / 1e9, tflops=flops / (ms * 1e-3) / 1e12,
                 attn_kernel_us=1e3 * attn_ms, call_bytes=call_bytes,
                 attn_kernel_gbs=call_bytes / (attn_ms * 1e-3) / 1e9,
                 attn_kernel_hbm_frac=call_bytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 attn_kernel_mfma_frac=flops / (attn_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                max_abs_diff_vs_separate=dict(out=d_out, lse=d_lse))
+                step_timing=timing, max_abs_diff_vs_separate=dict(out=d_out, lse=d_lse))
 
 
 def bench_merge_sweep(replays: int = 20, warmup: int = 5):
@@ -559,7 +569,10 @@ def config_summary(r):
         out["all_shards_step"] = dict(ms_per_step=round(a["ms_per_step"], 5), kv_gbs=round(a["kv_gbs"], 1),
                                       attn_kernel_us=round(a["attn_kernel_us"], 2),
                                       attn_kernel_hbm_frac=round(a["attn_kernel_hbm_frac"], 4),
-                                      attn_kernel_mfma_frac=round(a.get("attn_kernel_mfma_frac", 0.0), 4))
+                                      attn_kernel_mfma_frac=round(a.get("attn_kernel_mfma_frac", 0.0), 4),
+                                      algorithmic_bytes_per_launch=int(a["call_bytes"]),
+                                      traffic=traffic_from_profile("all_shards_" + r["name"]),
+                                      step_timing=a.get("step_timing", "graph replay"))
     return out
 
 
@@ -691,7 +704,8 @@ def main() -> int:
                                  attn_kernel_us=round(res["all_shards"]["attn_kernel_us"], 2),
                                  attn_kernel_hbm_frac=round(res["all_shards"]["attn_kernel_hbm_frac"], 4),
                                  timing="mla_decode_all_shards: every shard in one launch, merge fused, "
-                                        "graph replay; schedule built once per step")
+                                        + res["all_shards"].get("step_timing", "graph replay")
+                                        + "; schedule built once per step")
                             if "all_shards" in res else None),
         "roofline": roof,
         "configs": per_config,
