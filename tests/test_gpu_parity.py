@@ -327,6 +327,28 @@ def test_step_is_deterministic():
     assert torch.equal(a.lse.view(torch.int32), b.lse.view(torch.int32))
 
 
+@pytest.mark.parametrize("name", ["kimi_like", "deepseek_like_fp8", "mtp_q4", "skewed"])
+def test_gather_paths_agree_bit_for_bit(name):
+    """The shard-local KV indices and the block table name the same rows, and
+    the owned counts and the schedule are the same, so every shard's partial
+    (out, lse) and the merged result must be bit-identical between the two
+    gathers (the step driver reads the block table by default)."""
+    wl = _small(name)
+    dw = ST.DeviceWorkload.upload(wl)
+    a, b = ST.StepBuffers(dw), ST.StepBuffers(dw)
+    a.fill_nan()
+    b.fill_nan()
+    _flush(f"gather paths {name}")
+    ST.run_step(dw, a, use_metadata=True)
+    ST.run_step(dw, b, use_metadata=False)
+    torch.cuda.synchronize()
+    for r in range(wl.shards):
+        assert torch.equal(a.outs[r].view(torch.uint8), b.outs[r].view(torch.uint8)), f"out shard {r}"
+        assert torch.equal(a.lses[r].view(torch.uint8), b.lses[r].view(torch.uint8)), f"lse shard {r}"
+    assert torch.equal(a.out.view(torch.uint8), b.out.view(torch.uint8))
+    assert torch.equal(a.lse.view(torch.uint8), b.lse.view(torch.uint8))
+
+
 # --------------------------------------------------------------------------
 # merge
 # --------------------------------------------------------------------------
