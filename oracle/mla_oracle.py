@@ -37,6 +37,10 @@ What it computes, and the passage each step follows:
 * ``merge`` -- [symm_a2a] Modifications, the fourth kernel (and the ag_rs /
   a2a combines under Motivation): the LSE-weighted softmax reduction of all
   ranks' partial outputs into the full-context result.
+* ``quantize_query`` -- [DCP decode] implementation step 3 (the fp8 KV path
+  prepares the query with a fused concat-and-quantise): e4m3 codes of the
+  query by the same rounding rule as the fp8 KV rows; ``decode_partial``
+  then reads the query as those codes times the query scale.
 * ``append_kv`` / ``encode_e4m3`` -- [DCP decode] key code (the layout test:
   each appended token grows exactly one rank's local length, rank
   (L - 1) mod S) and implementation steps 3-4 (the KV row is written with
@@ -177,6 +181,11 @@ def attend(qrows: np.ndarray, K: np.ndarray, scale: float, visible: np.ndarray
 
 
 def _q_rows(wl, b: int) -> np.ndarray:
+    """Query rows of request b in fp64: the bf16 query, or, when the workload
+    carries e4m3 query codes, their values times the query scale."""
+    codes = getattr(wl, "q_codes", None)
+    if codes is not None:
+        return (decode_e4m3(codes[b]) * float(wl.q_scale)).reshape(wl.q_len * wl.heads, D_QK)
     return decode_bf16(wl.q[b]).reshape(wl.q_len * wl.heads, D_QK)
 
 
@@ -308,6 +317,17 @@ def encode_e4m3(x) -> np.ndarray:
     code = np.where(pick_hi, hi, lo).astype(np.uint8)
     code = np.where(np.isnan(x), np.uint8(0x7F), code)
     return code | sign
+
+
+def quantize_query(q_bits: np.ndarray, q_scale: float) -> np.ndarray:
+    """e4m3 codes of a bf16 query ([DCP decode] 实现拆解 step 3: with an fp8
+    KV pool the query is prepared by a fused concat-and-quantise). Each code
+    is the nearest e4m3 value to the fp32 quotient q / q_scale, by the same
+    rule as the fp8 KV rows (ties to the even code, saturating at 448, NaN
+    keeps its sign). ``q_bits`` holds bf16 patterns (uint16), the 512 latent
+    dims and the 64 rope dims of each row already side by side."""
+    x = decode_bf16(q_bits).astype(np.float32)             # exact
+    return encode_e4m3(x / np.float32(q_scale))
 
 
 def append_kv(kv_pages: np.ndarray, k_nope: np.ndarray, k_rope: np.ndarray, seq_lens: Sequence[int],

@@ -153,6 +153,11 @@ class Workload:
     # per-request decode depth (rows i < q_lens[b] are real, the rest padding
     # up to the step's q_len); None = every request q_len deep
     q_lens: Optional[np.ndarray] = None
+    # the query as e4m3 codes [B, q_len, H, 576] uint8 with a per-tensor
+    # dequant scale (the fp8-KV path's concat-and-quantise of the query), or
+    # None: the query is read as bf16
+    q_codes: Optional[np.ndarray] = None
+    q_scale: float = 0.0
 
     @property
     def max_pages(self) -> int:
