@@ -61,6 +61,7 @@ class DecodeArgs(ctypes.Structure):
         ("q_rope", ctypes.c_void_p),
         ("q_row_stride", ctypes.c_int64),
         ("q_rope_row_stride", ctypes.c_int64),
+        ("q_scale", ctypes.c_float),
     ]
 
 
@@ -103,7 +104,8 @@ class AppendArgs(ctypes.Structure):
 
 EXPORTS = ("mla_build_shard_metadata", "mla_decode_workspace_bytes", "mla_decode_partial",
            "mla_decode_partial_noalloc", "mla_decode_plan",
-           "mla_decode_all_shards", "mla_decode_all_shards_workspace_bytes", "mla_merge_partials", "mla_append_kv", "mla_status_string", "mla_last_error", "mla_abi_version",
+           "mla_decode_all_shards", "mla_decode_all_shards_workspace_bytes", "mla_merge_partials", "mla_append_kv",
+           "mla_quantize_q", "mla_status_string", "mla_last_error", "mla_abi_version",
            "mla_sizeof_decode_args", "mla_sizeof_merge_args", "mla_sizeof_append_args")
 
 _lib = None
@@ -140,6 +142,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_merge_partials.restype = ctypes.c_int
     lib.mla_append_kv.argtypes = [ctypes.POINTER(AppendArgs), vp]
     lib.mla_append_kv.restype = ctypes.c_int
+    i64 = ctypes.c_int64
+    lib.mla_quantize_q.argtypes = [vp, vp, i64, i64, i64, ctypes.c_float, vp, vp]
+    lib.mla_quantize_q.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_last_error.argtypes = []
@@ -242,12 +247,21 @@ def _row_stride(t, dims: int, what: str) -> int:
 
 def _decode_args(q, kv_pages, block_table, seq_lens, shard_id, num_shards, q_len, out, lse, workspace,
                  kv_scale, softmax_scale, lse_base, local_seq_lens, local_kv_indices, split_target, events,
-                 reuse_plan, q_lens=None, q_rope=None):
+                 reuse_plan, q_lens=None, q_rope=None, q_scale=0.0):
+    import torch
     a = DecodeArgs()
     B, ql, H = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
     if ql != q_len:
         raise ValueError("q.shape[1] must equal q_len")
-    if q_rope is None:
+    if q.dtype == torch.uint8:
+        # e4m3 query codes [B, q_len, H, 576] with their dequant scale
+        if not q_scale > 0.0 or q_rope is not None:
+            raise ValueError("an e4m3 query (uint8 codes) needs q_scale > 0 and no q_rope")
+        a.q_row_stride = _row_stride(q, D_QK, "q (e4m3 codes)")
+        a.q_scale = float(q_scale)
+    elif q_scale != 0.0:
+        raise ValueError("q_scale applies to an e4m3 query (uint8 codes) only")
+    elif q_rope is None:
         a.q_row_stride = _row_stride(q, D_QK, "q")
     else:
         if tuple(q_rope.shape[:3]) != (B, ql, H):
@@ -279,7 +293,7 @@ def mla_decode_partial(q, kv_pages, block_table, seq_lens, shard_id: int, num_sh
                        out, lse, workspace, *, kv_scale: float = 1.0, softmax_scale: float,
                        lse_base: int = LSE_BASE_E, local_seq_lens=None, local_kv_indices=None,
                        split_target: int = 0, events=None, reuse_plan: bool = False, q_lens=None,
-                       q_rope=None, stream=None) -> int:
+                       q_rope=None, q_scale: float = 0.0, stream=None) -> int:
     """Rank-local (out, lse) of one shard; returns the LSE base written.
 
     q [B, q_len, H, 576] bf16; kv_pages [P, 64, 576] bf16 or uint8 (e4m3);
@@ -291,12 +305,14 @@ def mla_decode_partial(q, kv_pages, block_table, seq_lens, shard_id: int, num_sh
     ``q_lens``: optional [B] i32 decode depth per request (rows past it are
     padding, written (0, -inf)). ``q_rope``: optional [B, q_len, H, 64] bf16
     rope part of the query; then ``q`` is the [B, q_len, H, 512] latent part
-    (either may be a strided view, e.g. two slices of one buffer).
+    (either may be a strided view, e.g. two slices of one buffer). A uint8
+    ``q`` [B, q_len, H, 576] holds e4m3 query codes (mla_quantize_q) whose
+    values are code x ``q_scale`` (fp8 KV only).
     """
     lib = load()
     a = _decode_args(q, kv_pages, block_table, seq_lens, shard_id, num_shards, q_len, out, lse, workspace,
                      kv_scale, softmax_scale, lse_base, local_seq_lens, local_kv_indices, split_target, events,
-                     reuse_plan, q_lens, q_rope)
+                     reuse_plan, q_lens, q_rope, q_scale)
     written = ctypes.c_int(-1)
     _check(lib.mla_decode_partial(ctypes.byref(a), ctypes.byref(written), _stream_ptr(stream)))
     return int(written.value)
@@ -305,14 +321,15 @@ def mla_decode_partial(q, kv_pages, block_table, seq_lens, shard_id: int, num_sh
 def mla_decode_partial_noalloc(q, kv_pages, block_table, seq_lens, shard_id: int, num_shards: int, q_len: int,
                                out, lse, *, kv_scale: float = 1.0, softmax_scale: float,
                                lse_base: int = LSE_BASE_E, local_seq_lens=None, local_kv_indices=None,
-                               split_target: int = 0, events=None, q_lens=None, q_rope=None, stream=None) -> int:
+                               split_target: int = 0, events=None, q_lens=None, q_rope=None,
+                               q_scale: float = 0.0, stream=None) -> int:
     """mla_decode_partial without a workspace: the library's own device
     scratch holds the schedule and partials (calls on one device must not
     overlap). Returns the LSE base written."""
     lib = load()
     a = _decode_args(q, kv_pages, block_table, seq_lens, shard_id, num_shards, q_len, out, lse, None,
                      kv_scale, softmax_scale, lse_base, local_seq_lens, local_kv_indices, split_target, events,
-                     False, q_lens, q_rope)
+                     False, q_lens, q_rope, q_scale)
     written = ctypes.c_int(-1)
     _check(lib.mla_decode_partial_noalloc(ctypes.byref(a), ctypes.byref(written), _stream_ptr(stream)))
     return int(written.value)
@@ -321,7 +338,7 @@ def mla_decode_partial_noalloc(q, kv_pages, block_table, seq_lens, shard_id: int
 def mla_decode_all_shards(q, kv_pages, block_table, seq_lens, num_shards: int, q_len: int, out, lse, workspace,
                           *, kv_scale: float = 1.0, softmax_scale: float, lse_base: int = LSE_BASE_E,
                           split_target: int = 0, events=None, reuse_plan: bool = False, q_lens=None,
-                          q_rope=None, stream=None) -> int:
+                          q_rope=None, q_scale: float = 0.0, stream=None) -> int:
     """Every shard of the cyclic split in one launch, merged: out / lse get
     the full-context result. Shapes as mla_decode_partial; workspace of at
     least mla_decode_all_shards_workspace_bytes(B, H, q_len, num_shards).
@@ -331,7 +348,7 @@ def mla_decode_all_shards(q, kv_pages, block_table, seq_lens, num_shards: int, q
     lib = load()
     a = _decode_args(q, kv_pages, block_table, seq_lens, 0, num_shards, q_len, out, lse, workspace,
                      kv_scale, softmax_scale, lse_base, None, None, split_target, events, reuse_plan, q_lens,
-                     q_rope)
+                     q_rope, q_scale)
     written = ctypes.c_int(-1)
     _check(lib.mla_decode_all_shards(ctypes.byref(a), ctypes.byref(written), _stream_ptr(stream)))
     return int(written.value)
@@ -340,13 +357,13 @@ def mla_decode_all_shards(q, kv_pages, block_table, seq_lens, num_shards: int, q
 def mla_decode_plan(q, kv_pages, block_table, seq_lens, shard_id: int, num_shards: int, q_len: int,
                     out, lse, workspace, *, kv_scale: float = 1.0, softmax_scale: float,
                     lse_base: int = LSE_BASE_E, local_seq_lens=None, local_kv_indices=None,
-                    split_target: int = 0, stream=None) -> None:
+                    split_target: int = 0, q_scale: float = 0.0, stream=None) -> None:
     """The work schedule of mla_decode_partial with the same arguments, into
     ``workspace`` (built once per decode step, reused with reuse_plan)."""
     lib = load()
     a = _decode_args(q, kv_pages, block_table, seq_lens, shard_id, num_shards, q_len, out, lse, workspace,
                      kv_scale, softmax_scale, lse_base, local_seq_lens, local_kv_indices, split_target, None,
-                     False)
+                     False, q_scale=q_scale)
     _check(lib.mla_decode_plan(ctypes.byref(a), _stream_ptr(stream)))
 
 
@@ -371,6 +388,24 @@ def mla_merge_partials(outs: Sequence, lses: Sequence, bases: Sequence[int], out
     if events is not None:
         a.event_begin, a.event_end = int(events[0].cuda_event), int(events[1].cuda_event)
     _check(lib.mla_merge_partials(ctypes.byref(a), _stream_ptr(stream)))
+
+
+def mla_quantize_q(q, out, q_scale: float, q_rope=None, stream=None) -> None:
+    """e4m3 codes of a bf16 query into ``out`` [B, q_len, H, 576] uint8
+    (contiguous): the nearest e4m3 value to q / q_scale, ties to even,
+    saturating. ``q`` [B, q_len, H, 576] bf16, or its [.., 512] latent part
+    with ``q_rope`` [.., 64] (strided views allowed, as for the decode)."""
+    lib = load()
+    if out.dim() != 4 or int(out.shape[3]) != D_QK or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, q_len, H, 576] uint8 tensor")
+    rows = int(out.shape[0]) * int(out.shape[1]) * int(out.shape[2])
+    if q_rope is None:
+        qs, rs = _row_stride(q, D_QK, "q"), 0
+    else:
+        qs, rs = _row_stride(q, 512, "q (latent part)"), _row_stride(q_rope, D_QK - 512, "q_rope")
+    if tuple(q.shape[:3]) != tuple(out.shape[:3]):
+        raise ValueError("q and out must agree in [B, q_len, H]")
+    _check(lib.mla_quantize_q(_ptr(q), _ptr(q_rope), qs, rs, rows, float(q_scale), _ptr(out), _stream_ptr(stream)))
 
 
 def mla_append_kv(k_nope, k_rope, seq_lens, block_table, kv_pages, shard_id: int, num_shards: int, *,

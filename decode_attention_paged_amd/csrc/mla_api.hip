@@ -162,6 +162,38 @@ mla_status_t mla_build_shard_metadata(const int32_t* seq_lens, const int32_t* bl
   return ok();
 }
 
+mla_status_t mla_quantize_q(const void* q, const void* q_rope, int64_t q_row_stride, int64_t q_rope_row_stride,
+                            int64_t rows, float q_scale, void* out, void* stream) {
+  if (rows < 0) return fail(MLA_STATUS_INVALID_ARGUMENT, "rows must be >= 0 (got %lld)", (long long)rows);
+  if (!(q_scale > 0.f) || !isfinite(q_scale))
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "q_scale must be finite and > 0");
+  const bool split = q_rope != nullptr;
+  const int64_t qs = q_row_stride == 0 ? (split ? 512 : MLA_D_QK) : q_row_stride;
+  const int64_t rs = q_rope_row_stride == 0 ? 64 : q_rope_row_stride;
+  if (qs < (split ? 512 : MLA_D_QK) || qs % 8 != 0)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "q_row_stride %lld must be a multiple of 8 and >= %d",
+                (long long)q_row_stride, split ? 512 : MLA_D_QK);
+  if (split && (rs < 64 || rs % 8 != 0))
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "q_rope_row_stride %lld must be a multiple of 8 and >= 64",
+                (long long)q_rope_row_stride);
+  if (rows > 0 && (q == nullptr || out == nullptr))
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "q and out are required");
+  if (((uintptr_t)q & 15) != 0 || ((uintptr_t)q_rope & 15) != 0 || ((uintptr_t)out & 15) != 0)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "q, q_rope and out must be 16-byte aligned");
+  if (rows == 0) return ok();
+  mla::QuantizeQParams p;
+  p.q = (const uint16_t*)q;
+  p.q_rope = split ? (const uint16_t*)q_rope : p.q + 512;
+  p.q_stride = qs;
+  p.q_rope_stride = split ? rs : qs;
+  p.rows = rows;
+  p.q_scale = q_scale;
+  p.out = (uint8_t*)out;
+  hipError_t err = mla::launch_quantize_q(p, (hipStream_t)stream);
+  if (err != hipSuccess) return fail(MLA_STATUS_DEVICE_ERROR, "quantize_q launch: %s", hipGetErrorString(err));
+  return ok();
+}
+
 mla_status_t mla_append_kv(const mla_append_args_t* a, void* stream) {
   if (a == nullptr) return fail(MLA_STATUS_INVALID_ARGUMENT, "args is NULL");
   if (a->batch < 0) return fail(MLA_STATUS_INVALID_ARGUMENT, "batch must be >= 0 (got %d)", a->batch);
@@ -260,7 +292,20 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
     if (!a->q || !a->kv_pages || !a->block_table || !a->seq_lens || !a->out || !a->lse || (!a->workspace && !noalloc))
       return fail(MLA_STATUS_INVALID_ARGUMENT, "q, kv_pages, block_table, seq_lens, out, lse and workspace are required");
   }
-  {
+  if (!(a->q_scale >= 0.f) || !isfinite(a->q_scale))
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "q_scale must be 0 (bf16 query) or finite and > 0 (e4m3 query codes)");
+  const bool q8 = a->q_scale > 0.f;
+  if (q8) {
+    if (a->kv_dtype != MLA_DTYPE_FP8_E4M3)
+      return fail(MLA_STATUS_INVALID_ARGUMENT, "an e4m3 query (q_scale > 0) needs an FP8_E4M3 KV pool");
+    if (a->q_rope != nullptr)
+      return fail(MLA_STATUS_INVALID_ARGUMENT, "an e4m3 query holds all 576 dims of a row: q_rope must be NULL");
+    const int64_t qs = a->q_row_stride == 0 ? MLA_D_QK : a->q_row_stride;
+    if (qs < MLA_D_QK || qs % 16 != 0)
+      return fail(MLA_STATUS_INVALID_ARGUMENT, "q_row_stride %lld of the e4m3 query must be a multiple of 16 and >= %d",
+                  (long long)a->q_row_stride, MLA_D_QK);
+    if (((uintptr_t)a->q & 15) != 0) return fail(MLA_STATUS_INVALID_ARGUMENT, "q must be 16-byte aligned");
+  } else {
     const bool split = a->q_rope != nullptr;
     const int64_t qs = a->q_row_stride == 0 ? (split ? 512 : MLA_D_QK) : a->q_row_stride;
     const int64_t rs = a->q_rope_row_stride == 0 ? 64 : a->q_rope_row_stride;
@@ -329,7 +374,11 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
   }
   p = mla::DecodeParams{};
   p.q = (const uint16_t*)a->q;
-  if (a->q_rope != nullptr) {
+  if (q8) {
+    p.q8 = (const uint8_t*)a->q;
+    p.q8_stride = a->q_row_stride == 0 ? MLA_D_QK : a->q_row_stride;
+    p.q_rope = p.q;
+  } else if (a->q_rope != nullptr) {
     p.q_rope = (const uint16_t*)a->q_rope;
     p.q_stride = a->q_row_stride == 0 ? 512 : a->q_row_stride;
     p.q_rope_stride = a->q_rope_row_stride == 0 ? 64 : a->q_rope_row_stride;
@@ -355,7 +404,8 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
   p.num_shards = a->num_shards;
   p.fold = fold;
   const float kv_scale = a->kv_dtype == MLA_DTYPE_FP8_E4M3 ? a->kv_scale : 1.f;
-  p.scale_log2 = (float)((double)a->softmax_scale * (double)kv_scale * 1.4426950408889634);
+  p.scale_log2 = (float)((double)a->softmax_scale * (double)kv_scale * (q8 ? (double)a->q_scale : 1.0) *
+                         1.4426950408889634);
   p.out_scale = kv_scale;
   p.lse_base2 = a->lse_base == MLA_LSE_BASE_2;
   p.out_bf16 = a->out_dtype == MLA_DTYPE_BF16;

@@ -6,7 +6,10 @@
 // layout test in which exactly one rank's local length grows per appended
 // token, the rank (L - 1) mod S). The row goes through the pool's plain row
 // write (实现拆解 step 4: the fused bf16 KV write is disabled under DCP), and
-// fp8 pools store it quantised (实现拆解 step 3: the fp8 KV path).
+// fp8 pools store it quantised (实现拆解 step 3: the fp8 KV path). The same
+// step prepares the query for an fp8 pool by one fused pass that puts its
+// latent and rope dims side by side and quantises them (quantize_q_kernel),
+// with the same rounding rule.
 //
 // One wave per appended token: 72 lanes' worth of 8-value chunks (64 latent
 // + 8 rope) spread over the wave's 64 lanes, 16-byte loads, 16-byte (bf16)
@@ -48,6 +51,21 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
   return sign | code;
 }
 
+// e4m3 codes of eight bf16 values (one 16-byte chunk) divided by `scale`
+// (finite, > 0): NaN keeps the input's sign; otherwise the fp32 quotient
+// (IEEE division; finite or infinite) is rounded by e4m3_code.
+__device__ __forceinline__ u32x2_t quantize8(const u32x4_t x, float scale) {
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t bits = (x[e >> 1] >> (16 * (e & 1))) << 16;   // bf16 -> f32, exact
+    const uint32_t code = (bits & 0x7FFFFFFFu) > 0x7F800000u ? (((bits >> 24) & 0x80u) | 0x7Fu)
+                                                             : e4m3_code(__uint_as_float(bits) / scale);
+    w[e >> 2] |= code << (8 * (e & 3));
+  }
+  return u32x2_t{w[0], w[1]};
+}
+
 __global__ __launch_bounds__(64) void append_kernel(AppendParams p) {
   const int token = blockIdx.x;                 // b * n_new + i
   const int b = token / p.n_new, i = token - b * p.n_new;
@@ -65,26 +83,32 @@ __global__ __launch_bounds__(64) void append_kernel(AppendParams p) {
   for (int c = lane; c < kChunks; c += 64) {
     const u32x4_t x = c < kNopeChunks ? *(const u32x4_t*)(nope + 8 * c)
                                       : *(const u32x4_t*)(rope + 8 * (c - kNopeChunks));
-    if (!p.fp8) {
-      *(u32x4_t*)((uint16_t*)p.kv + row * kDqk + 8 * c) = x;
-    } else {
-      uint32_t w[2] = {0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t bits = (x[e >> 1] >> (16 * (e & 1))) << 16;   // bf16 -> f32, exact
-        // NaN keeps the input's sign; otherwise the quotient is finite or
-        // infinite (kv_scale is finite and > 0) and is rounded as above
-        const uint32_t code = (bits & 0x7FFFFFFFu) > 0x7F800000u
-                                  ? (((bits >> 24) & 0x80u) | 0x7Fu)
-                                  : e4m3_code(__uint_as_float(bits) / p.kv_scale);   // IEEE fp32 division
-        w[e >> 2] |= code << (8 * (e & 3));
-      }
-      *(u32x2_t*)((uint8_t*)p.kv + row * kDqk + 8 * c) = u32x2_t{w[0], w[1]};
-    }
+    if (!p.fp8) *(u32x4_t*)((uint16_t*)p.kv + row * kDqk + 8 * c) = x;
+    else *(u32x2_t*)((uint8_t*)p.kv + row * kDqk + 8 * c) = quantize8(x, p.kv_scale);
+  }
+}
+
+// Query concat-and-quantise: one thread per 8-value chunk of a row (64
+// latent chunks from q, 8 rope chunks from q_rope), grid-stride.
+__global__ __launch_bounds__(256) void quantize_q_kernel(QuantizeQParams p) {
+  const long long total = p.rows * kChunks;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long long)gridDim.x * 256) {
+    const long long n = i / kChunks;
+    const int c = (int)(i - n * kChunks);
+    const u32x4_t x = c < kNopeChunks ? *(const u32x4_t*)(p.q + n * p.q_stride + 8 * c)
+                                      : *(const u32x4_t*)(p.q_rope + n * p.q_rope_stride + 8 * (c - kNopeChunks));
+    *(u32x2_t*)(p.out + n * kDqk + 8 * c) = quantize8(x, p.q_scale);
   }
 }
 
 }  // namespace
+
+hipError_t launch_quantize_q(const QuantizeQParams& p, hipStream_t stream) {
+  if (p.rows == 0) return hipSuccess;
+  const long long blocks = (p.rows * kChunks + 255) / 256;
+  hipLaunchKernelGGL(quantize_q_kernel, dim3((unsigned)(blocks < 2048 ? blocks : 2048)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
   const long long tokens = (long long)p.batch * p.n_new;

@@ -19,6 +19,10 @@ struct DecodeParams {
   const uint16_t* q;              // bf16 query rows, dims 0..511 (and 512..575 unless q_rope)
   const uint16_t* q_rope;         // bf16 rope dims 512..575 of every row (q + 512 when not split)
   int64_t q_stride, q_rope_stride;   // elements between consecutive query rows
+  // the query as e4m3 codes [rows][576] (row n at byte n * q8_stride), or
+  // null: the bf16 query above; only with e4m3 KV
+  const uint8_t* q8;
+  int64_t q8_stride;
   const uint8_t* kv;              // [num_pages][64][576] bf16 or e4m3
   const int32_t* block_table;     // [B][max_pages]
   const int32_t* seq_lens;        // [B] global lengths
@@ -34,7 +38,7 @@ struct DecodeParams {
   // schedule, every piece leaves a partial and the combine merges all pieces
   // of all shards into the full-context result
   int32_t fold;
-  float scale_log2;               // softmax_scale * kv_scale * log2(e)
+  float scale_log2;               // softmax_scale * kv_scale (* q_scale) * log2(e)
   float out_scale;                // kv_scale (fp8) or 1
   int32_t lse_base2;              // write lse in base 2 (else natural)
   int32_t out_bf16;               // out dtype bf16 (else f32)
@@ -108,6 +112,14 @@ struct AppendParams {
   float kv_scale;
 };
 
+struct QuantizeQParams {
+  const uint16_t* q;              // bf16, dims 0..511 of row n at n * q_stride
+  const uint16_t* q_rope;         // bf16, dims 512..575 of row n at n * q_rope_stride
+  int64_t q_stride, q_rope_stride, rows;
+  float q_scale;                  // divisor, finite and > 0
+  uint8_t* out;                   // [rows][576] e4m3 codes
+};
+
 hipError_t launch_metadata(const int32_t* seq_lens, const int32_t* block_table, int32_t batch,
                            int32_t max_pages, int32_t shard, int32_t num_shards,
                            int32_t* local_seq_lens, int32_t* local_kv_indices,
@@ -118,5 +130,6 @@ hipError_t launch_decode_stream(const DecodeParams& p, bool run_plan, hipEvent_t
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+hipError_t launch_quantize_q(const QuantizeQParams& p, hipStream_t stream);
 
 }  // namespace mla

@@ -582,9 +582,10 @@ __device__ __forceinline__ void copy8_tile_part_rt(int j, const uint8_t* srcw, u
 constexpr int kWsRows = 64;
 constexpr int kWsStagePitch = 272;     // output staging row: 128 bf16 + 16 bytes
 
-template <bool kLocal, bool kFp8, bool kFold>
+template <bool kLocal, bool kFp8, bool kFold, bool kQ8 = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_ws_kernel(DecodeParams p) {
+  static_assert(!kQ8 || kFp8, "an e4m3 query goes with an e4m3 KV pool");
   constexpr int kNS = 4;
   constexpr int kStageB = kFp8 ? kStage8 : kStageBytes;
   constexpr int kCopies = kFp8 ? 5 : 9;
@@ -636,6 +637,13 @@ void attn_ws_kernel(DecodeParams p) {
     Cursor cc;
     cc.start_known(p, rec_seg, rec_tile, rec_cnt);
     bf16x8_t qreg[kKS];
+    // e4m3 query (kQ8): the B operands of this wave's five fp8 MFMAs, each
+    // 32 codes a lane: dims 32 m0 + 16 hi .. + 15 and 32 m1 + 16 hi .. + 15
+    // with (m0, m1) = (4 j + ds, 4 j + 2 + ds) for j < 4, and the rope group
+    // m0 = 16 + ds with a zero second half for j = 4; the A operand of MFMA
+    // j holds the same dims of the lane's token (k8_load of 2 j and 2 j + 1)
+    typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
+    i32x8_t q8reg[5];
     bf16x8_t ka[kAhead];
     u32x4_t kraw[2];
     f32x16_t acc;
@@ -654,7 +662,20 @@ void attn_ws_kernel(DecodeParams p) {
       acc = f32x16_t{};
     };
     auto qk_step = [&](const uint8_t* ks, int i) {
-      if constexpr (kFp8) {
+      if constexpr (kQ8) {
+        // fp8 MFMA j after step 4 j + 1 (and the last after step 17); the
+        // next MFMA's K bytes are read right after it is issued
+        if (i % 4 == 1 || i == kKS - 1) {
+          const int j = i / 4;
+          const i32x8_t a = {(int32_t)kraw[0][0], (int32_t)kraw[0][1], (int32_t)kraw[0][2], (int32_t)kraw[0][3],
+                             (int32_t)kraw[1][0], (int32_t)kraw[1][1], (int32_t)kraw[1][2], (int32_t)kraw[1][3]};
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, q8reg[j], acc, 0, 0, 0, 127, 0, 127);
+          if (j < 4) {
+            kraw[0] = k8_load(ks, 2 * j + 2);
+            kraw[1] = k8_load(ks, 2 * j + 3);
+          }
+        }
+      } else if constexpr (kFp8) {
         const int j = i >> 1, u = i & 1;
         const bf16x8_t a = cvt_fp8x8(kraw[j & 1][2 * u], kraw[j & 1][2 * u + 1]);
         if (u == 1 && j + 2 < kKS / 2) kraw[j & 1] = k8_load(ks, j + 2);
@@ -673,7 +694,18 @@ void attn_ws_kernel(DecodeParams p) {
       const int n = min(ntiles - tile0, Uw - t);
       const int row = rb * kWsRows + rg * 32 + tok;
       const bool row_ok = row < p.rows;
-      {
+      if constexpr (kQ8) {
+        const long long qn = (long long)b * p.rows + (row_ok ? row : 0);
+        const uint8_t* qrow8 = p.q8 + qn * p.q8_stride + 16 * hi;
+#pragma unroll
+        for (int j = 0; j < 5; ++j) {
+          const u32x4_t x0 = *(const u32x4_t*)(qrow8 + 32 * (j < 4 ? 4 * j + ds : 16 + ds));
+          const u32x4_t x1 = j < 4 ? *(const u32x4_t*)(qrow8 + 32 * (4 * j + 2 + ds)) : u32x4_t{};
+          const i32x8_t x = {(int32_t)x0[0], (int32_t)x0[1], (int32_t)x0[2], (int32_t)x0[3],
+                             (int32_t)x1[0], (int32_t)x1[1], (int32_t)x1[2], (int32_t)x1[3]};
+          q8reg[j] = row_ok ? x : i32x8_t{};
+        }
+      } else {
         const long long qn = (long long)b * p.rows + (row_ok ? row : 0);
         const uint16_t* qrow = p.q + qn * p.q_stride;
         const uint16_t* rrow = p.q_rope + qn * p.q_rope_stride - 512;
@@ -1065,7 +1097,11 @@ hipError_t launch_decode_stream(const DecodeParams& p, bool run_plan, hipEvent_t
   const bool local = p.local_kv_indices != nullptr;
   const bool fold = p.fold > 1;
   if (fold && local) return hipErrorInvalidValue;
-  if (p.kv_fp8)
+  if (p.kv_fp8 && p.q8 != nullptr)
+    fn = fold    ? reinterpret_cast<const void*>(&attn_ws_kernel<false, true, true, true>)
+         : local ? reinterpret_cast<const void*>(&attn_ws_kernel<true, true, false, true>)
+                 : reinterpret_cast<const void*>(&attn_ws_kernel<false, true, false, true>);
+  else if (p.kv_fp8)
     fn = fold    ? reinterpret_cast<const void*>(&attn_ws_kernel<false, true, true>)
          : local ? reinterpret_cast<const void*>(&attn_ws_kernel<true, true, false>)
                  : reinterpret_cast<const void*>(&attn_ws_kernel<false, true, false>);

@@ -42,6 +42,10 @@ class DeviceWorkload:
     block_table: torch.Tensor  # [B, max_pages] i32
     seq_lens: torch.Tensor     # [B] i32
     q_lens: Optional[torch.Tensor] = None   # [B] i32 decode depth per request, or None
+    # e4m3 query codes [B, q_len, H, 576] and their scale (fp8 KV only): the
+    # decode reads these instead of the bf16 query when q_scale > 0
+    q8: Optional[torch.Tensor] = None
+    q_scale: float = 0.0
 
     @staticmethod
     def upload(wl, device="cuda", out_dtype: Optional[str] = None) -> "DeviceWorkload":
@@ -59,7 +63,22 @@ class DeviceWorkload:
             block_table=torch.from_numpy(np.ascontiguousarray(wl.block_table)).to(device),
             seq_lens=torch.from_numpy(np.ascontiguousarray(wl.seq_lens)).to(device),
             q_lens=(torch.from_numpy(np.ascontiguousarray(wl.q_lens)).to(device)
-                    if getattr(wl, "q_lens", None) is not None else None))
+                    if getattr(wl, "q_lens", None) is not None else None),
+            q8=(torch.from_numpy(np.ascontiguousarray(wl.q_codes)).to(device)
+                if getattr(wl, "q_codes", None) is not None else None),
+            q_scale=float(getattr(wl, "q_scale", 0.0)) if getattr(wl, "q_codes", None) is not None else 0.0)
+
+    def quantize_query(self, q_scale: float, stream=None) -> None:
+        """The e4m3 codes of the bf16 query on device (the concat-and-quantise
+        prep of the fp8 KV path); later decode calls read them."""
+        if self.q8 is None:
+            self.q8 = torch.empty(self.q.shape, dtype=torch.uint8, device=self.q.device)
+        L.mla_quantize_q(self.q, self.q8, q_scale, stream=stream)
+        self.q_scale = float(q_scale)
+
+    def query(self):
+        """(query tensor, q_scale) the decode calls pass."""
+        return (self.q8, self.q_scale) if self.q_scale > 0 else (self.q, 0.0)
 
     def local_max(self, shard: int) -> int:
         return L.mla_shard_local_max(self.max_seq_len, shard, self.shards)
@@ -109,24 +128,27 @@ def _workspace(bufs: StepBuffers, shard: int):
 def run_plan(dw: DeviceWorkload, bufs: StepBuffers, shard: int, use_metadata: bool = False,
              split_target: int = 0, stream=None) -> None:
     """The shard's work schedule into its workspace (once per decode step)."""
+    q, q_scale = dw.query()
     L.mla_decode_plan(
-        dw.q, dw.kv_pages, dw.block_table, dw.seq_lens, shard, dw.shards, dw.q_len,
+        q, dw.kv_pages, dw.block_table, dw.seq_lens, shard, dw.shards, dw.q_len,
         bufs.outs[shard], bufs.lses[shard], _workspace(bufs, shard), kv_scale=dw.kv_scale,
         softmax_scale=dw.softmax_scale, lse_base=dw.lse_base,
         local_seq_lens=bufs.local_seq_lens[shard] if use_metadata else None,
         local_kv_indices=bufs.local_kv_indices[shard] if use_metadata else None,
-        split_target=split_target, stream=stream)
+        split_target=split_target, q_scale=q_scale, stream=stream)
 
 
 def run_partial(dw: DeviceWorkload, bufs: StepBuffers, shard: int, use_metadata: bool = False,
                 split_target: int = 0, events=None, reuse_plan: bool = False, stream=None) -> int:
+    q, q_scale = dw.query()
     return L.mla_decode_partial(
-        dw.q, dw.kv_pages, dw.block_table, dw.seq_lens, shard, dw.shards, dw.q_len,
+        q, dw.kv_pages, dw.block_table, dw.seq_lens, shard, dw.shards, dw.q_len,
         bufs.outs[shard], bufs.lses[shard], _workspace(bufs, shard), kv_scale=dw.kv_scale,
         softmax_scale=dw.softmax_scale, lse_base=dw.lse_base,
         local_seq_lens=bufs.local_seq_lens[shard] if use_metadata else None,
         local_kv_indices=bufs.local_kv_indices[shard] if use_metadata else None,
-        split_target=split_target, events=events, reuse_plan=reuse_plan, q_lens=dw.q_lens, stream=stream)
+        split_target=split_target, events=events, reuse_plan=reuse_plan, q_lens=dw.q_lens, q_scale=q_scale,
+        stream=stream)
 
 
 def run_merge(dw: DeviceWorkload, bufs: StepBuffers, out_base: int = L.LSE_BASE_E, stream=None,
@@ -179,7 +201,8 @@ def run_all_shards(dw: DeviceWorkload, bufs: StepBuffers, out_base: int = L.LSE_
                    events=None, reuse_plan: bool = False, stream=None) -> int:
     """Every shard in one launch with the merge fused, into bufs.out / bufs.lse."""
     ws = all_shards_workspace(dw, bufs)
-    return L.mla_decode_all_shards(dw.q, dw.kv_pages, dw.block_table, dw.seq_lens, dw.shards, dw.q_len,
+    q, q_scale = dw.query()
+    return L.mla_decode_all_shards(q, dw.kv_pages, dw.block_table, dw.seq_lens, dw.shards, dw.q_len,
                                    bufs.out, bufs.lse, ws, kv_scale=dw.kv_scale, softmax_scale=dw.softmax_scale,
                                    lse_base=out_base, split_target=split_target, events=events,
-                                   reuse_plan=reuse_plan, q_lens=dw.q_lens, stream=stream)
+                                   reuse_plan=reuse_plan, q_lens=dw.q_lens, q_scale=q_scale, stream=stream)

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 7
+#define MLA_ABI_VERSION 8
 #define MLA_PAGE_SIZE 64
 #define MLA_D_QK 576
 #define MLA_D_V 512
@@ -190,6 +190,19 @@ typedef struct mla_decode_args {
   const void* q_rope;            /* [rows] x 64 bf16 at q_rope_row_stride, or NULL */
   int64_t q_row_stride;
   int64_t q_rope_row_stride;
+  /* query as e4m3 codes ([DCP decode] 实现拆解 step 3: with an fp8 KV pool
+   * the query is prepared by a fused concat-and-quantise, mla_quantize_q).
+   * 0: `q` is the bf16 query above (exact, the default). > 0 and finite:
+   * `q` holds [rows][576] e4m3 codes (row n at byte n * q_row_stride,
+   * q_row_stride = 0 meaning 576, a multiple of 16), the query value being
+   * code x q_scale; q_rope must be NULL and kv_dtype FP8_E4M3. The scores
+   * then run on the fp8 matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4:
+   * code x code, accumulated in fp32); P V stays bf16. Results match the
+   * oracle's decode of the same codes; against the bf16 query they carry the
+   * query's quantisation error (measured: 2e-2 in LSE, 5e-2 in out on the
+   * 16-32K-token deepseek-like workload; several times that on contexts of a
+   * few hundred tokens, where the softmax is sharper). */
+  float q_scale;
 } mla_decode_args_t;
 
 /* Bytes of workspace mla_decode_partial needs for these sizes (host only,
@@ -359,6 +372,28 @@ typedef struct mla_append_args {
 } mla_append_args_t;
 
 mla_status_t mla_append_kv(const mla_append_args_t* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Query concat-and-quantise ([DCP decode] 实现拆解 step 3: with an fp8 KV
+ * pool the decode's query is prepared by one fused pass that puts the 512
+ * latent dims and the 64 rope dims of each row side by side and quantises
+ * them to fp8). Writes the e4m3 codes of `rows` query rows:
+ * out[n][d] = nearest e4m3 value to the fp32 quotient q[n][d] / q_scale,
+ * ties to the even code, magnitudes above 448 (and infinities) saturating
+ * to +-448, NaN giving the NaN code with the input's sign (the rule of the
+ * fp8 KV rows in mla_append_kv).
+ * q: bf16 (device); row n's dims 0..511 at element n * q_row_stride, dims
+ * 512..575 following them when q_rope is NULL, else at element
+ * n * q_rope_row_stride of q_rope (bf16, device). Strides are in elements,
+ * multiples of 8 (0 = 576, 512 with q_rope; 0 = 64 for q_rope); q and
+ * q_rope 16-byte aligned. out: [rows][576] uint8 (device, contiguous,
+ * 16-byte aligned; the `q` of an mla_decode_args_t with q_scale > 0).
+ * Errors: INVALID_ARGUMENT for null q / out (rows > 0), rows < 0, a stride
+ * or alignment outside the above, q_scale not finite and > 0;
+ * DEVICE_ERROR if the launch fails.
+ * ---------------------------------------------------------------------- */
+mla_status_t mla_quantize_q(const void* q, const void* q_rope, int64_t q_row_stride, int64_t q_rope_row_stride,
+                            int64_t rows, float q_scale, void* out, void* stream);
 
 /* ------------------------------------------------------------------------
  * Introspection.

@@ -39,7 +39,7 @@ def test_struct_layouts_and_version(lib):
     assert lib.mla_sizeof_decode_args() == ctypes.sizeof(L.DecodeArgs)
     assert lib.mla_sizeof_merge_args() == ctypes.sizeof(L.MergeArgs)
     assert lib.mla_sizeof_append_args() == ctypes.sizeof(L.AppendArgs)
-    assert lib.mla_abi_version() == 7
+    assert lib.mla_abi_version() == 8
     assert lib.mla_status_string(L.STATUS_INVALID_ARGUMENT) == b"invalid argument"
 
 
@@ -209,3 +209,51 @@ def test_append_empty_batch_and_bf16_scale_are_ok_without_device(lib):
     assert lib.mla_append_kv(ctypes.byref(a), None) == L.STATUS_OK
     a.kv_dtype, a.kv_scale = L.DTYPE_BF16, 0.0          # the scale is not used for a bf16 pool
     assert lib.mla_append_kv(ctypes.byref(a), None) == L.STATUS_OK
+
+
+@pytest.mark.parametrize("fields", [
+    dict(q_scale=-1.0),                                     # negative
+    dict(q_scale=float("nan")),
+    dict(q_scale=float("inf")),
+    dict(q_scale=0.5),                                      # e4m3 query with a bf16 pool
+    dict(q_scale=0.5, kv_dtype=L.DTYPE_FP8_E4M3, q_rope=0x2000),       # codes hold all 576 dims
+    dict(q_scale=0.5, kv_dtype=L.DTYPE_FP8_E4M3, q_row_stride=584),    # not a multiple of 16
+    dict(q_scale=0.5, kv_dtype=L.DTYPE_FP8_E4M3, q_row_stride=560),    # below 576
+    dict(q_scale=0.5, kv_dtype=L.DTYPE_FP8_E4M3, q=0x1008),            # not 16-byte aligned
+])
+def test_e4m3_query_argument_errors(lib, fields):
+    for fn in (lib.mla_decode_partial, lib.mla_decode_all_shards):
+        a = _valid_args()
+        a.workspace_bytes = 1 << 40
+        for k, v in fields.items():
+            setattr(a, k, v)
+        assert fn(ctypes.byref(a), None, None) == L.STATUS_INVALID_ARGUMENT, fields
+        assert "q" in lib.mla_last_error().decode()
+
+
+def test_e4m3_query_empty_batch_is_ok_without_device(lib):
+    a = _valid_args()
+    a.batch, a.kv_dtype, a.q_scale, a.q_row_stride = 0, L.DTYPE_FP8_E4M3, 0.25, 592
+    assert lib.mla_decode_partial(ctypes.byref(a), None, None) == L.STATUS_OK
+
+
+@pytest.mark.parametrize("args,ok", [
+    ((0x1000, None, 0, 0, 0, 1.0, 0x2000), True),           # no rows: nothing to run
+    ((0x1000, None, 0, 0, -1, 1.0, 0x2000), False),         # rows < 0
+    ((0x1000, None, 0, 0, 4, 0.0, 0x2000), False),          # scale 0
+    ((0x1000, None, 0, 0, 4, float("nan"), 0x2000), False),
+    ((0x1000, None, 0, 0, 4, float("inf"), 0x2000), False),
+    ((None, None, 0, 0, 4, 1.0, 0x2000), False),            # null q
+    ((0x1000, None, 0, 0, 4, 1.0, None), False),            # null out
+    ((0x1000, None, 572, 0, 4, 1.0, 0x2000), False),        # stride below 576
+    ((0x1000, None, 580, 0, 4, 1.0, 0x2000), False),        # stride not a multiple of 8
+    ((0x1000, 0x3000, 504, 0, 4, 1.0, 0x2000), False),      # latent stride below 512
+    ((0x1000, 0x3000, 512, 60, 4, 1.0, 0x2000), False),     # rope stride below 64
+    ((0x1004, None, 0, 0, 4, 1.0, 0x2000), False),          # q not 16-byte aligned
+    ((0x1000, None, 0, 0, 4, 1.0, 0x2008), False),          # out not 16-byte aligned
+])
+def test_quantize_q_argument_errors(lib, args, ok):
+    st = lib.mla_quantize_q(*args, None)
+    assert (st == L.STATUS_OK) == ok, (args, lib.mla_last_error())
+    if not ok:
+        assert st == L.STATUS_INVALID_ARGUMENT and lib.mla_last_error()

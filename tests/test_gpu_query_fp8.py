@@ -1,0 +1,164 @@
+"""GPU checks of the e4m3 query path ([DCP decode] 实现拆解 step 3: with an fp8
+KV pool the query is prepared by a fused concat-and-quantise, and the
+scores run on the fp8 matrix cores).
+
+* mla_quantize_q is bit-exact against the oracle's codes on every bf16
+  pattern (NaN, infinities, subnormals, saturation), for a contiguous query
+  and for its latent and rope parts given as two strided views;
+* the decode from e4m3 query codes against the oracle's decode of the same
+  codes: every shard through both gathers with the segments whole or cut,
+  the merged step, the single launch of every shard, q_len 4 with a
+  per-request depth, and inputs that force the online-softmax rescale, at
+  the fp8-KV bar (6e-2);
+* codes made on the device and on the host give bit-identical decodes.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as U
+import rescale_util as R
+from oracle import mla_oracle as O
+from workloads import make_config
+
+pytestmark = pytest.mark.gpu
+
+if U.gpu_available():
+    from decode_attention_paged_amd import _lib as L
+    from decode_attention_paged_amd import step as ST
+
+SMALL_FP8 = dict(batch=2, lens=("uniform", 700, 1500))
+
+
+def _flush(msg):
+    print(msg, flush=True)
+
+
+def _with_codes(wl, q_scale):
+    return dataclasses.replace(wl, q_codes=O.quantize_query(wl.q, q_scale), q_scale=q_scale)
+
+
+@pytest.mark.parametrize("q_scale", [1.0, 0.37, 2.0 ** -4])
+def test_quantize_q_bit_exact_on_every_bf16_pattern(q_scale):
+    _flush(f"quantize_q every pattern, scale {q_scale}")
+    rows = -(-65536 // 576)
+    flat = np.resize(np.arange(65536, dtype=np.uint32).astype(np.uint16), rows * 576)
+    q_bits = flat.reshape(1, 1, rows, 576)
+    q = torch.from_numpy(q_bits.copy()).view(torch.bfloat16).cuda()
+    out = torch.full(q.shape, 0xA5, dtype=torch.uint8, device="cuda")
+    L.mla_quantize_q(q, out, q_scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), O.quantize_query(q_bits, q_scale))
+
+
+def test_quantize_q_from_split_views():
+    _flush("quantize_q split views")
+    rng = np.random.default_rng(71)
+    B, ql, H, W = 3, 2, 16, 640
+    vals = (rng.standard_normal((B, ql, H, W)) * 40.0).astype(np.float32)
+    buf_bits = (vals.view(np.uint32) >> 16).astype(np.uint16)
+    buf = torch.from_numpy(buf_bits.copy()).view(torch.bfloat16).cuda()
+    q_nope, q_rope = buf[..., :512], buf[..., 576:640]
+    out = torch.empty((B, ql, H, 576), dtype=torch.uint8, device="cuda")
+    L.mla_quantize_q(q_nope, out, 0.75, q_rope=q_rope)
+    torch.cuda.synchronize()
+    ref = O.quantize_query(np.concatenate([buf_bits[..., :512], buf_bits[..., 576:640]], axis=-1), 0.75)
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("split_target", [0, 1, 37])
+@pytest.mark.parametrize("use_metadata", [True, False])
+def test_e4m3_query_partials_and_merge(use_metadata, split_target):
+    wl = _with_codes(make_config(3, **SMALL_FP8), 0.5)
+    dw = ST.DeviceWorkload.upload(wl)
+    assert dw.q8 is not None and dw.q_scale == 0.5
+    bufs = ST.StepBuffers(dw)
+    bufs.fill_nan()
+    tol = U.TOL["fp8"]
+    refs = [O.decode_partial(wl, r, wl.shards, wl.lse_base) for r in range(wl.shards)]
+    for r in range(wl.shards):
+        _flush(f"e4m3 query meta={use_metadata} split={split_target} shard {r}/{wl.shards}")
+        if use_metadata:
+            ST.run_metadata(dw, bufs, r)
+        ST.run_partial(dw, bufs, r, use_metadata=use_metadata, split_target=split_target)
+        torch.cuda.synchronize()
+        U.assert_partial_close(bufs.outs[r], bufs.lses[r], refs[r][0], refs[r][1], wl.lse_base, tol,
+                               f"e4m3 query shard {r}")
+    ST.run_merge(dw, bufs)
+    torch.cuda.synchronize()
+    mo, ml = O.merge([p[0] for p in refs], [p[1] for p in refs], [wl.lse_base] * wl.shards)
+    U.assert_partial_close(bufs.out, bufs.lse, mo, ml, "e", tol, "e4m3 query merged")
+
+
+@pytest.mark.parametrize("split_target", [0, 16])
+def test_e4m3_query_single_launch(split_target):
+    _flush(f"e4m3 query single launch split={split_target}")
+    wl = _with_codes(make_config(3, **SMALL_FP8), 0.5)
+    dw = ST.DeviceWorkload.upload(wl)
+    bufs = ST.StepBuffers(dw)
+    bufs.fill_nan()
+    ST.run_all_shards(dw, bufs, split_target=split_target)
+    torch.cuda.synchronize()
+    ro, rl, _ = O.decode_step(wl)
+    U.assert_partial_close(bufs.out, bufs.lse, ro, rl, "e", U.TOL["fp8"], "e4m3 query single launch")
+
+
+def test_e4m3_query_draft_rows_with_depths():
+    _flush("e4m3 query q_len 4, per-request depth")
+    wl = _with_codes(make_config(4, kv_dtype="fp8", shards=2, batch=3, lens=("uniform", 100, 400),
+                                 var_q=True), 0.25)
+    dw = ST.DeviceWorkload.upload(wl)
+    bufs = ST.StepBuffers(dw)
+    bufs.fill_nan()
+    for r in range(wl.shards):
+        ST.run_partial(dw, bufs, r)
+        torch.cuda.synchronize()
+        ro, rl = O.decode_partial(wl, r, wl.shards, wl.lse_base)
+        U.assert_partial_close(bufs.outs[r], bufs.lses[r], ro, rl, wl.lse_base, U.TOL["fp8"],
+                               f"e4m3 query q4 shard {r}")
+    bufs.fill_nan()
+    ST.run_all_shards(dw, bufs)
+    torch.cuda.synchronize()
+    ro, rl, _ = O.decode_step(wl)
+    U.assert_partial_close(bufs.out, bufs.lse, ro, rl, "e", U.TOL["fp8"], "e4m3 query q4 single launch")
+
+
+@pytest.mark.parametrize("split_target", [0, 7])
+@pytest.mark.parametrize("name", sorted(n for n in R.SPECS if n.startswith("fp8")))
+def test_e4m3_query_forced_rescale(name, split_target):
+    _flush(f"e4m3 query rescale {name} split={split_target}")
+    wl = _with_codes(R.rising_workload(name), 0.5)
+    dw = ST.DeviceWorkload.upload(wl)
+    bufs = ST.StepBuffers(dw)
+    bufs.fill_nan()
+    refs = [O.decode_partial(wl, r, wl.shards, wl.lse_base) for r in range(wl.shards)]
+    for r in range(wl.shards):
+        ST.run_partial(dw, bufs, r, split_target=split_target)
+        torch.cuda.synchronize()
+        U.assert_partial_close(bufs.outs[r], bufs.lses[r], refs[r][0], refs[r][1], wl.lse_base, U.TOL["fp8"],
+                               f"e4m3 query rescale {name} shard {r}")
+    bufs.fill_nan()
+    ST.run_all_shards(dw, bufs, split_target=split_target)
+    torch.cuda.synchronize()
+    mo, ml = O.merge([p[0] for p in refs], [p[1] for p in refs], [wl.lse_base] * wl.shards)
+    U.assert_partial_close(bufs.out, bufs.lse, mo, ml, "e", U.TOL["fp8"], f"e4m3 query rescale {name} single")
+
+
+def test_device_and_host_codes_decode_identically():
+    _flush("e4m3 query device vs host codes")
+    wl = make_config(3, **SMALL_FP8)
+    dw_dev = ST.DeviceWorkload.upload(wl)
+    dw_dev.quantize_query(0.5)
+    torch.cuda.synchronize()
+    assert np.array_equal(dw_dev.q8.cpu().numpy(), O.quantize_query(wl.q, 0.5))
+    dw_host = ST.DeviceWorkload.upload(_with_codes(wl, 0.5))
+    a, b = ST.StepBuffers(dw_dev), ST.StepBuffers(dw_host)
+    a.fill_nan()
+    b.fill_nan()
+    ST.run_step(dw_dev, a)
+    ST.run_step(dw_host, b)
+    torch.cuda.synchronize()
+    for x, y in [(a.out, b.out), (a.lse, b.lse)] + list(zip(a.outs, b.outs)) + list(zip(a.lses, b.lses)):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
