@@ -30,24 +30,22 @@ constexpr int kNopeChunks = 512 / 8;   // 64 of them from k_nope
 // (bias 7) and 3 mantissa bits, subnormals at exponent field 0, no
 // infinities, S.1111.111 = NaN, largest finite 448. Round to nearest, ties
 // to even; magnitudes above 448 (infinities too) saturate to 448.
+// Every case is computed and the result selected (no branches: the lanes
+// of a wave hold values of every kind).
 __device__ __forceinline__ uint32_t e4m3_code(float y) {
   const uint32_t u = __float_as_uint(y);
   const uint32_t sign = (u >> 24) & 0x80u;
   const uint32_t mag = u & 0x7FFFFFFFu;
-  if (mag > 0x7F800000u) return sign | 0x7Fu;              // NaN
-  if (mag >= 0x43E00000u) return sign | 0x7Eu;             // >= 448 (incl. inf)
-  uint32_t code;
-  if (mag >= 0x3C800000u) {                                // >= 2^-6: normal
-    // keep 3 of the 23 mantissa bits, round the other 20 to nearest even,
-    // then move the exponent bias from 127 to 7
-    const uint32_t r = (mag + 0x7FFFFu + ((mag >> 20) & 1u)) >> 20;
-    code = r - (120u << 3);
-    code = code > 0x7Eu ? 0x7Eu : code;
-  } else {
-    // subnormal: value k * 2^-9, k = |y| * 512 rounded to nearest even
-    // (k = 8 is the smallest normal, code 0x08)
-    code = (uint32_t)__builtin_rintf(__uint_as_float(mag) * 512.0f);
-  }
+  // normal (>= 2^-6): keep 3 of the 23 mantissa bits, round the other 20 to
+  // nearest even, then move the exponent bias from 127 to 7
+  const uint32_t r = (mag + 0x7FFFFu + ((mag >> 20) & 1u)) >> 20;
+  const uint32_t normal = min(r - (120u << 3), 0x7Eu);
+  // subnormal: value k * 2^-9, k = |y| * 512 rounded to nearest even (k = 8
+  // is the smallest normal, code 0x08)
+  const uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(mag) * 512.0f);
+  uint32_t code = mag >= 0x3C800000u ? normal : sub;
+  code = mag >= 0x43E00000u ? 0x7Eu : code;                // >= 448 (incl. inf)
+  code = mag > 0x7F800000u ? 0x7Fu : code;                 // NaN
   return sign | code;
 }
 
@@ -59,8 +57,8 @@ __device__ __forceinline__ u32x2_t quantize8(const u32x4_t x, float scale) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const uint32_t bits = (x[e >> 1] >> (16 * (e & 1))) << 16;   // bf16 -> f32, exact
-    const uint32_t code = (bits & 0x7FFFFFFFu) > 0x7F800000u ? (((bits >> 24) & 0x80u) | 0x7Fu)
-                                                             : e4m3_code(__uint_as_float(bits) / scale);
+    const uint32_t q = e4m3_code(__uint_as_float(bits) / scale);   // both cases computed, then selected
+    const uint32_t code = (bits & 0x7FFFFFFFu) > 0x7F800000u ? (((bits >> 24) & 0x80u) | 0x7Fu) : q;
     w[e >> 2] |= code << (8 * (e & 3));
   }
   return u32x2_t{w[0], w[1]};
