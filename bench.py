@@ -31,6 +31,10 @@ Reported:
                 (the shard's KV rows + Q + partial out + LSE) / mean duration,
                 against 8 TB/s;
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload.
+
+The fp8-KV workload is also timed with its query quantised to e4m3 codes
+(mla_quantize_q, then the decode reads the codes): `e4m3_query` under its
+entry in `configs`, beside the bf16-query figures, which stay its main ones.
 """
 from __future__ import annotations
 
@@ -294,6 +298,8 @@ def bench_workload(index: int, steps: int, warmup: int, rotate: bool = True, spl
     )
     if split_target == 0:
         res["all_shards"] = bench_all_shards(wl, dws, bufs, steps, warmup, kv_bytes, flops, use_graph)
+        if wl.kv_dtype == "fp8":
+            res["e4m3_query"] = bench_e4m3_query(wl, dws, bufs, steps, warmup, kv_bytes, per_shard, use_graph)
     # the contraction runs on bf16 MFMAs for both KV types (fp8 pages are
     # converted to bf16 exactly, in registers), so its peak is the bf16 one
     peak_tf = BF16_PEAK_TFLOPS
@@ -365,6 +371,127 @@ def bench_all_shards(wl, dws, bufs, steps: int, warmup: int, kv_bytes: int, flop
     ms = 1e3 * (time.perf_counter() - t0) / steps
     del graphs
     return _all_shards_result(wl, kv_bytes, flops, ms, attn_ms, d_out, d_lse, "graph replay")
+
+
+QUANT_REPEAT = 8
+
+
+def bench_e4m3_query(wl, dws, bufs, steps: int, warmup: int, kv_bytes: int, per_shard, use_graph: bool = True):
+    """The fp8-KV step with the query quantised too: mla_quantize_q turns the
+    bf16 query into e4m3 codes (q_scale = max |q| / 448, one per step), then
+    every shard's partial decode reads the codes (scores on the fp8 matrix
+    cores) and the merge follows. Timed: the attention kernel per shard (HIP
+    events around its launch), the quantise kernel (events around it, queued
+    behind an attention launch so the host's launch latency falls outside,
+    QUANT_REPEAT launches back to back per pair of events, so the figure is
+    a launch's share of a back-to-back run),
+    the step (quantise + partials on concurrent streams + merge) and the
+    single launch of every shard (quantise + one call), both as graph
+    replays checked bit for bit against the eager call. Also reported: the
+    largest difference from the bf16-query step (the quantisation error)."""
+    import torch
+
+    from decode_attention_paged_amd import step as ST
+
+    for dw in dws:
+        dw.q_scale = 0.0
+    ST.run_step(dws[0], bufs)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = bufs.out.float().clone(), bufs.lse.clone()
+    q_scale = float(dws[0].q.float().abs().max().item()) / 448.0
+    log(f"[bench] {wl.name}: e4m3 query (q_scale {q_scale:.5f})")
+    for dw in dws:
+        dw.quantize_query(q_scale)
+    torch.cuda.synchronize()
+    try:
+        ST.run_step(dws[0], bufs)
+        torch.cuda.synchronize()
+        fin = torch.isfinite(ref_lse)
+        d_out = (bufs.out.float() - ref_out).abs().max().item()
+        d_lse = (bufs.lse[fin] - ref_lse[fin]).abs().max().item() if bool(fin.any()) else 0.0
+        S = wl.shards
+        ev = [[(HipEvent(), HipEvent()) for _ in range(S)] for _ in range(steps)]
+        qev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for k in range(warmup + steps):
+            dw = dws[k % len(dws)]
+            timed = k >= warmup
+            for r in range(S):
+                ST.run_partial(dw, bufs, r, reuse_plan=True, events=ev[k - warmup][r] if timed else None)
+            if timed:
+                qev[k - warmup][0].record()
+            for _ in range(QUANT_REPEAT):
+                dw.quantize_query(q_scale)
+            if timed:
+                qev[k - warmup][1].record()
+            ST.run_merge(dw, bufs)
+        torch.cuda.synchronize()
+        attn_us = 1e3 * statistics.mean(a.elapsed_ms(b) for row in ev for a, b in row)
+        quant_us = 1e3 * statistics.mean(a.elapsed_time(b) for a, b in qev) / QUANT_REPEAT
+        rows = wl.batch * wl.q_len * wl.heads
+        # algorithmic bytes per launch: the bf16-query figure less the query's
+        # halved size (576 code bytes per row instead of 1152)
+        launch_bytes = statistics.mean(b for b, _ in per_shard) - rows * 576
+        launch_flops = statistics.mean(f for _, f in per_shard)
+        quant_bytes = rows * 576 * 3
+        out = dict(q_scale=q_scale, attn_kernel_us_per_shard=attn_us,
+                   attn_kernel_bytes_per_launch=launch_bytes,
+                   attn_kernel_gbs=launch_bytes / (attn_us * 1e-6) / 1e9,
+                   attn_kernel_hbm_frac=launch_bytes / (attn_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                   attn_kernel_mfma_frac=launch_flops / (attn_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+                   quantize_us=quant_us, quantize_bytes=quant_bytes,
+                   quantize_gbs=quant_bytes / (quant_us * 1e-6) / 1e9,
+                   max_abs_diff_vs_bf16_query=dict(out=d_out, lse=d_lse))
+
+        def step_fn(dw, streams):
+            dw.quantize_query(q_scale)
+            ST.run_step_concurrent(dw, bufs, streams, reuse_plan=True)
+
+        def single_fn(dw, streams):
+            dw.quantize_query(q_scale)
+            ST.run_all_shards(dw, bufs, reuse_plan=True)
+
+        streams = [torch.cuda.Stream() for _ in range(S)]
+        for tag, fn in (("step", step_fn), ("all_shards_step", single_fn)):
+            for dw in dws:
+                fn(dw, streams)
+            torch.cuda.synchronize()
+            if use_graph:
+                graphs = []
+                for dw in dws:
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        fn(dw, streams)
+                    graphs.append(g)
+                torch.cuda.synchronize()
+                for i, dw in enumerate(dws):
+                    fn(dw, streams)
+                    torch.cuda.synchronize()
+                    eo, el = bufs.out.clone(), bufs.lse.clone()
+                    bufs.fill_nan()
+                    graphs[i].replay()
+                    torch.cuda.synchronize()
+                    if not (torch.equal(bufs.out.view(torch.uint8), eo.view(torch.uint8))
+                            and torch.equal(bufs.lse.view(torch.uint8), el.view(torch.uint8))):
+                        raise RuntimeError(f"graph replay of the e4m3-query {tag} differs from the eager call")
+                run = lambda k: graphs[k % len(graphs)].replay()   # noqa: E731
+            else:
+                run = lambda k: fn(dws[k % len(dws)], streams)    # noqa: E731
+            for k in range(warmup):
+                run(k)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for k in range(steps):
+                run(k)
+            torch.cuda.synchronize()
+            ms = 1e3 * (time.perf_counter() - t0) / steps
+            out[tag] = dict(ms_per_step=ms, kv_gbs=kv_bytes / (ms * 1e-3) / 1e9,
+                            timing="graph replay" if use_graph else "eager calls")
+            if use_graph:
+                del graphs
+        return out
+    finally:
+        for dw in dws:
+            dw.q_scale = 0.0
 
 
 def _all_shards_result(wl, kv_bytes, flops, ms, attn_ms, d_out, d_lse, timing):
@@ -576,6 +703,23 @@ def config_summary(r):
                                       algorithmic_bytes_per_launch=int(a["call_bytes"]),
                                       traffic=traffic_from_profile("all_shards_" + r["name"]),
                                       step_timing=a.get("step_timing", "graph replay"))
+    if "e4m3_query" in r:
+        e = r["e4m3_query"]
+        out["e4m3_query"] = dict(
+            q_scale=round(e["q_scale"], 6),
+            attn_kernel_us_per_shard=round(e["attn_kernel_us_per_shard"], 2),
+            attn_kernel=dict(bound="hbm", achieved=round(e["attn_kernel_gbs"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                             frac=round(e["attn_kernel_hbm_frac"], 4),
+                             algorithmic_bytes_per_launch=int(e["attn_kernel_bytes_per_launch"]),
+                             traffic=traffic_from_profile("e4m3_query_" + r["name"])),
+            quantize_kernel=dict(us=round(e["quantize_us"], 2), bytes=int(e["quantize_bytes"]),
+                                 gbs=round(e["quantize_gbs"], 1)),
+            step=dict(ms_per_step=round(e["step"]["ms_per_step"], 5), kv_gbs=round(e["step"]["kv_gbs"], 1),
+                      timing=e["step"]["timing"] + ", quantise + shard partials on concurrent streams + merge"),
+            all_shards_step=dict(ms_per_step=round(e["all_shards_step"]["ms_per_step"], 5),
+                                 kv_gbs=round(e["all_shards_step"]["kv_gbs"], 1),
+                                 timing=e["all_shards_step"]["timing"] + ", quantise + one call"),
+            max_abs_diff_vs_bf16_query={k: float(f"{v:.3e}") for k, v in e["max_abs_diff_vs_bf16_query"].items()})
     return out
 
 
@@ -656,6 +800,12 @@ def main() -> int:
             log(f"[bench] config {idx} {r['name']} single launch: {a['ms_per_step']:.3f} ms/step, "
                 f"{a['kv_gbs']:.0f} KV-GB/s, attn kernel {a['attn_kernel_us']:.1f} us "
                 f"({100 * a['attn_kernel_hbm_frac']:.1f}% HBM)")
+        if "e4m3_query" in r:
+            e = r["e4m3_query"]
+            log(f"[bench] config {idx} {r['name']} e4m3 query: step {e['step']['ms_per_step']:.3f} ms, single "
+                f"launch {e['all_shards_step']['ms_per_step']:.3f} ms, attn kernel "
+                f"{e['attn_kernel_us_per_shard']:.1f} us/shard, quantise {e['quantize_us']:.1f} us, "
+                f"vs bf16 query out {e['max_abs_diff_vs_bf16_query']['out']:.2e}")
 
     cpu = None if args.no_cpu else cpu_baseline(wl, args.cpu_seconds)
     mfma_bound = res["attn_kernel_mfma_frac"] > res["attn_kernel_hbm_frac"]
