@@ -149,14 +149,19 @@ __global__ __launch_bounds__(1024) void stream_plan_kernel(DecodeParams p) {
     p.req_cnt[q] = owned_count(p, b, p.fold > 1 ? ri : p.shard);
   }
   // tiles and costs (a super-segment costs its tiles plus kPieceCost for
-  // loading its queries) of this thread's super-segments, scanned over the block
+  // loading its queries) of this thread's super-segments, scanned over the
+  // block. When the launch runs every shard, a piece continues across the
+  // shards of its row block (their super-segments are neighbours), so only a
+  // row block's first shard pays the query cost; shard 0 owns token 0, so it
+  // has tiles whenever any shard of the request has
+  auto piece_cost = [&](int s) { return p.fold > 1 && s % p.fold != 0 ? 0 : kPieceCost; };
   int su = 0, sc = 0;
   for (int s = s0; s < s1; ++s) {
     const int cnt = sup_count(p, s);
     if (in_lds) s_cnt[s] = cnt;
     const int n = (cnt + kTile - 1) / kTile;
     su += n;
-    sc += n > 0 ? n + kPieceCost : 0;
+    sc += n > 0 ? n + piece_cost(s) : 0;
   }
   int2 tot;
   const int2 ex = block_excl_scan2(su, sc, s_wave, tot);
@@ -167,7 +172,7 @@ __global__ __launch_bounds__(1024) void stream_plan_kernel(DecodeParams p) {
       off[s] = u;
       coff[s] = c;
       u += n;
-      c += n > 0 ? n + kPieceCost : 0;
+      c += n > 0 ? n + piece_cost(s) : 0;
     }
   }
   const int U = tot.x, C = tot.y;
@@ -192,7 +197,7 @@ __global__ __launch_bounds__(1024) void stream_plan_kernel(DecodeParams p) {
     const long long x = (long long)g * C / NG;
     const int s = last_le(coff, nsup + 1, x);
     const int n = off[s + 1] - off[s];
-    long long k = x - coff[s] - kPieceCost;
+    long long k = x - coff[s] - piece_cost(s);
     k = k < 0 ? 0 : (k > n - 1 ? n - 1 : k);
     s_wgu[g] = off[s] + (int)k;
     p.wg_ustart[g] = off[s] + (int)k;
@@ -231,39 +236,51 @@ __global__ __launch_bounds__(1024) void stream_plan_kernel(DecodeParams p) {
   }
 
   // pieces of each segment (one per non-empty group its super-segment
-  // meets) and partial slots (only for segments cut into several pieces,
-  // unless the launch runs several shards: then every piece leaves a
-  // partial), allocated in segment order so that the shards of one row
-  // block have consecutive slots
-  const int np_slot = p.fold > 1 ? 1 : 2;
-  const int sper = (nseg + 1023) / 1024;
+  // meets) and partial slots (only for segments cut into several pieces),
+  // allocated in segment order. When the launch runs every shard, the
+  // pieces are those of the row block's run of S segments (one per group
+  // the run meets: a group's piece spans the run's shards it holds), every
+  // piece leaves a partial, and each segment of the run records the run's
+  // slots (thread ranges are whole runs)
+  const bool runs = p.fold > 1;
+  const int np_slot = runs ? 1 : 2;
+  int sper = (nseg + 1023) / 1024;
+  if (runs) sper = (sper + p.fold - 1) / p.fold * p.fold;
   const int q0 = min(tid * sper, nseg), q1 = min(q0 + sper, nseg);
   auto seg_pieces = [&](int s, int& first) {
-    int sp = s;
+    int o, e;
     if (GR > 1) {
       const int q = s / p.fold, ri = s - q * p.fold;
-      const int b = q / RB;
-      sp = b * p.fold + ri;
+      const int sp = (q / RB) * p.fold + ri;
+      o = off[runs ? sp - ri : sp];
+      e = off[runs ? sp - ri + p.fold : sp + 1];
+    } else {
+      const int r0 = runs ? s % p.fold : 0;
+      o = off[s - r0];
+      e = off[runs ? s - r0 + p.fold : s + 1];
     }
-    const int o = off[sp], n = off[sp + 1] - o;
     first = 0;
-    if (n <= 0) return 0;
+    if (e <= o) return 0;
     first = last_le(s_wgu, NG, o);
-    return last_le(s_wgu, NG, o + n - 1) - first + 1;
+    return last_le(s_wgu, NG, e - 1) - first + 1;
   };
   int ms = 0;
   for (int s = q0; s < q1; ++s) {
+    if (runs && s % p.fold != 0) continue;
     int first;
     const int np = seg_pieces(s, first);
     ms += np >= np_slot ? np : 0;
   }
   const int2 ex2 = block_excl_scan2(ms, 0, s_wave, tot);
-  int slot = ex2.x;
+  int slot = ex2.x, run_slot = slot;
   for (int s = q0; s < q1; ++s) {
     int first;
     const int np = seg_pieces(s, first);
-    p.seg_info[s] = make_int4(slot, np, first, 0);
-    slot += np >= np_slot ? np : 0;
+    if (!runs || s % p.fold == 0) {
+      run_slot = slot;
+      slot += np >= np_slot ? np : 0;
+    }
+    p.seg_info[s] = make_int4(run_slot, np, first, 0);
   }
 }
 
@@ -325,6 +342,29 @@ struct Cursor {
       ntiles = (cnt + kTile - 1) / kTile;
       if (ntiles > 0) break;
     }
+  }
+  // move n >= 1 units forward (they exist)
+  template <bool kFold>
+  __device__ __forceinline__ void advance_by(const DecodeParams& p, int n) {
+    for (;;) {
+      const int left = ntiles - 1 - tile;
+      if (n <= left) {
+        tile += n;
+        return;
+      }
+      n -= left + 1;
+      tile = ntiles - 1;
+      advance<kFold>(p);
+      if (n == 0) return;
+    }
+  }
+  // units from here to the end of the row block's run when the launch runs
+  // every shard (this segment's and the later shards' of the same request
+  // and row block)
+  __device__ __forceinline__ int run_units(const DecodeParams& p) const {
+    int n = ntiles - tile;
+    for (int q = r + 1; q < p.fold; ++q) n += (ld_const(p.req_cnt + b * p.fold + q) + kTile - 1) / kTile;
+    return n;
   }
 };
 
@@ -691,7 +731,10 @@ void attn_ws_kernel(DecodeParams p) {
     int t = 0;
     while (t < Uw) {
       const int b = cc.b, rb = cc.rb, tile0 = cc.tile, ntiles = cc.ntiles, cnt = cc.cnt, sh = cc.r, seg = cc.seg;
-      const int n = min(ntiles - tile0, Uw - t);
+      // a piece: the rest of the segment, or, when the launch runs every
+      // shard, the rest of the row block's run over its shards (the online
+      // softmax simply continues over the next shard's tokens)
+      const int n = min(kFold ? cc.run_units(p) : ntiles - tile0, Uw - t);
       const int row = rb * kWsRows + rg * 32 + tok;
       const bool row_ok = row < p.rows;
       if constexpr (kQ8) {
@@ -722,22 +765,36 @@ void attn_ws_kernel(DecodeParams p) {
       wait_vmcnt<0>();
       // owned tokens row (draft i) may see: t = j S + r <= L - q_b + i, with
       // q_b the request's decode depth (rows i >= q_b are padding: none)
-      int jvis = 0;
-      {
-        int L = ld_const(p.seq_lens + b);
-        L = L < 0 ? 0 : min(L, p.max_pages * kPage);
-        int qb = p.q_len;
-        if (p.q_lens != nullptr) {
-          qb = ld_const(p.q_lens + b);
-          qb = qb < 0 ? 0 : (qb > p.q_len ? p.q_len : qb);
-        }
-        const int i = (row >= p.heads) + (row >= 2 * p.heads) + (row >= 3 * p.heads);
-        for (int k = 0; k < p.q_len; ++k) {
-          const int lim = L - qb + k - sh;
-          const int jl = lim >= 0 ? min(cnt, lim / p.num_shards + 1) : 0;
-          jvis = i == k && k < qb ? jl : jvis;
-        }
+      int L = ld_const(p.seq_lens + b);
+      L = L < 0 ? 0 : min(L, p.max_pages * kPage);
+      int qb = p.q_len;
+      if (p.q_lens != nullptr) {
+        qb = ld_const(p.q_lens + b);
+        qb = qb < 0 ? 0 : (qb > p.q_len ? p.q_len : qb);
       }
+      const int di = (row >= p.heads) + (row >= 2 * p.heads) + (row >= 3 * p.heads);
+      auto jvis_of = [&](int shv, int cntv) {
+        int jv = 0;
+        for (int k = 0; k < p.q_len; ++k) {
+          const int lim = L - qb + k - shv;
+          const int jl = lim >= 0 ? min(cntv, lim / p.num_shards + 1) : 0;
+          jv = di == k && k < qb ? jl : jv;
+        }
+        return jv;
+      };
+      const int jvis = jvis_of(sh, cnt);
+      // kFold: the visibility limit of each tile of the piece, from a cursor
+      // over its tiles (the shard changes within a piece)
+      Cursor cs = cc;
+      int jv_sh = sh, jv_cur = jvis, limk = 0;
+      auto next_lim = [&](int k) {
+        if (cs.r != jv_sh) {
+          jv_sh = cs.r;
+          jv_cur = jvis_of(cs.r, cs.cnt);
+        }
+        limk = jv_cur - cs.tile * kTile;
+        if (k + 1 < n) cs.template advance<kFold>(p);
+      };
       float m_ref = kNegInf, l_sum = 0.f;
       // online softmax of a tile in base 2 (lane: one row, 16 tokens; value
       // v is token 8 (v >> 2) + 4 hi + (v & 3)); tokens at or past the row's
@@ -748,7 +805,7 @@ void attn_ws_kernel(DecodeParams p) {
       int lim = 0;
       auto softmax_chunk = [&](int c, int k, f32x16_t& sc, bf16x8_t (&pb)[2]) {
         if (c == 0) {
-          lim = jvis - (tile0 + k) * kTile - 4 * hi;
+          lim = (kFold ? limk : jvis - (tile0 + k) * kTile) - 4 * hi;
           tmax = kNegInf;
         }
         if (c < 2) {
@@ -768,14 +825,27 @@ void attn_ws_kernel(DecodeParams p) {
           neg_m = m_ref == kNegInf ? 0.f : -m_ref;
         }
         if (c >= 2) {
+          // pairs of probabilities rounded to bf16 together; the row sum
+          // adds the rounded pair (v_dot2c_f32_bf16 with {1, 1}), i.e. the
+          // values the P V product takes, so the output is an exact weighted
+          // mean of V rows. Against the unrounded sum this halves the largest
+          // error on short contexts, where outputs are as large as single V
+          // rows (a CPU model of this arithmetic on the skewed workload's
+          // shortest requests: ~0.019 -> ~0.011), and it is one instruction
+          // per pair instead of two additions
           constexpr int kE = kChunks - 2;
-          const int v0 = (c - 2) * 16 / kE, v1 = (c - 1) * 16 / kE;
+          typedef float f32x2_t __attribute__((ext_vector_type(2)));
+          typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+          const int v0 = 2 * ((c - 2) * 8 / kE), v1 = 2 * ((c - 1) * 8 / kE);
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
+          for (int v = 0; v < 16; v += 2) {
             if (v >= v0 && v < v1) {
-              const float pr = exp2_fast(__builtin_fmaf(sc[v], p.scale_log2, neg_m));
-              l_sum += pr;
-              pb[v >> 3][v & 7] = (__bf16)pr;
+              const f32x2_t pr = {exp2_fast(__builtin_fmaf(sc[v], p.scale_log2, neg_m)),
+                                  exp2_fast(__builtin_fmaf(sc[v + 1], p.scale_log2, neg_m))};
+              const bf16x2v_t pk = __builtin_convertvector(pr, bf16x2v_t);
+              l_sum = __builtin_amdgcn_fdot2_f32_bf16(pk, bf16x2v_t{(__bf16)1.f, (__bf16)1.f}, l_sum, false);
+              pb[v >> 3][v & 7] = pk[0];
+              pb[v >> 3][(v & 7) + 1] = pk[1];
             }
           }
         }
@@ -818,6 +888,7 @@ void attn_ws_kernel(DecodeParams p) {
         const uint8_t* ksq = smem + kStageB * ((t + k + 1) & (kNS - 1));
         qk_start(ksq);
         if (ds == 0) {
+          if constexpr (kFold) next_lim(k);
           bf16x8_t pb[2];
 #pragma unroll
           for (int i = 0; i < kKS; ++i) {
@@ -839,6 +910,7 @@ void attn_ws_kernel(DecodeParams p) {
       // place when this workgroup holds the whole segment of a one-shard launch)
       const bool single = !kFold && tile0 == 0 && n == ntiles;
       if (ds == 0) {
+        if constexpr (kFold) next_lim(n - 1);
         bf16x8_t pb[2];
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) softmax_chunk(c, n - 1, s_cur, pb);
@@ -860,8 +932,12 @@ void attn_ws_kernel(DecodeParams p) {
       __syncthreads();   // every output wave is done with the stages
       t += n;
       if (t < Uw) {
-        cc.tile = ntiles - 1;
-        cc.template advance<kFold>(p);
+        if constexpr (kFold) {
+          cc.template advance_by<kFold>(p, n);
+        } else {
+          cc.tile = ntiles - 1;
+          cc.template advance<kFold>(p);
+        }
       }
     }
     wait_vmcnt<0>();
@@ -980,7 +1056,7 @@ void attn_ws_kernel(DecodeParams p) {
     int t = 0;
     while (t < Uw) {
       const int b = cc.b, rb = cc.rb, tile0 = cc.tile, ntiles = cc.ntiles, seg = cc.seg;
-      const int n = min(ntiles - tile0, Uw - t);
+      const int n = min(kFold ? cc.run_units(p) : ntiles - tile0, Uw - t);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -1066,8 +1142,12 @@ void attn_ws_kernel(DecodeParams p) {
       }
       t += n;
       if (t < Uw) {
-        cc.tile = ntiles - 1;
-        cc.template advance<kFold>(p);
+        if constexpr (kFold) {
+          cc.template advance_by<kFold>(p, n);
+        } else {
+          cc.tile = ntiles - 1;
+          cc.template advance<kFold>(p);
+        }
       }
     }
     // no copy may still be writing this workgroup's LDS when it exits

@@ -4,8 +4,8 @@ partials of the cyclic split followed by their LSE-weighted merge, and the
 unsharded attention they must equal. Covers every workload shape scaled
 down, shard counts 1-16, q_len 4 with per-request depths, both LSE bases and
 output dtypes, zero-length requests, more segments than the schedule keeps
-in LDS, sampled requests at the full kimi-like size, the reused schedule and
-HIP-graph replays.
+in LDS, sampled requests at the full kimi-like, fp8 and skewed sizes, the
+reused schedule and HIP-graph replays.
 """
 import numpy as np
 import pytest
@@ -151,11 +151,13 @@ def test_all_shards_many_segments_and_reused_schedule():
     assert torch.equal(bufs.lse.view(torch.int32), first_l.view(torch.int32))
 
 
-@pytest.mark.parametrize("index", [2, 3])
+@pytest.mark.parametrize("index", [2, 3, 5])
 def test_all_shards_full_size_sampled(index):
-    """The full kimi-like (S 4) and fp8 (S 8) workloads in the launch
-    configuration the benchmark times; sampled requests against the
-    unsharded oracle, every row written."""
+    """The full kimi-like (S 4), fp8 (S 8) and skewed (S 8) workloads in the
+    launch configuration the benchmark times; sampled requests against the
+    unsharded oracle (skewed: its eight shortest requests, whose outputs are
+    close to single V rows and so the largest, the longest and the median
+    too), every row written."""
     wl = make_config(index)
     dw = ST.DeviceWorkload.upload(wl)
     bufs = ST.StepBuffers(dw)
@@ -165,6 +167,9 @@ def test_all_shards_full_size_sampled(index):
     torch.cuda.synchronize()
     assert not torch.isnan(bufs.out.float()).any() and not torch.isnan(bufs.lse).any()
     sample = [0, 7, wl.batch - 1]
+    if index == 5:
+        order = np.argsort(wl.seq_lens, kind="stable")
+        sample = sorted({int(x) for x in order[:8]} | {int(order[-1]), int(order[len(order) // 2])})
     full_o, full_l = O.decode_full(wl, requests=sample)
     U.assert_partial_close(bufs.out[sample], bufs.lse[sample], full_o, full_l, "e", U.TOL[wl.kv_dtype],
                            f"full {wl.name}")
