@@ -262,8 +262,11 @@ mla_status_t mla_decode_plan(const mla_decode_args_t* args, void* stream);
  * decode] 功能与动机 and 实现拆解 step 3: shard r attends over the tokens
  * t = j S + r it owns) and merges their partials with the LSE-weighted
  * reduction of [symm_a2a] Modifications (fourth kernel) inside the same
- * call: the pieces of every shard's share of a request are combined in one
- * pass, so no per-shard (out, lse) is written or re-read. `out` / `lse`
+ * call: the shards of a row block are neighbours in the schedule and a
+ * workgroup's online softmax runs on from one shard's tokens to the next
+ * (the merge of two shards' states is exact arithmetic), and the pieces a
+ * row block is cut into are combined in one pass, so no per-shard
+ * (out, lse) is written or re-read. `out` / `lse`
  * receive the merged result, which is the full-context attention of every
  * query row (the per-shard formula above with O the union over r):
  *   out[b,i,h,:] = merge_r (out_r, lse_r),  lse[b,i,h] = log sum_r exp(lse_r)
