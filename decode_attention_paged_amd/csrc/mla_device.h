@@ -101,4 +101,8 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
+// s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt at maximum): every LDS and
+// scalar-memory operation the wave issued has completed.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 }  // namespace mla

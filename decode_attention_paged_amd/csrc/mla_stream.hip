@@ -1139,6 +1139,10 @@ void attn_ws_kernel(DecodeParams p) {
           const bf16x8_t x = *(const bf16x8_t*)(sb + kWsStagePitch * rr + 16 * c16);
           if (row0 + rr < p.rows) __builtin_nontemporal_store(x, (bf16x8_t*)(obase + (long long)rr * kDv + 128 * wq + 8 * c16));
         }
+        // the staging writes are complete before the next barrier on every
+        // control path (the reads above wait for them only where a row's
+        // store runs; row 0 always does, but the compiler cannot know it)
+        wait_lgkmcnt0();
       }
       t += n;
       if (t < Uw) {
