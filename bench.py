@@ -30,7 +30,10 @@ Reported:
                 the library around its launch: algorithmic bytes per launch
                 (the shard's KV rows + Q + partial out + LSE) / mean duration,
                 against 8 TB/s;
-  cpu_baseline  the fp64 oracle on a bounded sample of the same workload.
+  cpu_baseline  the fp64 oracle on a bounded sample of the same workload;
+  hbm_measured  on-box HBM references from library kernels (a 1 GiB device
+                copy and a 1 GiB read), against the larger of which the
+                HBM-bound kernels' fractions are also given.
 
 The fp8-KV workload is also timed with its query quantised to e4m3 codes
 (mla_quantize_q, then the decode reads the codes): `e4m3_query` under its
@@ -520,6 +523,43 @@ def _all_shards_result(wl, kv_bytes, flops, ms, attn_ms, d_out, d_lse, timing):
                 step_timing=timing, max_abs_diff_vs_separate=dict(out=d_out, lse=d_lse))
 
 
+def measure_copy_peak(nbytes: int = 1 << 30, reps: int = 10):
+    """On-box HBM references from library kernels, timed by events over
+    `reps` back-to-back runs: a device-to-device copy of `nbytes` (read and
+    written once: 2 x nbytes per run) and a sum over `nbytes` of fp32 (read
+    once), both sequential streams. `gbs` is the larger of the two; the
+    HBM-bound kernels' fractions of it are reported next to those of the
+    8 TB/s spec. They are references, not the chip's ceiling: LDS-DMA streams
+    written for this library move more (6.0-6.9 TB/s sequential)."""
+    import torch
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3
+
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    copy_gbs = 2 * nbytes * reps / timed(lambda: dst.copy_(src)) / 1e9
+    del src, dst
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    out = torch.empty((), dtype=torch.float32, device="cuda")
+    read_gbs = nbytes * reps / timed(lambda: torch.sum(x, dim=0, out=out)) / 1e9
+    del x, out
+    torch.cuda.empty_cache()
+    return dict(gbs=round(max(copy_gbs, read_gbs), 1), copy_gbs=round(copy_gbs, 1), read_gbs=round(read_gbs, 1),
+                bytes=nbytes, runs=reps,
+                method="events around back-to-back runs of a device-to-device copy (torch copy_, read + "
+                       "write bytes) and an fp32 sum (torch sum, read bytes) of 1 GiB")
+
+
 def bench_merge_sweep(replays: int = 20, warmup: int = 5):
     """Merge-only: 4 partials of [T, 64, 512] bf16 + fp32 LSE -> [T, 64, 512] bf16.
 
@@ -819,6 +859,13 @@ def main() -> int:
                 f"vs bf16 query out {e['max_abs_diff_vs_bf16_query']['out']:.2e}")
 
     cpu = None if args.no_cpu else cpu_baseline(wl, args.cpu_seconds)
+    hbm_measured = measure_copy_peak()
+    log(f"[bench] on-box HBM references: copy {hbm_measured['copy_gbs']:.0f} GB/s, "
+        f"read {hbm_measured['read_gbs']:.0f} GB/s")
+    for r in per_config.values():
+        ak = r["attn_kernel"]
+        if ak["bound"] == "hbm":
+            ak["frac_of_measured_reference"] = round(ak["achieved"] / hbm_measured["gbs"], 4)
     mfma_bound = res["attn_kernel_mfma_frac"] > res["attn_kernel_hbm_frac"]
     if mfma_bound:
         peak = BF16_PEAK_TFLOPS
@@ -832,6 +879,9 @@ def main() -> int:
     roof["kernel"] = kname + ", mean of %d launches" % (args.steps * wl.shards)
     roof["mean_launch_us"] = res["attn_kernel_mean_us"]
     roof["algorithmic_bytes_per_launch"] = res["attn_kernel_bytes_per_launch"]
+    if roof["bound"] == "hbm":
+        roof["measured_reference"] = hbm_measured["gbs"]
+        roof["frac_of_measured_reference"] = roof["achieved"] / hbm_measured["gbs"]
 
     line = {
         "metric": METRIC,
@@ -872,9 +922,13 @@ def main() -> int:
                                         + "; schedule built once per step")
                             if "all_shards" in res else None),
         "roofline": roof,
+        "hbm_measured": hbm_measured,
         "configs": per_config,
         "cpu_baseline": cpu,
     }
+    if line["merge_roofline"]:
+        line["merge_roofline"]["frac_of_measured_reference"] = round(
+            line["merge_roofline"]["achieved"] / hbm_measured["gbs"], 4)
     if args.details:
         os.makedirs(os.path.dirname(os.path.abspath(args.details)), exist_ok=True)
         with open(args.details, "w") as f:
