@@ -355,6 +355,19 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
       const int32_t slots = all_cus ? (per_xcd / rgroup) * rgroup : per_xcd - per_xcd / 16;
       grid = 8 * (slots > 0 ? slots : 1);
     }
+    if (a->split_target <= 0) {
+      // a small step has less work than CUs: the schedule uses at most one
+      // group per cost unit, and the cost (tiles + the piece cost of each
+      // super-segment) is bounded from the batch, the row blocks, the shards
+      // and the block table's width (no request reads past max_pages x 64
+      // tokens), so only that many workgroups are launched and the rest are
+      // not dispatched just to exit
+      const int64_t local_tokens = ((int64_t)a->max_pages * MLA_PAGE_SIZE + a->num_shards - 1) / a->num_shards;
+      const int64_t tiles = (local_tokens + mla::kTile - 1) / mla::kTile;
+      const int64_t supers = (int64_t)a->batch * fold * (rgroup == 1 ? row_blocks : 1);
+      const int64_t need = supers * (tiles + mla::kPieceCost) * rgroup;
+      if (need < grid) grid = (int32_t)((need + 7) / 8 * 8);
+    }
     if (grid < 8) grid = 8;
     if (grid > mla::kMaxGrid) grid = mla::kMaxGrid;
     grid = (grid / rgroup) * rgroup;

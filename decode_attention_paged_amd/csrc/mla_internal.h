@@ -12,6 +12,7 @@ constexpr int kPage = 64;
 constexpr int kDqk = 576;       // latent 512 + rope 64
 constexpr int kDv = 512;        // V = first 512 latent dims
 constexpr int kTile = 32;       // KV tokens per attention tile
+constexpr int kPieceCost = 3;   // query load + epilogue of a piece, in tiles (the schedule's cost model)
 constexpr int kMaxShards = 16;
 
 // Everything the plan / attention / combine kernels need for one shard.

@@ -43,7 +43,6 @@ constexpr int kRopeBase = kTile * 1024;             // rope part of a bf16 stage
 // and unnormalised probabilities stay below 2^kRescaleSlack.
 constexpr float kRescaleSlack = 8.0f;
 
-constexpr int kPieceCost = 3;     // query load + epilogue of a piece, in tiles
 
 
 
