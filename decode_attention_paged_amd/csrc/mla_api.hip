@@ -102,6 +102,7 @@ WorkspaceLayout decode_workspace_layout(int32_t batch, int32_t rows, int32_t max
   w.wg_start = off;  off = align_up(off + sizeof(int2) * (size_t)kMaxGrid, 256);
   w.wg_ustart = off; off = align_up(off + sizeof(int32_t) * (size_t)(kMaxGrid + 1), 256);
   w.wg_rec = off;    off = align_up(off + sizeof(int32_t) * (size_t)kMaxGrid * kRecInts, 256);
+  w.grp_sync = off;  off = align_up(off + sizeof(int32_t) * (size_t)kMaxGrid, 256);
   w.spart_lse = off; off = align_up(off + sizeof(float) * (size_t)w.max_slots * rows_blk, 256);
   w.spart_o = off;   off = align_up(off + sizeof(uint16_t) * (size_t)w.max_slots * rows_blk * kDv, 256);
   w.total = off;
@@ -432,6 +433,7 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
   p.seg_info = (int4*)(ws + w.seg_info);
   p.wg_start = (int2*)(ws + w.wg_start);
   p.wg_rec = (int32_t*)(ws + w.wg_rec);
+  p.grp_sync = (int32_t*)(ws + w.grp_sync);
   p.spart_lse = (float*)(ws + w.spart_lse);
   p.spart_o = (uint16_t*)(ws + w.spart_o);
   p.rows_blk = rows_blk;

@@ -38,6 +38,11 @@ __device__ __forceinline__ float wave_sum(float x) {
 __global__ __launch_bounds__(256) void stream_combine_kernel(DecodeParams p) {
   constexpr int kPieces = 4;
   const int b = blockIdx.x;
+  // the attention launch before this kernel is complete: its row-block
+  // groups' rendezvous counters go back to zero for the next launch
+  if (b == 0 && blockIdx.y == 0 && p.fold > 1) {
+    for (int q = threadIdx.x; q < kMaxGrid; q += blockDim.x) p.grp_sync[q] = 0;
+  }
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.y * 4 + (threadIdx.x >> 6);
   if (row >= p.rows) return;

@@ -70,6 +70,10 @@ struct DecodeParams {
   // workgroups per row-block group: a request's row_blocks row blocks run on
   // that many neighbouring workgroups over the same tiles (1: plain schedule)
   int32_t rgroup;
+  // [kMaxGrid] arrival counters of the row-block groups' rendezvous in the
+  // launch of every shard (zeroed by the schedule and after every launch by
+  // the piece combine)
+  int32_t* grp_sync;
 };
 
 constexpr int kMaxGrid = 1024;  // persistent workgroups of the streaming kernel
@@ -83,7 +87,7 @@ constexpr int kRecInts = 8;     // start record of a workgroup: 6 ints used
 inline int32_t stream_rows_per_block(int32_t) { return 64; }
 
 struct WorkspaceLayout {
-  size_t plan, req_cnt, seg_off, seg_coff, seg_info, wg_start, wg_ustart, wg_rec, spart_lse, spart_o, total;
+  size_t plan, req_cnt, seg_off, seg_coff, seg_info, wg_start, wg_ustart, wg_rec, grp_sync, spart_lse, spart_o, total;
   int32_t max_slots;
 };
 // max_slots < 0: the bound every schedule fits (segments + the largest grid)

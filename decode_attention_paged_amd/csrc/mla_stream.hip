@@ -142,6 +142,8 @@ __global__ __launch_bounds__(1024) void stream_plan_kernel(DecodeParams p) {
   const int per = (nsup + 1023) / 1024;
   const int s0 = min(tid * per, nsup), s1 = min(s0 + per, nsup);
 
+  // the row-block groups' rendezvous counters start at zero
+  for (int q = tid; q < kMaxGrid; q += 1024) p.grp_sync[q] = 0;
   // owned-token counts per request and shard
   for (int q = tid; q < p.batch * p.fold; q += 1024) {
     const int b = q / p.fold, ri = q - b * p.fold;
@@ -726,6 +728,29 @@ void attn_ws_kernel(DecodeParams p) {
       }
     };
     f32x4_t* xmine = xbuf + (rg * 4) * 64 + lane;
+    // launch of every shard, row-block groups: the workgroups of a group walk
+    // the same tiles for their row blocks, and each tile comes from HBM once
+    // only while they stay close (the later one reads it from L2). Over long
+    // walks their clocks drift them apart, so every kSyncTiles tiles one
+    // partner score wave of each adds to the group's counter and waits, a
+    // bounded number of polls, for the others to arrive; the barrier after
+    // it holds the whole workgroup. It paces only: the results do not
+    // depend on it, and a partner that never comes costs kSyncPolls polls.
+    constexpr int kSyncTiles = 64;
+    constexpr int kSyncPolls = 8;
+    auto rendezvous = [&](int tile) {
+      if (p.rgroup > 1 && wave == 2 && tile > 0 && tile % kSyncTiles == 0) {
+        if (lane == 0) {
+          int32_t* ctr = p.grp_sync + g / p.rgroup;
+          const int target = (tile / kSyncTiles) * p.rgroup;
+          __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int i = 0; i < kSyncPolls; ++i) {
+            if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) break;
+            __builtin_amdgcn_s_sleep(16);
+          }
+        }
+      }
+    };
 
     int t = 0;
     while (t < Uw) {
@@ -869,6 +894,7 @@ void attn_ws_kernel(DecodeParams p) {
 
       f32x16_t s_cur;
       // tile 0: its scores
+      if constexpr (kFold) rendezvous(t);
       __syncthreads();   // tile t landed
       {
         const uint8_t* ksq = smem + kStageB * (t & (kNS - 1));
@@ -883,6 +909,7 @@ void attn_ws_kernel(DecodeParams p) {
       __syncthreads();   // partials exchanged
       if (ds == 0) s_cur = partner_sum();
       for (int k = 0; k + 1 < n; ++k) {
+        if constexpr (kFold) rendezvous(t + k + 1);
         __syncthreads();   // tile t + k + 1 landed
         const uint8_t* ksq = smem + kStageB * ((t + k + 1) & (kNS - 1));
         qk_start(ksq);
