@@ -774,6 +774,76 @@ def config_summary(r):
     return out
 
 
+def assemble_line(args, wl, res, merge, append, per_config, cpu, hbm_measured) -> dict:
+    """The JSON line: the headline workload's step and attention kernel, the
+    merge sweep and append timing, every workload under `configs`, the CPU
+    baseline and the on-box HBM references."""
+    mfma_bound = res["attn_kernel_mfma_frac"] > res["attn_kernel_hbm_frac"]
+    if mfma_bound:
+        peak = BF16_PEAK_TFLOPS
+        roof = dict(bound="mfma", achieved=res["attn_kernel_tflops"], peak=peak, unit="TFLOP/s",
+                    frac=res["attn_kernel_tflops"] / peak)
+    else:
+        roof = dict(bound="hbm", achieved=res["attn_kernel_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=res["attn_kernel_gbs"] / HBM_PEAK_GBS)
+    roof["traffic"] = traffic_from_profile(wl.name)
+    kname = "attn_ws_kernel<block table, %s KV> (mla_stream.hip)" % wl.kv_dtype
+    roof["kernel"] = kname + ", mean of %d launches" % (args.steps * wl.shards)
+    roof["mean_launch_us"] = res["attn_kernel_mean_us"]
+    roof["algorithmic_bytes_per_launch"] = res["attn_kernel_bytes_per_launch"]
+    if roof["bound"] == "hbm":
+        roof["measured_reference"] = hbm_measured["gbs"]
+        roof["frac_of_measured_reference"] = roof["achieved"] / hbm_measured["gbs"]
+
+    line = {
+        "metric": METRIC,
+        "value": round(res["kv_gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",            # MFMA contraction type (fp8 KV is converted to bf16)
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: batch {wl.batch}, {wl.heads} heads, q_len {wl.q_len}, "
+                               f"{wl.shards} cyclic shards, {wl.kv_dtype} KV, page 64, "
+                               f"{res['tokens']} context tokens, partials + merge",
+                   "global_batch": wl.batch, "shards": wl.shards, "step": res["step_timing"],
+                   "per_decode_step": "schedule %.1f us per shard, not in the step (shard metadata, not used by the step: %.1f us)"
+                                      % (res["plan_us_per_shard"], res["metadata_us_per_shard"])},
+        "tflops": round(res["tflops"], 3),
+        "merge_us": {T: round(v["us_median"], 2) for T, v in merge.items()} if merge else None,
+        "merge_kernel_us": {T: round(v["kernel_us_mean"], 2) for T, v in merge.items()} if merge else None,
+        "merge_roofline": (dict(bound="hbm", T=128, achieved=round(merge["128"]["kernel_gbs"], 1), peak=HBM_PEAK_GBS,
+                                unit="GB/s", frac=round(merge["128"]["kernel_gbs"] / HBM_PEAK_GBS, 4),
+                                kernel_us=round(merge["128"]["kernel_us_mean"], 2))
+                           if merge and "128" in merge else None),
+        "merge_step": dict(us=round(res["merge_us"], 2), bytes=int(res["merge_bytes"]),
+                           gbs=round(res["merge_gbs"], 1), frac=round(res["merge_hbm_frac"], 4),
+                           shards=wl.shards, timing="the step's merge kernel, its own dispatch (eager)"),
+        "append_us": append,
+        "all_shards_step": (dict(ms_per_step=round(res["all_shards"]["ms_per_step"], 5),
+                                 kv_gbs=round(res["all_shards"]["kv_gbs"], 1),
+                                 attn_kernel_us=round(res["all_shards"]["attn_kernel_us"], 2),
+                                 attn_kernel_hbm_frac=round(res["all_shards"]["attn_kernel_hbm_frac"], 4),
+                                 timing="mla_decode_all_shards: every shard in one launch, merge fused, "
+                                        + res["all_shards"].get("step_timing", "graph replay")
+                                        + "; schedule built once per step")
+                            if "all_shards" in res else None),
+        "roofline": roof,
+        "hbm_measured": hbm_measured,
+        "configs": per_config,
+        "cpu_baseline": cpu,
+    }
+    if line["merge_roofline"]:
+        line["merge_roofline"]["frac_of_measured_reference"] = round(
+            line["merge_roofline"]["achieved"] / hbm_measured["gbs"], 4)
+    return line
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -866,69 +936,7 @@ def main() -> int:
         ak = r["attn_kernel"]
         if ak["bound"] == "hbm":
             ak["frac_of_measured_reference"] = round(ak["achieved"] / hbm_measured["gbs"], 4)
-    mfma_bound = res["attn_kernel_mfma_frac"] > res["attn_kernel_hbm_frac"]
-    if mfma_bound:
-        peak = BF16_PEAK_TFLOPS
-        roof = dict(bound="mfma", achieved=res["attn_kernel_tflops"], peak=peak, unit="TFLOP/s",
-                    frac=res["attn_kernel_tflops"] / peak)
-    else:
-        roof = dict(bound="hbm", achieved=res["attn_kernel_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=res["attn_kernel_gbs"] / HBM_PEAK_GBS)
-    roof["traffic"] = traffic_from_profile(wl.name)
-    kname = "attn_ws_kernel<block table, %s KV> (mla_stream.hip)" % wl.kv_dtype
-    roof["kernel"] = kname + ", mean of %d launches" % (args.steps * wl.shards)
-    roof["mean_launch_us"] = res["attn_kernel_mean_us"]
-    roof["algorithmic_bytes_per_launch"] = res["attn_kernel_bytes_per_launch"]
-    if roof["bound"] == "hbm":
-        roof["measured_reference"] = hbm_measured["gbs"]
-        roof["frac_of_measured_reference"] = roof["achieved"] / hbm_measured["gbs"]
-
-    line = {
-        "metric": METRIC,
-        "value": round(res["kv_gbs"], 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(res["ms_per_step"], 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",            # MFMA contraction type (fp8 KV is converted to bf16)
-        "data": "synthetic",
-        "config": {"workload": f"{wl.name}: batch {wl.batch}, {wl.heads} heads, q_len {wl.q_len}, "
-                               f"{wl.shards} cyclic shards, {wl.kv_dtype} KV, page 64, "
-                               f"{res['tokens']} context tokens, partials + merge",
-                   "global_batch": wl.batch, "shards": wl.shards, "step": res["step_timing"],
-                   "per_decode_step": "schedule %.1f us per shard, not in the step (shard metadata, not used by the step: %.1f us)"
-                                      % (res["plan_us_per_shard"], res["metadata_us_per_shard"])},
-        "tflops": round(res["tflops"], 3),
-        "merge_us": {T: round(v["us_median"], 2) for T, v in merge.items()} if merge else None,
-        "merge_kernel_us": {T: round(v["kernel_us_mean"], 2) for T, v in merge.items()} if merge else None,
-        "merge_roofline": (dict(bound="hbm", T=128, achieved=round(merge["128"]["kernel_gbs"], 1), peak=HBM_PEAK_GBS,
-                                unit="GB/s", frac=round(merge["128"]["kernel_gbs"] / HBM_PEAK_GBS, 4),
-                                kernel_us=round(merge["128"]["kernel_us_mean"], 2))
-                           if merge and "128" in merge else None),
-        "merge_step": dict(us=round(res["merge_us"], 2), bytes=int(res["merge_bytes"]),
-                           gbs=round(res["merge_gbs"], 1), frac=round(res["merge_hbm_frac"], 4),
-                           shards=wl.shards, timing="the step's merge kernel, its own dispatch (eager)"),
-        "append_us": append,
-        "all_shards_step": (dict(ms_per_step=round(res["all_shards"]["ms_per_step"], 5),
-                                 kv_gbs=round(res["all_shards"]["kv_gbs"], 1),
-                                 attn_kernel_us=round(res["all_shards"]["attn_kernel_us"], 2),
-                                 attn_kernel_hbm_frac=round(res["all_shards"]["attn_kernel_hbm_frac"], 4),
-                                 timing="mla_decode_all_shards: every shard in one launch, merge fused, "
-                                        + res["all_shards"].get("step_timing", "graph replay")
-                                        + "; schedule built once per step")
-                            if "all_shards" in res else None),
-        "roofline": roof,
-        "hbm_measured": hbm_measured,
-        "configs": per_config,
-        "cpu_baseline": cpu,
-    }
-    if line["merge_roofline"]:
-        line["merge_roofline"]["frac_of_measured_reference"] = round(
-            line["merge_roofline"]["achieved"] / hbm_measured["gbs"], 4)
+    line = assemble_line(args, wl, res, merge, append, per_config, cpu, hbm_measured)
     if args.details:
         os.makedirs(os.path.dirname(os.path.abspath(args.details)), exist_ok=True)
         with open(args.details, "w") as f:
