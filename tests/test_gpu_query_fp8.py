@@ -13,7 +13,10 @@ scores run on the fp8 matrix cores).
 * codes made on the device and on the host give bit-identical decodes;
 * at the deepseek-like full size, the decode from device-made codes stays
   within the fp8-KV bar of the bf16-query definition (the quantisation of Q
-  counted).
+  counted);
+* an fp8 pool's out-of-pool page reads the e4m3 NaN row and poisons its
+  request (out and LSE) through either query form, per shard, merged and in
+  the single launch.
 """
 import dataclasses
 
@@ -192,3 +195,48 @@ def test_e4m3_query_full_size_within_fp8_bar_of_the_bf16_query_definition():
     torch.cuda.synchronize()
     U.assert_partial_close(bufs.out[sample], bufs.lse[sample], ref_o, ref_l, "e", U.TOL["fp8"],
                            "e4m3 query single launch vs the bf16-query definition")
+
+
+@pytest.mark.parametrize("split_target", [8, 64])
+@pytest.mark.parametrize("e4m3_query", [False, True])
+def test_fp8_pool_bad_page_ids_poison_out_and_lse(e4m3_query, split_target):
+    """With an fp8 pool, a page id outside it reads the e4m3 NaN row (code
+    0x7F): the request that owns it comes out NaN, out and LSE, on every
+    shard, after the merge and in the single launch, with the bf16 query
+    (fp8 K converted in registers) and with e4m3 query codes (the fp8
+    matrix cores take the NaN code); segments whole (8 workgroups) or cut
+    (64). The other requests match the oracle."""
+    from workloads import make_workload
+    S = 2
+    wl = make_workload("bad8", batch=16, heads=16, q_len=1, shards=S, kv_dtype="fp8",
+                       lens=("fixed", (200,) * 16), seed=9, out_dtype="bf16")
+    if e4m3_query:
+        wl = _with_codes(wl, 0.25)
+    wl.block_table[0, 1] = 10_000
+    ok = list(range(1, wl.batch))
+    dw = ST.DeviceWorkload.upload(wl)
+    bufs = ST.StepBuffers(dw)
+    bufs.fill_nan()
+    parts = []
+    for r in range(S):
+        _flush(f"fp8 bad page shard {r} e4m3={e4m3_query} split={split_target}")
+        ST.run_partial(dw, bufs, r, split_target=split_target)
+        torch.cuda.synchronize()
+        o, l = bufs.outs[r].float().cpu().numpy(), bufs.lses[r].cpu().numpy()
+        assert np.isnan(o[0]).all() and np.isnan(l[0]).all(), f"shard {r}: poisoned request not NaN"
+        ref = O.decode_partial(wl, r, S, wl.lse_base, requests=ok)
+        parts.append(ref)
+        U.assert_partial_close(bufs.outs[r][ok], bufs.lses[r][ok], ref[0], ref[1], wl.lse_base, U.TOL["fp8"],
+                               f"fp8 untouched shard {r}")
+    ST.run_merge(dw, bufs)
+    torch.cuda.synchronize()
+    mo, ml = bufs.out.float().cpu().numpy(), bufs.lse.cpu().numpy()
+    assert np.isnan(mo[0]).all() and np.isnan(ml[0]).all(), "merged poisoned request not NaN"
+    ro, rl = O.merge([p_[0] for p_ in parts], [p_[1] for p_ in parts], [wl.lse_base] * S)
+    U.assert_partial_close(bufs.out[ok], bufs.lse[ok], ro, rl, "e", U.TOL["fp8"], "fp8 merged untouched")
+    bufs.fill_nan()
+    ST.run_all_shards(dw, bufs, split_target=split_target)
+    torch.cuda.synchronize()
+    mo, ml = bufs.out.float().cpu().numpy(), bufs.lse.cpu().numpy()
+    assert np.isnan(mo[0]).all() and np.isnan(ml[0]).all(), "single launch: poisoned request not NaN"
+    U.assert_partial_close(bufs.out[ok], bufs.lse[ok], ro, rl, "e", U.TOL["fp8"], "fp8 single launch untouched")
