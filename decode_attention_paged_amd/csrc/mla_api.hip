@@ -344,11 +344,11 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
     // combine) alongside, which shortens a step of concurrent partials of
     // one-row-block requests. Requests of several row blocks (row-block
     // groups, every XCD holding whole groups) and the single launch of every
-    // shard with fp8 KV (compute-bound) take every CU the group size fits:
-    // there the extra workgroups gain more than the free CUs (deepseek-like
+    // shard (nothing runs beside it) take every CU the group size fits:
+    // there the extra workgroups gain more than free CUs would (deepseek-like
     // fp8 step 0.424 -> 0.403 ms, q_len 4 0.438 -> 0.390, skewed 0.645 ->
-    // 0.628; the one-row-block kimi-like step is within noise either way).
-    const bool all_cus = rgroup > 1 || (all_shards && a->num_shards > 1 && a->kv_dtype == MLA_DTYPE_FP8_E4M3);
+    // 0.628; kimi-like single launch 96.4 -> 94.1 µs).
+    const bool all_cus = rgroup > 1 || (all_shards && a->num_shards > 1);
     if (a->split_target > 0) {
       grid = a->split_target;
     } else {
