@@ -366,7 +366,7 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
       const int64_t local_tokens = ((int64_t)a->max_pages * MLA_PAGE_SIZE + a->num_shards - 1) / a->num_shards;
       const int64_t tiles = (local_tokens + mla::kTile - 1) / mla::kTile;
       const int64_t supers = (int64_t)a->batch * fold * (rgroup == 1 ? row_blocks : 1);
-      const int64_t need = supers * (tiles + mla::kPieceCost) * rgroup;
+      const int64_t need = supers * (tiles + mla::kPieceCostMax) * rgroup;
       if (need < grid) grid = (int32_t)((need + 7) / 8 * 8);
     }
     if (grid < 8) grid = 8;

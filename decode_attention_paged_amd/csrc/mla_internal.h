@@ -12,7 +12,14 @@ constexpr int kPage = 64;
 constexpr int kDqk = 576;       // latent 512 + rope 64
 constexpr int kDv = 512;        // V = first 512 latent dims
 constexpr int kTile = 32;       // KV tokens per attention tile
-constexpr int kPieceCost = 3;   // query load + epilogue of a piece, in tiles (the schedule's cost model)
+// the schedule's cost of a piece (its query load and epilogue) in tiles: a
+// bf16 tile's time is mostly its 36 KB read, an fp8 tile's mostly its
+// MFMA work, so a piece weighs more bf16 tiles than fp8 ones (fits of
+// per-workgroup times: ~3.2-3.7 and ~2.4; interleaved sweeps of the
+// schedule: 5 and 3 best)
+constexpr int kPieceCostBf16 = 5;
+constexpr int kPieceCostFp8 = 3;
+constexpr int kPieceCostMax = kPieceCostBf16 > kPieceCostFp8 ? kPieceCostBf16 : kPieceCostFp8;
 constexpr int kMaxShards = 16;
 
 // Everything the plan / attention / combine kernels need for one shard.

@@ -155,6 +155,7 @@ __global__ __launch_bounds__(1024) void stream_plan_kernel(DecodeParams p) {
   // shards of its row block (their super-segments are neighbours), so only a
   // row block's first shard pays the query cost; shard 0 owns token 0, so it
   // has tiles whenever any shard of the request has
+  const int kPieceCost = p.kv_fp8 ? kPieceCostFp8 : kPieceCostBf16;
   auto piece_cost = [&](int s) { return p.fold > 1 && s % p.fold != 0 ? 0 : kPieceCost; };
   int su = 0, sc = 0;
   for (int s = s0; s < s1; ++s) {
