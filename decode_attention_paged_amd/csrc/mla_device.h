@@ -81,16 +81,27 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const uint8_t* p) {
 // that the compiler's wait-count bookkeeping does not make later LDS reads of
 // other buffers wait for them; every caller waits for completion explicitly
 // (s_waitcnt vmcnt + barrier) before any wave reads the destination. M0 holds
-// the LDS base (one wait state after writing it).
+// the LDS base (one wait state after writing it). kNT: the non-temporal
+// (streaming) cache policy, for data that no other workgroup reads again.
+template <bool kNT>
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds_base));
+  if constexpr (kNT)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :: "v"(src), "s"(lds_base));
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(lds_base));
 }
 // Same copy with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit
 // byte offset.
+template <bool kNT>
 __device__ __forceinline__ void lds_dma16_sbase(const void* base, uint32_t offset, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(offset), "s"(base), "s"(lds_base));
+  if constexpr (kNT)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :: "v"(offset), "s"(base), "s"(lds_base));
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(offset), "s"(base), "s"(lds_base));
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:

@@ -507,11 +507,11 @@ __device__ __forceinline__ const uint8_t* token_src(const DecodeParams& p, const
 // Copy j of a bf16 tile into a stage (the layout above):
 // j = 0 moves the eight rope tails of the wave's tokens, j = 1 + i the 1 KB
 // main part of token 8 w + i (one row per copy, as a scalar base).
-template <int kJ>
+template <int kJ, bool kNT>
 __device__ __forceinline__ void copy_tile_part(const uint8_t* src, uint32_t stage_lds, int wave) {
   const int lane = threadIdx.x & 63;
   if constexpr (kJ == 0) {
-    lds_dma16(src + 16 * (64 + ((lane & 7) ^ rope_swz(8 * wave + (lane >> 3)))),
+    lds_dma16<kNT>(src + 16 * (64 + ((lane & 7) ^ rope_swz(8 * wave + (lane >> 3)))),
               __builtin_amdgcn_readfirstlane(stage_lds + kRopeBase + 1024 * wave));
   } else {
     constexpr int i = kJ - 1;
@@ -519,21 +519,22 @@ __device__ __forceinline__ void copy_tile_part(const uint8_t* src, uint32_t stag
     const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)a, 8 * i);
     const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(a >> 32), 8 * i);
     const uint8_t* base = reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
-    lds_dma16_sbase(base, (uint32_t)(16 * (lane ^ chunk_swz(8 * wave + i))),
-                    __builtin_amdgcn_readfirstlane(stage_lds + 1024 * (8 * wave + i)));
+    lds_dma16_sbase<kNT>(base, (uint32_t)(16 * (lane ^ chunk_swz(8 * wave + i))),
+                         __builtin_amdgcn_readfirstlane(stage_lds + 1024 * (8 * wave + i)));
   }
 }
+template <bool kNT>
 __device__ __forceinline__ void copy_tile_part_rt(int j, const uint8_t* src, uint32_t stage_lds, int wave) {
   switch (j) {
-    case 0: copy_tile_part<0>(src, stage_lds, wave); break;
-    case 1: copy_tile_part<1>(src, stage_lds, wave); break;
-    case 2: copy_tile_part<2>(src, stage_lds, wave); break;
-    case 3: copy_tile_part<3>(src, stage_lds, wave); break;
-    case 4: copy_tile_part<4>(src, stage_lds, wave); break;
-    case 5: copy_tile_part<5>(src, stage_lds, wave); break;
-    case 6: copy_tile_part<6>(src, stage_lds, wave); break;
-    case 7: copy_tile_part<7>(src, stage_lds, wave); break;
-    default: copy_tile_part<8>(src, stage_lds, wave); break;
+    case 0: copy_tile_part<0, kNT>(src, stage_lds, wave); break;
+    case 1: copy_tile_part<1, kNT>(src, stage_lds, wave); break;
+    case 2: copy_tile_part<2, kNT>(src, stage_lds, wave); break;
+    case 3: copy_tile_part<3, kNT>(src, stage_lds, wave); break;
+    case 4: copy_tile_part<4, kNT>(src, stage_lds, wave); break;
+    case 5: copy_tile_part<5, kNT>(src, stage_lds, wave); break;
+    case 6: copy_tile_part<6, kNT>(src, stage_lds, wave); break;
+    case 7: copy_tile_part<7, kNT>(src, stage_lds, wave); break;
+    default: copy_tile_part<8, kNT>(src, stage_lds, wave); break;
   }
 }
 
@@ -562,7 +563,7 @@ __device__ __forceinline__ bf16x8_t cvt_fp8x8(uint32_t w0, uint32_t w1) {
 // per lane the row of token 8 w + (lane >> 3)): j < 4 moves the 512-byte
 // main parts of tokens 8 w + 2 j and + 1 (one per half wave), j = 4 the
 // eight 64-byte rope tails (a half copy, 32 lanes).
-template <int kJ>
+template <int kJ, bool kNT>
 __device__ __forceinline__ void copy8_tile_part(const uint8_t* srcw, uint32_t stage_lds, int wave) {
   const int lane = threadIdx.x & 63;
   const uint64_t a = reinterpret_cast<uint64_t>(srcw);
@@ -576,7 +577,7 @@ __device__ __forceinline__ void copy8_tile_part(const uint8_t* srcw, uint32_t st
     const int t = 8 * wave + 2 * kJ + (second ? 1 : 0);
     const int pos = lane & 31, x = (pos ^ t) & 15;
     const int c = pos ^ (t & 15) ^ (4 * (x & 1));
-    lds_dma16(reinterpret_cast<const uint8_t*>(row) + 16 * c,
+    lds_dma16<kNT>(reinterpret_cast<const uint8_t*>(row) + 16 * c,
               __builtin_amdgcn_readfirstlane(stage_lds + 512 * (8 * wave + 2 * kJ)));
   } else {
     const int tl = (lane >> 2) & 7;
@@ -585,16 +586,17 @@ __device__ __forceinline__ void copy8_tile_part(const uint8_t* srcw, uint32_t st
     const uint8_t* row = reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
     const int t = 8 * wave + tl;
     const int r = (lane & 3) ^ ((t >> 2) & 3);
-    if (lane < 32) lds_dma16(row + 512 + 16 * r, __builtin_amdgcn_readfirstlane(stage_lds + kRope8 + 512 * wave));
+    if (lane < 32) lds_dma16<kNT>(row + 512 + 16 * r, __builtin_amdgcn_readfirstlane(stage_lds + kRope8 + 512 * wave));
   }
 }
+template <bool kNT>
 __device__ __forceinline__ void copy8_tile_part_rt(int j, const uint8_t* srcw, uint32_t stage_lds, int wave) {
   switch (j) {
-    case 0: copy8_tile_part<0>(srcw, stage_lds, wave); break;
-    case 1: copy8_tile_part<1>(srcw, stage_lds, wave); break;
-    case 2: copy8_tile_part<2>(srcw, stage_lds, wave); break;
-    case 3: copy8_tile_part<3>(srcw, stage_lds, wave); break;
-    default: copy8_tile_part<4>(srcw, stage_lds, wave); break;
+    case 0: copy8_tile_part<0, kNT>(srcw, stage_lds, wave); break;
+    case 1: copy8_tile_part<1, kNT>(srcw, stage_lds, wave); break;
+    case 2: copy8_tile_part<2, kNT>(srcw, stage_lds, wave); break;
+    case 3: copy8_tile_part<3, kNT>(srcw, stage_lds, wave); break;
+    default: copy8_tile_part<4, kNT>(srcw, stage_lds, wave); break;
   }
 }
 
@@ -624,7 +626,7 @@ __device__ __forceinline__ void copy8_tile_part_rt(int j, const uint8_t* srcw, u
 constexpr int kWsRows = 64;
 constexpr int kWsStagePitch = 272;     // output staging row: 128 bf16 + 16 bytes
 
-template <bool kLocal, bool kFp8, bool kFold, bool kQ8 = false>
+template <bool kLocal, bool kFp8, bool kFold, bool kQ8, bool kNT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_ws_kernel(DecodeParams p) {
   static_assert(!kQ8 || kFp8, "an e4m3 query goes with an e4m3 KV pool");
@@ -994,8 +996,8 @@ void attn_ws_kernel(DecodeParams p) {
       }
     }
     auto copy_part = [&](int j, const uint8_t* src, uint32_t st) {
-      if constexpr (kFp8) copy8_tile_part_rt(j, src, st, wq);
-      else copy_tile_part_rt(j, src, st, wq);
+      if constexpr (kFp8) copy8_tile_part_rt<kNT>(j, src, st, wq);
+      else copy_tile_part_rt<kNT>(j, src, st, wq);
     };
     Cursor cc, cl;
     cc.start_known(p, rec_seg, rec_tile, rec_cnt);
@@ -1186,6 +1188,21 @@ void attn_ws_kernel(DecodeParams p) {
   }
 }
 
+template <bool kNT>
+const void* pick_ws_kernel(bool fp8, bool q8, bool fold, bool local) {
+  if (fp8 && q8)
+    return fold    ? reinterpret_cast<const void*>(&attn_ws_kernel<false, true, true, true, kNT>)
+           : local ? reinterpret_cast<const void*>(&attn_ws_kernel<true, true, false, true, kNT>)
+                   : reinterpret_cast<const void*>(&attn_ws_kernel<false, true, false, true, kNT>);
+  if (fp8)
+    return fold    ? reinterpret_cast<const void*>(&attn_ws_kernel<false, true, true, false, kNT>)
+           : local ? reinterpret_cast<const void*>(&attn_ws_kernel<true, true, false, false, kNT>)
+                   : reinterpret_cast<const void*>(&attn_ws_kernel<false, true, false, false, kNT>);
+  return fold    ? reinterpret_cast<const void*>(&attn_ws_kernel<false, false, true, false, kNT>)
+         : local ? reinterpret_cast<const void*>(&attn_ws_kernel<true, false, false, false, kNT>)
+                 : reinterpret_cast<const void*>(&attn_ws_kernel<false, false, false, false, kNT>);
+}
+
 }  // namespace
 
 hipError_t launch_decode_plan(const DecodeParams& p, hipStream_t stream) {
@@ -1208,18 +1225,14 @@ hipError_t launch_decode_stream(const DecodeParams& p, bool run_plan, hipEvent_t
   const bool local = p.local_kv_indices != nullptr;
   const bool fold = p.fold > 1;
   if (fold && local) return hipErrorInvalidValue;
-  if (p.kv_fp8 && p.q8 != nullptr)
-    fn = fold    ? reinterpret_cast<const void*>(&attn_ws_kernel<false, true, true, true>)
-         : local ? reinterpret_cast<const void*>(&attn_ws_kernel<true, true, false, true>)
-                 : reinterpret_cast<const void*>(&attn_ws_kernel<false, true, false, true>);
-  else if (p.kv_fp8)
-    fn = fold    ? reinterpret_cast<const void*>(&attn_ws_kernel<false, true, true>)
-         : local ? reinterpret_cast<const void*>(&attn_ws_kernel<true, true, false>)
-                 : reinterpret_cast<const void*>(&attn_ws_kernel<false, true, false>);
-  else
-    fn = fold    ? reinterpret_cast<const void*>(&attn_ws_kernel<false, false, true>)
-         : local ? reinterpret_cast<const void*>(&attn_ws_kernel<true, false, false>)
-                 : reinterpret_cast<const void*>(&attn_ws_kernel<false, false, false>);
+  // streaming (non-temporal) tile copies when no other workgroup reads the
+  // same tiles (one row block per request): the KV stream then does not
+  // evict the lines that are read again (block table, queries) from the
+  // caches (kimi-like per-shard kernel ~+5%, single launch ~-10%); row-block
+  // groups read each tile from L2 after their first member, so they keep the
+  // default policy (streaming there: MTP +3-6%, skewed +1.5-3%)
+  fn = p.rgroup == 1 ? pick_ws_kernel<true>(p.kv_fp8, p.q8 != nullptr, fold, local)
+                     : pick_ws_kernel<false>(p.kv_fp8, p.q8 != nullptr, fold, local);
   err = hipExtLaunchKernel(fn, dim3(p.grid), dim3(512), args, 0, stream, ev_begin, ev_end, 0);
   if (err != hipSuccess) return err;
   return launch_combine(p, stream);
