@@ -24,7 +24,7 @@ STATUS_WORKSPACE_TOO_SMALL = 3
 STATUS_DEVICE_ERROR = 4
 DTYPE_F32, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
 LSE_BASE_E, LSE_BASE_2 = 0, 1
-PAGE_SIZE, D_QK, D_V, MAX_SHARDS, MAX_Q_LEN = 64, 576, 512, 16, 4
+PAGE_SIZE, D_QK, D_V, MAX_SHARDS, MAX_Q_LEN, MAX_HEADS = 64, 576, 512, 16, 4, 16384
 
 
 class DecodeArgs(ctypes.Structure):

@@ -233,7 +233,9 @@ mla_status_t mla_append_kv(const mla_append_args_t* a, void* stream) {
 }
 
 size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t q_len) {
-  if (batch < 0 || num_heads < 16 || num_heads % 16 != 0 || q_len < 1 || q_len > MLA_MAX_Q_LEN) return 0;
+  if (batch < 0 || num_heads < 16 || num_heads > MLA_MAX_HEADS || num_heads % 16 != 0 || q_len < 1 ||
+      q_len > MLA_MAX_Q_LEN)
+    return 0;
   return mla::decode_workspace_layout(batch, num_heads * q_len).total;
 }
 
@@ -253,8 +255,9 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
   launch = false;
   if (a == nullptr) return fail(MLA_STATUS_INVALID_ARGUMENT, "args is NULL");
   if (a->batch < 0) return fail(MLA_STATUS_INVALID_ARGUMENT, "batch must be >= 0 (got %d)", a->batch);
-  if (a->num_heads < 16 || a->num_heads % 16 != 0)
-    return fail(MLA_STATUS_INVALID_ARGUMENT, "num_heads must be a positive multiple of 16 (got %d)", a->num_heads);
+  if (a->num_heads < 16 || a->num_heads > MLA_MAX_HEADS || a->num_heads % 16 != 0)
+    return fail(MLA_STATUS_INVALID_ARGUMENT, "num_heads must be a multiple of 16 in [16, %d] (got %d)", MLA_MAX_HEADS,
+                a->num_heads);
   if (a->q_len < 1 || a->q_len > MLA_MAX_Q_LEN)
     return fail(MLA_STATUS_INVALID_ARGUMENT, "q_len must be in [1, %d] (got %d)", MLA_MAX_Q_LEN, a->q_len);
   if (a->page_size != MLA_PAGE_SIZE)

@@ -44,6 +44,9 @@ extern "C" {
 #define MLA_D_V 512
 #define MLA_MAX_SHARDS 16
 #define MLA_MAX_Q_LEN 4
+/* query heads per request: with q_len <= 4, a request's rows then fill at
+ * most 1024 blocks of 64, the most workgroups a decode launch uses */
+#define MLA_MAX_HEADS 16384
 
 typedef enum mla_status {
   MLA_STATUS_OK = 0,
@@ -133,7 +136,7 @@ typedef struct mla_decode_args {
   int32_t local_kv_stride;
   /* sizes */
   int32_t batch;
-  int32_t num_heads;             /* positive multiple of 16                       */
+  int32_t num_heads;             /* multiple of 16 in [16, MLA_MAX_HEADS]         */
   int32_t q_len;                 /* 1 .. MLA_MAX_Q_LEN                            */
   int32_t max_pages;
   int32_t num_pages;             /* page ids outside [0, num_pages) read as NaN   */
@@ -214,7 +217,8 @@ size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t q_le
  * a query stride that is negative, not a multiple of 8 or below the dims it
  * holds (576, or 512 with q_rope; 64 for q_rope), a query pointer that is
  * not 16-byte aligned,
- * num_heads not a positive multiple of 16, q_len outside [1, 4],
+ * num_heads not a multiple of 16 in [16, MLA_MAX_HEADS], q_len outside
+ * [1, 4],
  * page_size != 64, bad shard ids, num_pages < 1, max_pages < 1,
  * split_target outside [0, 1024], a dtype other than those listed;
  * WORKSPACE_TOO_SMALL; DEVICE_ERROR if a launch

@@ -48,6 +48,8 @@ def test_workspace_size_is_host_only(lib):
     assert n > 128 * 128 * 512 * 4
     assert lib.mla_decode_workspace_bytes(4, 17, 1) == 0       # heads not a multiple of 16
     assert lib.mla_decode_workspace_bytes(4, 16, 5) == 0       # q_len > 4
+    assert lib.mla_decode_workspace_bytes(4, L.MAX_HEADS, 4) > 0
+    assert lib.mla_decode_workspace_bytes(4, L.MAX_HEADS + 16, 1) == 0    # more than 1024 row blocks at q_len 4
     assert lib.mla_decode_workspace_bytes(2, 16, 4) < lib.mla_decode_workspace_bytes(2, 32, 4)
 
 
@@ -68,6 +70,7 @@ def _valid_args():
 @pytest.mark.parametrize("field,value,status", [
     ("num_heads", 24, L.STATUS_INVALID_ARGUMENT),
     ("num_heads", 0, L.STATUS_INVALID_ARGUMENT),
+    ("num_heads", L.MAX_HEADS + 16, L.STATUS_INVALID_ARGUMENT),
     ("q_len", 0, L.STATUS_INVALID_ARGUMENT),
     ("q_len", 5, L.STATUS_INVALID_ARGUMENT),
     ("page_size", 32, L.STATUS_INVALID_ARGUMENT),
