@@ -215,6 +215,34 @@ def test_partial_parity_partial_row_blocks(kv_dtype, heads, q_len, out_dtype):
                                f"rows {heads * q_len} shard {r}")
 
 
+def test_maximum_heads_fill_the_workgroup_tables():
+    """num_heads at its maximum (16384) with q_len 4: one request is 1024
+    row blocks, so its row-block group takes all 1024 workgroups that the
+    schedule's tables hold. Each shard's partial and the single launch of
+    every shard match the oracle; the merged reference is the oracle's merge
+    of its own shard partials."""
+    wl = make_workload("maxheads", batch=2, heads=L.MAX_HEADS, q_len=4, shards=2, kv_dtype="bf16",
+                       lens=("uniform", 40, 160), seed=91)
+    dw = ST.DeviceWorkload.upload(wl)
+    bufs = ST.StepBuffers(dw)
+    bufs.fill_nan()
+    tol = U.TOL[wl.kv_dtype]
+    parts = []
+    for r in range(wl.shards):
+        _flush(f"max heads {L.MAX_HEADS} x q_len 4, shard {r}")
+        ST.run_partial(dw, bufs, r)
+        torch.cuda.synchronize()
+        ref_o, ref_l = O.decode_partial(wl, r, wl.shards, wl.lse_base)
+        U.assert_partial_close(bufs.outs[r], bufs.lses[r], ref_o, ref_l, wl.lse_base, tol, f"max heads shard {r}")
+        parts.append((ref_o, ref_l))
+    _flush(f"max heads {L.MAX_HEADS} x q_len 4, every shard in one launch")
+    bufs.fill_nan()
+    ST.run_all_shards(dw, bufs)
+    torch.cuda.synchronize()
+    ref_o, ref_l = O.merge([o for o, _ in parts], [l for _, l in parts], [wl.lse_base] * wl.shards)
+    U.assert_partial_close(bufs.out, bufs.lse, ref_o, ref_l, "e", tol, "max heads, every shard in one launch")
+
+
 def test_partial_bf16_output():
     wl = _small("kimi_like")
     dw = ST.DeviceWorkload.upload(wl, out_dtype="bf16")
