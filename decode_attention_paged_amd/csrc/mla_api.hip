@@ -270,6 +270,8 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
   if (a->num_pages < 1) return fail(MLA_STATUS_INVALID_ARGUMENT, "num_pages must be >= 1 (got %d)", a->num_pages);
   if ((long long)a->num_pages * MLA_PAGE_SIZE > 0x7FFFFFFFLL)
     return fail(MLA_STATUS_UNSUPPORTED, "num_pages %d exceeds 2^31 KV rows", a->num_pages);
+  if ((long long)a->max_pages * MLA_PAGE_SIZE > 0x7FFFFFFFLL)
+    return fail(MLA_STATUS_UNSUPPORTED, "max_pages %d exceeds 2^31 tokens per request", a->max_pages);
   if (a->kv_dtype != MLA_DTYPE_BF16 && a->kv_dtype != MLA_DTYPE_FP8_E4M3)
     return fail(MLA_STATUS_INVALID_ARGUMENT, "kv_dtype must be BF16 or FP8_E4M3");
   if (a->out_dtype != MLA_DTYPE_F32 && a->out_dtype != MLA_DTYPE_BF16)

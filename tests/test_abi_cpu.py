@@ -84,6 +84,8 @@ def _valid_args():
     ("lse", None, L.STATUS_INVALID_ARGUMENT),
     ("softmax_scale", 0.0, L.STATUS_INVALID_ARGUMENT),
     ("num_pages", 0, L.STATUS_INVALID_ARGUMENT),
+    ("num_pages", 2 ** 25 + 1, L.STATUS_UNSUPPORTED),           # pool rows past int32
+    ("max_pages", 2 ** 25 + 1, L.STATUS_UNSUPPORTED),           # tokens a request can hold past int32
     ("local_seq_lens", 0x2000, L.STATUS_INVALID_ARGUMENT),     # without local_kv_indices
     ("split_target", 100000, L.STATUS_INVALID_ARGUMENT),
     ("workspace_bytes", 0, L.STATUS_WORKSPACE_TOO_SMALL),
