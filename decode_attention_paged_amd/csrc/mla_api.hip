@@ -328,6 +328,19 @@ static mla_status_t prepare_decode(const mla_decode_args_t* a, mla::DecodeParams
   const int32_t fold = all_shards ? a->num_shards : 1;
   if ((int64_t)a->batch * fold > 0x7FFFFFFFLL)
     return fail(MLA_STATUS_INVALID_ARGUMENT, "batch %d x %d shards is too large", a->batch, fold);
+  {
+    // the schedule counts tiles and their costs in 32-bit integers: bound
+    // them from the sizes alone (every request as long as its block-table
+    // row allows)
+    const int64_t rb = (rows + mla::stream_rows_per_block(rows) - 1) / mla::stream_rows_per_block(rows);
+    const int64_t local_tokens = ((int64_t)a->max_pages * MLA_PAGE_SIZE + a->num_shards - 1) / a->num_shards;
+    const int64_t tiles = (local_tokens + mla::kTile - 1) / mla::kTile;
+    const int64_t segs = (int64_t)a->batch * fold * rb;
+    if (segs * (tiles + mla::kPieceCostMax) > 0x7FFFFFFFLL)
+      return fail(MLA_STATUS_UNSUPPORTED,
+                  "batch %d x %lld row blocks x %lld tiles per request (max_pages %d) exceeds the schedule's 2^31 "
+                  "tiles; split the batch", a->batch, (long long)(fold * rb), (long long)tiles, a->max_pages);
+  }
   mla::WorkspaceLayout w = mla::decode_workspace_layout(a->batch * fold, rows);
   if (!noalloc && a->batch > 0 && a->workspace_bytes < w.total)
     return fail(MLA_STATUS_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", w.total, a->workspace_bytes);

@@ -222,7 +222,8 @@ size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t q_le
  * page_size != 64, bad shard ids, num_pages < 1, max_pages < 1,
  * split_target outside [0, 1024], a dtype other than those listed;
  * UNSUPPORTED when num_pages * 64 (rows of the pool) or max_pages * 64
- * (tokens a request can hold) exceeds 2^31 - 1;
+ * (tokens a request can hold) exceeds 2^31 - 1, or when batch x 64-row
+ * blocks x 32-token tiles a request can hold (per shard) reaches 2^31;
  * WORKSPACE_TOO_SMALL; DEVICE_ERROR if a launch
  * fails. `lse_base_written` (host, may be NULL) receives the base of `lse`,
  * which is always the requested one. */

@@ -98,6 +98,18 @@ def test_decode_argument_errors(lib, field, value, status):
     assert lib.mla_last_error()
 
 
+def test_schedule_size_bound(lib):
+    """The schedule counts tiles in 32-bit integers: sizes whose bound (every
+    request as long as its block-table row) reaches 2^31 are refused before
+    any device call, and the next smaller batch gets past the check."""
+    a = _valid_args()
+    a.batch, a.max_pages, a.num_shards, a.shard_id = 2 ** 16, 2 ** 15, 1, 0    # 2^16 x 65536 tiles
+    assert lib.mla_decode_partial(ctypes.byref(a), None, None) == L.STATUS_UNSUPPORTED
+    assert b"split the batch" in lib.mla_last_error()
+    a.batch = 2 ** 10
+    assert lib.mla_decode_partial(ctypes.byref(a), None, None) == L.STATUS_WORKSPACE_TOO_SMALL
+
+
 @pytest.mark.parametrize("fields", [
     dict(q_row_stride=100),                                 # not a multiple of 8
     dict(q_row_stride=512),                                 # below 576 without q_rope
